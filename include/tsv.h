@@ -1,0 +1,172 @@
+/*
+ * tsv.h -- query-aware page selection with sparse paged-attention decode on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The method is TinyServe's ("Query-Aware Cache Selection for Efficient LLM
+ * Serving", arXiv 2509.12211): every page (block) of the paged KV cache
+ * carries a bounding box of its keys; at each decode step the query is scored
+ * against every box, only the highest-scoring pages are kept, and masked
+ * softmax attention runs over the tokens of those pages alone (abstract;
+ * method details, key design).  The box is the per-channel [min, max] of the
+ * page's keys; the score of a page for one query head is
+ *     s = sum_d max(q_d * kmin_d, q_d * kmax_d),
+ * the largest q.k any point of the box reaches, so it bounds the true q.k of
+ * every token in the page.
+ *
+ * Conventions for every call
+ * --------------------------
+ *  B = batch, Hq / Hkv = query / KV heads, G = Hq / Hkv (query head hq reads
+ *  KV head hq / G), D = head_dim, P = page_size, MP = max_pages_per_seq,
+ *  NP = num_phys_pages.  len_b = seq_lens[b] counts the token being decoded;
+ *  n_b = ceil(len_b / P) pages; page p holds min(P, len_b - p*P) valid tokens.
+ *
+ *  Layouts (row-major, all device pointers on the current HIP device):
+ *    k_pool, v_pool  [NP][Hkv][P][D]   KV dtype
+ *    meta            [NP][Hkv][2][D]   KV dtype; row 0 = per-channel min,
+ *                                      row 1 = per-channel max of the page's
+ *                                      valid keys
+ *    q               [B][Hq][D]        fp32
+ *    out             [B][Hq][D]        fp32
+ *    block_table     [B][MP]           int32 physical page of logical page p
+ *    seq_lens        [B]               int32
+ *    sel             [B][Hkv][k_max]   int32 logical pages, ascending, -1 pad
+ *    sel_count       [B][Hkv]          int32
+ *    scores_out      [B][Hkv][MP]      fp32 (only p < n_b written)
+ *  q, out, pools, meta, k_new, v_new: 16-byte aligned; int32 arrays 4-byte.
+ *
+ *  Ownership: the caller allocates and owns every buffer.  The library
+ *  allocates nothing, keeps no state between calls and is thread-safe; calls
+ *  on one stream run in order, calls on different streams that write the same
+ *  buffers race.
+ *
+ *  Streams: `stream` is a hipStream_t (NULL = the default stream).  Every call
+ *  only enqueues work on it and returns without synchronising.
+ *
+ *  Data contents are not checked on the host.  The device clamps len_b into
+ *  [0, MP*P] and block-table entries into [0, NP) so that no access leaves
+ *  the buffers; a block-table entry outside [0, NP) gives undefined results.
+ *  A sequence with len_b = 0 selects nothing and its output rows are zero.
+ *  Pages shared by several sequences must be full wherever they are shared.
+ *
+ *  Return value: TSV_OK, or an error code.  Argument checks run before any
+ *  HIP call, so an error return has enqueued nothing.
+ */
+#ifndef TSV_H
+#define TSV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TSV_VERSION 1
+
+typedef enum { TSV_F32 = 0, TSV_F16 = 1, TSV_BF16 = 2 } tsv_dtype;
+
+typedef struct {
+  int32_t batch;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t page_size;
+  int32_t max_pages_per_seq;
+  int32_t num_phys_pages;
+  int32_t kv_dtype; /* tsv_dtype */
+} tsv_shape;
+
+enum {
+  TSV_OK = 0,
+  /* null pointer, non-positive size, Hq % Hkv != 0, k_max < 1,
+     n_sink outside [0, k_max], misaligned pointer, workspace too small */
+  TSV_ERR_INVALID_ARG = -1,
+  /* head_dim not 64/128, page_size not 8/16/32/64, G not 1/2/4/8,
+     unknown dtype, max_pages_per_seq > 4096 */
+  TSV_ERR_UNSUPPORTED = -2,
+  /* a kernel launch failed (hipGetLastError after the launch) */
+  TSV_ERR_HIP = -3
+};
+
+/* Library version (TSV_VERSION). */
+int tsv_version(void);
+
+/* Static description of a status code. */
+const char* tsv_status_string(int status);
+
+/* Bytes of the metadata array for `shape`: NP*Hkv*2*D*sizeof(KV dtype);
+   0 when the shape is invalid or unsupported. */
+size_t tsv_meta_bytes(const tsv_shape* shape);
+
+/* Bytes of scratch tsv_sparse_decode / tsv_decode_step need for rows of
+   k_max selected pages; 0 when the shape is invalid or unsupported.  The
+   workspace holds partial softmax states of the split decode and needs no
+   initialisation. */
+size_t tsv_workspace_bytes(const tsv_shape* shape, int32_t k_max);
+
+/* Rebuild the bounding box of every page p < n_b of every sequence from the
+   keys in k_pool (method details, key design: each block's box covers the
+   keys it contains).  Only valid slots are read.  Also the recovery path
+   after the pool is restored. */
+int tsv_meta_build(const tsv_shape* shape, const void* k_pool, void* meta,
+                   const int32_t* block_table, const int32_t* seq_lens,
+                   void* stream);
+
+/* Append one token per sequence and keep its page's box current.
+   seq_lens already counts the new token; k_new / v_new [B][Hkv][D] (KV dtype)
+   go to slot (len_b-1) % P of physical page block_table[b][(len_b-1)/P],
+   which the caller must have allocated.  Slot 0 resets the box to the new
+   key; any other slot widens it (min/max per channel).  Sequences with
+   len_b < 1 are skipped.  The page being written must not be shared. */
+int tsv_meta_append(const tsv_shape* shape, const void* k_new,
+                    const void* v_new, void* k_pool, void* v_pool, void* meta,
+                    const int32_t* block_table, const int32_t* seq_lens,
+                    void* stream);
+
+/* Score every page of every (sequence, KV head) against the query and keep
+   the top pages (method details, key design: compute the similarity of the
+   query to each block's box and load the most similar blocks).
+   Page score: fp32, each product q_d*kmin_d / q_d*kmax_d rounded once, the D
+   per-channel maxima summed as a balanced pairwise tree over contiguous
+   channels, the maximum taken over the G query heads of the KV head, -0
+   stored as +0.  Budget K_b = clamp(k_per_seq[b], 1, k_max) (k_per_seq may
+   be NULL: K_b = k_max); the first min(n_sink, K_b, n_b) pages are always
+   kept (attention-sink pages, counted inside the budget); the remaining
+   min(K_b, n_b) - that slots go to the highest scores, equal scores to the
+   lower logical page.  sel gets the chosen logical pages in ascending order,
+   -1 padded to k_max; sel_count the number chosen.  scores_out may be NULL. */
+int tsv_select_pages(const tsv_shape* shape, const float* q, const void* meta,
+                     const int32_t* block_table, const int32_t* seq_lens,
+                     int32_t k_max, const int32_t* k_per_seq, int32_t n_sink,
+                     int32_t* sel, int32_t* sel_count, float* scores_out,
+                     void* stream);
+
+/* Masked softmax attention of every query head over the valid tokens of its
+   KV head's selected pages only (abstract: masked attention over the loaded
+   pages): out = sum_t softmax(scale * q.k_t) v_t.  Tokens at or past len_b
+   are never read.  Entries of sel must be pages < n_b; with sel = every page
+   this is dense paged decode.  fp32 arithmetic; `workspace` of at least
+   tsv_workspace_bytes(shape, k_max) bytes. */
+int tsv_sparse_decode(const tsv_shape* shape, const float* q,
+                      const void* k_pool, const void* v_pool,
+                      const int32_t* block_table, const int32_t* seq_lens,
+                      const int32_t* sel, const int32_t* sel_count,
+                      int32_t k_max, float scale, float* out, void* workspace,
+                      size_t workspace_bytes, void* stream);
+
+/* One decode step: optional append (k_new and v_new both non-NULL, or both
+   NULL to skip it), page selection and sparse attention, enqueued on one
+   stream (abstract: page scoring, sparse memory access and masked attention
+   in one pass over the cache).  Arguments as in the three calls above. */
+int tsv_decode_step(const tsv_shape* shape, const float* q, const void* k_new,
+                    const void* v_new, void* k_pool, void* v_pool, void* meta,
+                    const int32_t* block_table, const int32_t* seq_lens,
+                    int32_t k_max, const int32_t* k_per_seq, int32_t n_sink,
+                    float scale, int32_t* sel, int32_t* sel_count,
+                    float* scores_out, float* out, void* workspace,
+                    size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* TSV_H */

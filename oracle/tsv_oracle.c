@@ -65,6 +65,18 @@ static float bf16_bits_to_float(uint16_t b) {
   return f;
 }
 
+/* every binary16 pattern decoded once by half_bits_to_float */
+static float half_table[65536];
+static int half_table_ready = 0;
+
+static float half_lookup(uint16_t h) {
+  if (!half_table_ready) {
+    for (uint32_t i = 0; i < 65536; ++i) half_table[i] = half_bits_to_float((uint16_t)i);
+    half_table_ready = 1;
+  }
+  return half_table[h];
+}
+
 static float kv_get(const void* base, int64_t i, int dtype) {
   if (dtype == TSVO_F32) {
     float f;
@@ -73,7 +85,7 @@ static float kv_get(const void* base, int64_t i, int dtype) {
   }
   uint16_t h;
   memcpy(&h, (const char*)base + 2 * i, 2);
-  return dtype == TSVO_F16 ? half_bits_to_float(h) : bf16_bits_to_float(h);
+  return dtype == TSVO_F16 ? half_lookup(h) : bf16_bits_to_float(h);
 }
 
 static void kv_copy(void* dst, int64_t di, const void* src, int64_t si,

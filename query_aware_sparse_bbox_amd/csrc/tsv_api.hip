@@ -1,0 +1,217 @@
+// C-ABI host layer of libtsv: argument validation, workspace carving and
+// kernel launches.  Every check runs before the first HIP call, so a rejected
+// call has touched neither the device nor the runtime.
+#include <stdint.h>
+
+#include "../../include/tsv.h"
+#include "tsv_launch.h"
+
+namespace {
+
+using tsv::Dims;
+
+constexpr size_t kAlign = 256;
+
+size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned(const void* p, size_t a) {
+  return (reinterpret_cast<uintptr_t>(p) % a) == 0;
+}
+
+// Shape check shared by every entry point; fills `d` on success.
+int check_shape(const tsv_shape* s, Dims* d) {
+  if (!s) return TSV_ERR_INVALID_ARG;
+  if (s->batch < 1 || s->num_q_heads < 1 || s->num_kv_heads < 1 ||
+      s->head_dim < 1 || s->page_size < 1 || s->max_pages_per_seq < 1 ||
+      s->num_phys_pages < 1)
+    return TSV_ERR_INVALID_ARG;
+  if (s->num_q_heads % s->num_kv_heads) return TSV_ERR_INVALID_ARG;
+  const int G = s->num_q_heads / s->num_kv_heads;
+  if (s->kv_dtype != TSV_F32 && s->kv_dtype != TSV_F16 && s->kv_dtype != TSV_BF16)
+    return TSV_ERR_UNSUPPORTED;
+  if (s->head_dim != 64 && s->head_dim != 128) return TSV_ERR_UNSUPPORTED;
+  if (s->page_size != 8 && s->page_size != 16 && s->page_size != 32 &&
+      s->page_size != 64)
+    return TSV_ERR_UNSUPPORTED;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return TSV_ERR_UNSUPPORTED;
+  if (s->max_pages_per_seq > tsv::kMaxPagesPerSeq) return TSV_ERR_UNSUPPORTED;
+  // element offsets are computed in 64 bits; token positions in 32 bits
+  if ((int64_t)s->max_pages_per_seq * s->page_size > INT32_MAX / 2)
+    return TSV_ERR_UNSUPPORTED;
+  d->B = s->batch;
+  d->Hq = s->num_q_heads;
+  d->Hkv = s->num_kv_heads;
+  d->D = s->head_dim;
+  d->P = s->page_size;
+  d->MP = s->max_pages_per_seq;
+  d->NP = s->num_phys_pages;
+  d->dt = s->kv_dtype;
+  d->G = G;
+  return TSV_OK;
+}
+
+size_t elem_bytes(const Dims& d) { return d.dt == TSV_F32 ? 4 : 2; }
+
+size_t partial_bytes(const Dims& d, int k_max) {
+  return round_up((size_t)d.B * d.Hq * tsv::decode_splits(d, k_max) *
+                  tsv::partial_stride(d) * sizeof(float));
+}
+
+size_t sel_phys_bytes(const Dims& d, int k_max) {
+  return round_up((size_t)d.B * d.Hkv * k_max * sizeof(int32_t));
+}
+
+int check_select_args(const Dims&, const float* q, const void* meta,
+                      const int32_t* bt, const int32_t* seq_lens, int32_t k_max,
+                      int32_t n_sink, const int32_t* sel,
+                      const int32_t* sel_count) {
+  if (!q || !meta || !bt || !seq_lens || !sel || !sel_count)
+    return TSV_ERR_INVALID_ARG;
+  if (k_max < 1 || n_sink < 0 || n_sink > k_max) return TSV_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(meta, 16)) return TSV_ERR_INVALID_ARG;
+  return TSV_OK;
+}
+
+int check_decode_args(const Dims& d, const float* q, const void* k_pool,
+                      const void* v_pool, const int32_t* bt,
+                      const int32_t* seq_lens, const int32_t* sel,
+                      const int32_t* sel_count, int32_t k_max, const float* out,
+                      const void* ws, size_t ws_bytes, bool need_phys) {
+  if (!q || !k_pool || !v_pool || !bt || !seq_lens || !sel || !sel_count ||
+      !out || !ws)
+    return TSV_ERR_INVALID_ARG;
+  if (k_max < 1) return TSV_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16) ||
+      !aligned(out, 16) || !aligned(ws, 16))
+    return TSV_ERR_INVALID_ARG;
+  size_t need = partial_bytes(d, k_max) + (need_phys ? sel_phys_bytes(d, k_max) : 0);
+  if (ws_bytes < need) return TSV_ERR_INVALID_ARG;
+  return TSV_OK;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? TSV_OK : TSV_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int tsv_version(void) { return TSV_VERSION; }
+
+const char* tsv_status_string(int status) {
+  switch (status) {
+    case TSV_OK: return "ok";
+    case TSV_ERR_INVALID_ARG: return "invalid argument";
+    case TSV_ERR_UNSUPPORTED: return "unsupported shape or dtype";
+    case TSV_ERR_HIP: return "HIP launch error";
+  }
+  return "unknown status";
+}
+
+size_t tsv_meta_bytes(const tsv_shape* shape) {
+  Dims d;
+  if (check_shape(shape, &d) != TSV_OK) return 0;
+  return (size_t)d.NP * d.Hkv * 2 * d.D * elem_bytes(d);
+}
+
+size_t tsv_workspace_bytes(const tsv_shape* shape, int32_t k_max) {
+  Dims d;
+  if (check_shape(shape, &d) != TSV_OK || k_max < 1) return 0;
+  return partial_bytes(d, k_max) + sel_phys_bytes(d, k_max);
+}
+
+int tsv_meta_build(const tsv_shape* shape, const void* k_pool, void* meta,
+                   const int32_t* block_table, const int32_t* seq_lens,
+                   void* stream) {
+  Dims d;
+  int rc = check_shape(shape, &d);
+  if (rc) return rc;
+  if (!k_pool || !meta || !block_table || !seq_lens) return TSV_ERR_INVALID_ARG;
+  return hip_status(tsv::launch_meta_build(d, k_pool, meta, block_table, seq_lens,
+                                           (hipStream_t)stream));
+}
+
+int tsv_meta_append(const tsv_shape* shape, const void* k_new, const void* v_new,
+                    void* k_pool, void* v_pool, void* meta,
+                    const int32_t* block_table, const int32_t* seq_lens,
+                    void* stream) {
+  Dims d;
+  int rc = check_shape(shape, &d);
+  if (rc) return rc;
+  if (!k_new || !v_new || !k_pool || !v_pool || !meta || !block_table || !seq_lens)
+    return TSV_ERR_INVALID_ARG;
+  return hip_status(tsv::launch_meta_append(d, k_new, v_new, k_pool, v_pool, meta,
+                                            block_table, seq_lens,
+                                            (hipStream_t)stream));
+}
+
+int tsv_select_pages(const tsv_shape* shape, const float* q, const void* meta,
+                     const int32_t* block_table, const int32_t* seq_lens,
+                     int32_t k_max, const int32_t* k_per_seq, int32_t n_sink,
+                     int32_t* sel, int32_t* sel_count, float* scores_out,
+                     void* stream) {
+  Dims d;
+  int rc = check_shape(shape, &d);
+  if (rc) return rc;
+  rc = check_select_args(d, q, meta, block_table, seq_lens, k_max, n_sink, sel,
+                         sel_count);
+  if (rc) return rc;
+  return hip_status(tsv::launch_score_select(d, q, meta, block_table, seq_lens, k_max,
+                                             k_per_seq, n_sink, sel, sel_count,
+                                             nullptr, scores_out,
+                                             (hipStream_t)stream));
+}
+
+int tsv_sparse_decode(const tsv_shape* shape, const float* q, const void* k_pool,
+                      const void* v_pool, const int32_t* block_table,
+                      const int32_t* seq_lens, const int32_t* sel,
+                      const int32_t* sel_count, int32_t k_max, float scale,
+                      float* out, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+  Dims d;
+  int rc = check_shape(shape, &d);
+  if (rc) return rc;
+  rc = check_decode_args(d, q, k_pool, v_pool, block_table, seq_lens, sel,
+                         sel_count, k_max, out, workspace, workspace_bytes, false);
+  if (rc) return rc;
+  return hip_status(tsv::launch_decode(d, q, k_pool, v_pool, block_table, seq_lens,
+                                       sel, nullptr, sel_count, k_max, scale,
+                                       static_cast<float*>(workspace), out,
+                                       (hipStream_t)stream));
+}
+
+int tsv_decode_step(const tsv_shape* shape, const float* q, const void* k_new,
+                    const void* v_new, void* k_pool, void* v_pool, void* meta,
+                    const int32_t* block_table, const int32_t* seq_lens,
+                    int32_t k_max, const int32_t* k_per_seq, int32_t n_sink,
+                    float scale, int32_t* sel, int32_t* sel_count,
+                    float* scores_out, float* out, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  Dims d;
+  int rc = check_shape(shape, &d);
+  if (rc) return rc;
+  if ((k_new == nullptr) != (v_new == nullptr)) return TSV_ERR_INVALID_ARG;
+  rc = check_select_args(d, q, meta, block_table, seq_lens, k_max, n_sink, sel,
+                         sel_count);
+  if (rc) return rc;
+  rc = check_decode_args(d, q, k_pool, v_pool, block_table, seq_lens, sel,
+                         sel_count, k_max, out, workspace, workspace_bytes, true);
+  if (rc) return rc;
+  hipStream_t s = (hipStream_t)stream;
+  float* partials = static_cast<float*>(workspace);
+  int32_t* sel_phys = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) +
+                                                 partial_bytes(d, k_max));
+  if (k_new) {
+    rc = hip_status(tsv::launch_meta_append(d, k_new, v_new, k_pool, v_pool, meta,
+                                            block_table, seq_lens, s));
+    if (rc) return rc;
+  }
+  rc = hip_status(tsv::launch_score_select(d, q, meta, block_table, seq_lens, k_max,
+                                           k_per_seq, n_sink, sel, sel_count,
+                                           sel_phys, scores_out, s));
+  if (rc) return rc;
+  return hip_status(tsv::launch_decode(d, q, k_pool, v_pool, block_table, seq_lens,
+                                       sel, sel_phys, sel_count, k_max, scale,
+                                       partials, out, s));
+}
+
+}  // extern "C"

@@ -1,0 +1,122 @@
+"""Host-side checks of the C ABI (no GPU needed, no kernel launched).
+
+The library must load, export every function include/tsv.h declares, report
+sizes, and reject bad arguments before making any HIP call.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tsv.h")
+
+
+@pytest.fixture(scope="module")
+def tsv():
+    from query_aware_sparse_bbox_amd import build as b
+    if not os.path.exists(b.LIB):
+        b.build()
+    import query_aware_sparse_bbox_amd as m
+    return m
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:int|size_t|const char\*)\s+(tsv_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ("tsv_meta_append", "tsv_select_pages", "tsv_sparse_decode", "tsv_decode_step",
+              "tsv_meta_build", "tsv_workspace_bytes", "tsv_meta_bytes", "tsv_status_string",
+              "tsv_version"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(tsv):
+    out = subprocess.run(["nm", "-D", "--defined-only", tsv.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r" T (tsv_\w+)$", out, re.M))
+    for n in declared_functions():
+        assert n in exported, n
+        assert getattr(tsv._lib, n)
+    assert set(tsv.EXPORTS) == set(declared_functions())
+
+
+def test_library_is_built_for_gfx950(tsv):
+    """The embedded device code targets gfx950 and nothing else."""
+    data = open(tsv.LIB_PATH, "rb").read()
+    targets = set(re.findall(rb"amdgcn-amd-amdhsa-+(gfx\w+)", data))
+    assert targets == {b"gfx950"}
+
+
+def test_version_and_status_strings(tsv):
+    assert tsv.tsv_version() == 1
+    assert tsv.status_string(0) == "ok"
+    assert "invalid" in tsv.status_string(-1)
+    assert "unsupported" in tsv.status_string(-2)
+
+
+def shape(**kw):
+    base = dict(batch=2, num_q_heads=8, num_kv_heads=2, head_dim=64, page_size=16,
+                max_pages_per_seq=10, num_phys_pages=20, kv_dtype=2)
+    base.update(kw)
+    from query_aware_sparse_bbox_amd import Shape
+    return Shape(**base)
+
+
+def test_sizes(tsv):
+    s = shape()
+    assert tsv.tsv_meta_bytes(s) == 20 * 2 * 2 * 64 * 2
+    assert tsv.tsv_meta_bytes(shape(kv_dtype=0)) == 20 * 2 * 2 * 64 * 4
+    ws = tsv.tsv_workspace_bytes(s, 8)
+    assert ws > 0 and ws % 256 == 0
+    assert tsv.tsv_workspace_bytes(s, 16) >= ws
+    assert tsv.tsv_workspace_bytes(s, 0) == 0
+    assert tsv.tsv_meta_bytes(shape(head_dim=96)) == 0
+    assert tsv.tsv_meta_bytes(shape(num_q_heads=7)) == 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(head_dim=96), -2), (dict(head_dim=32), -2), (dict(page_size=12), -2),
+    (dict(kv_dtype=7), -2), (dict(num_q_heads=24, num_kv_heads=8), -2),  # G = 3
+    (dict(num_q_heads=7), -1), (dict(batch=0), -1), (dict(num_phys_pages=0), -1),
+    (dict(max_pages_per_seq=5000), -2),
+])
+def test_bad_shapes_rejected_before_any_hip_call(tsv, kw, status):
+    s = shape(**kw)
+    fake = ctypes.c_void_p(1 << 20)  # never dereferenced: rejected first
+    rc = tsv._lib.tsv_select_pages(ctypes.byref(s), fake, fake, fake, fake, 4, None, 0,
+                                   fake, fake, None, None)
+    assert rc == status
+
+
+def test_bad_arguments_rejected_before_any_hip_call(tsv):
+    s = shape()
+    f = ctypes.c_void_p(1 << 20)
+    L = tsv._lib
+    # null required pointers
+    assert L.tsv_select_pages(ctypes.byref(s), None, f, f, f, 4, None, 0, f, f, None, None) == -1
+    assert L.tsv_meta_build(ctypes.byref(s), f, None, f, f, None) == -1
+    assert L.tsv_meta_append(ctypes.byref(s), f, None, f, f, f, f, f, None) == -1
+    # k_max / n_sink
+    assert L.tsv_select_pages(ctypes.byref(s), f, f, f, f, 0, None, 0, f, f, None, None) == -1
+    assert L.tsv_select_pages(ctypes.byref(s), f, f, f, f, 4, None, 5, f, f, None, None) == -1
+    assert L.tsv_select_pages(ctypes.byref(s), f, f, f, f, 4, None, -1, f, f, None, None) == -1
+    # misaligned q
+    mis = ctypes.c_void_p((1 << 20) + 4)
+    assert L.tsv_select_pages(ctypes.byref(s), mis, f, f, f, 4, None, 0, f, f, None, None) == -1
+    # workspace too small
+    need = L.tsv_workspace_bytes(ctypes.byref(s), 4)
+    assert L.tsv_sparse_decode(ctypes.byref(s), f, f, f, f, f, f, f, 4, ctypes.c_float(0.1), f,
+                               f, need // 2, None) == -1
+    assert L.tsv_decode_step(ctypes.byref(s), f, f, f, f, f, f, f, f, 4, None, 0,
+                             ctypes.c_float(0.1), f, f, None, f, f, need - 1, None) == -1
+    # k_new without v_new
+    assert L.tsv_decode_step(ctypes.byref(s), f, f, None, f, f, f, f, f, 4, None, 0,
+                             ctypes.c_float(0.1), f, f, None, f, f, need, None) == -1
+    # null shape
+    assert L.tsv_meta_build(None, f, f, f, f, None) == -1

@@ -1,0 +1,173 @@
+"""HIP path vs the CPU oracle, element by element, through the C ABI.
+
+Bars: page boxes equal by value, page scores bit-equal (-0 stored as +0),
+selections and counts bit-exact, outputs within max-abs 1e-5 (fp32 KV) or
+2e-3 (fp16 / bf16 KV).  The five decode configurations run at their full
+sizes in the launch configuration the benchmark times; smaller variants add
+ragged tails, several tiles per row and the method's degenerate cases.
+"""
+import numpy as np
+import pytest
+
+import workloads as W
+from gpu_harness import compare, gpu_run, oracle_run, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _case(wl, **kw):
+    say(f"[case] {wl.name} shape={wl.shape} kw={kw}")
+    o = oracle_run(wl, **kw)
+    say("  oracle done")
+    g = gpu_run(wl, **kw)
+    say("  gpu done")
+    err = compare(wl, g, o, step=kw.get("step", 0))
+    say(f"  max-abs err {err:.3e}")
+    return g, o
+
+
+@pytest.mark.parametrize("name", W.CONFIG_ORDER)
+def test_full_config(name):
+    wl = W.make(name)
+    _case(wl)
+
+
+@pytest.mark.parametrize("name,kw", [
+    ("tiny", dict(context=1000)),
+    ("tiny", dict(context=17, kv_dtype=W.BF16)),
+    ("tinyllama", dict(batch=3, context=1001)),
+    ("tinyllama", dict(batch=2, context=333, num_q_heads=8, num_kv_heads=4)),  # G = 2
+    ("gpt2", dict(batch=5, context=999)),
+    ("gpt2", dict(batch=3, context=500, head_dim=128, kv_dtype=W.F32)),
+    ("llama_long", dict(batch=2, context=5000)),
+    ("llama_long", dict(batch=2, context=3000, page_size=64, kv_dtype=W.F16)),
+    ("llama_long", dict(batch=2, context=3000, page_size=8)),
+    ("ragged", dict(batch=8, lens_range=(1, 3000))),
+    ("ragged", dict(batch=6, lens_range=(100, 2000), kv_dtype=W.BF16, num_q_heads=64)),
+])
+def test_small_variants(name, kw):
+    wl = W.make(name, **kw)
+    _case(wl)
+
+
+@pytest.mark.parametrize("dtype", [W.F32, W.F16, W.BF16])
+@pytest.mark.parametrize("G", [1, 4])
+def test_tie_heavy(dtype, G):
+    wl = W.tie_heavy(31 + G, kv_dtype=dtype, num_q_heads=2 * G, num_kv_heads=2, context=777,
+                     k_max=9, n_sink=1, value_range=2)
+    g, o = _case(wl)
+    # ties must actually occur among the scores for the case to mean anything
+    sc = o["scores"][:, :, :49]
+    assert max(len(v) - len(set(v.tolist())) for v in sc.reshape(-1, 49)) > 5
+
+
+def test_poisoned_unused_slots():
+    for name, kw in [("gpt2", dict(batch=4, context=301)),
+                     ("ragged", dict(batch=8, lens_range=(5, 900)))]:
+        wl = W.make(name, **kw)
+        W.poison_unused(wl)
+        g, _ = _case(wl)
+        assert np.all(np.isfinite(g["out"]))
+
+
+def test_all_pages_is_dense_attention():
+    wl = W.make("tinyllama", batch=2, context=1500)
+    _case(wl, k_max=wl.shape.max_pages_per_seq)
+    wl = W.make("ragged", batch=4, lens_range=(50, 1200), append_steps=0)
+    _case(wl, k_max=wl.shape.max_pages_per_seq, k_per_seq=None)
+
+
+def test_three_calls_equal_fused_step():
+    wl = W.make("ragged", batch=8, lens_range=(100, 4000))
+    a = gpu_run(wl)
+    b = gpu_run(wl, separate=True)
+    for k in ("sel", "cnt", "out", "meta", "k_pool", "v_pool"):
+        assert np.array_equal(a[k], b[k]), k
+
+
+def test_bitwise_deterministic():
+    wl = W.make("tinyllama", batch=4, context=2048)
+    a, b = gpu_run(wl), gpu_run(wl)
+    assert np.array_equal(a["out"].view(np.uint32), b["out"].view(np.uint32))
+    assert np.array_equal(a["scores"].view(np.uint32), b["scores"].view(np.uint32))
+
+
+def test_split_count_does_not_change_result():
+    """A wider sel row (more split slots) with the same budgets gives identical bits."""
+    wl = W.make("llama_long", batch=2, context=4000)
+    kp = np.full(wl.shape.batch, wl.k_max, dtype=np.int32)
+    a = gpu_run(wl, k_max=wl.k_max, k_per_seq=kp)
+    b = gpu_run(wl, k_max=wl.k_max + 40, k_per_seq=kp)
+    assert np.array_equal(a["out"].view(np.uint32), b["out"].view(np.uint32))
+    assert np.array_equal(a["sel"], b["sel"][:, :, :wl.k_max])
+
+
+def test_degenerate_lengths_and_budgets():
+    wl = W.make("tinyllama", batch=5, context=300)
+    wl.seq_lens = np.array([0, 1, 16, 17, 300], dtype=np.int32)
+    g, o = _case(wl, k_max=3, k_per_seq=np.array([9, 0, 1, 2, 3], np.int32), n_sink=1)
+    assert g["cnt"][0].tolist() == [0, 0, 0, 0] and np.all(g["out"][0] == 0)
+    _case(wl, k_max=2, k_per_seq=None, n_sink=2)   # every slot forced
+    _case(wl, k_max=40, k_per_seq=None, n_sink=0)  # K > n for every row
+
+
+def test_permuted_pool_same_selection():
+    a = W.make("tinyllama", batch=3, context=900)
+    b = W.make("tinyllama", batch=3, context=900, layout="permuted")
+    for bb in range(a.shape.batch):
+        for p in range(a.shape.max_pages_per_seq):
+            b.k_pool[b.block_table[bb, p]] = a.k_pool[a.block_table[bb, p]]
+            b.v_pool[b.block_table[bb, p]] = a.v_pool[a.block_table[bb, p]]
+    b.q = a.q
+    ga, gb = gpu_run(a), gpu_run(b)
+    assert np.array_equal(ga["sel"], gb["sel"])
+    assert np.array_equal(ga["out"].view(np.uint32), gb["out"].view(np.uint32))
+
+
+def test_ragged_appends_seventeen_steps():
+    """17 consecutive appends cover every slot residue mod 16 and page opens."""
+    import torch
+
+    import oracle as O
+    import query_aware_sparse_bbox_amd as T
+    from workloads import device as WD
+
+    wl = W.make("ragged", batch=16, append_steps=17)
+    sh = wl.shape
+    say(f"[case] ragged appends shape={sh}")
+    d = WD.upload(wl)
+    kp, vp = wl.k_pool.copy(), wl.v_pool.copy()
+    lens0 = wl.steps[0].seq_lens - 1
+    meta_o = O.meta_build(sh, kp, wl.block_table, lens0)
+    T.tsv_meta_build(sh, d.k_pool, d.meta, d.block_table, WD.i32(lens0))
+    B, Hq, Hkv, D = sh.batch, sh.num_q_heads, sh.num_kv_heads, sh.head_dim
+    sel = torch.empty((B, Hkv, wl.k_max), dtype=torch.int32, device="cuda")
+    cnt = torch.empty((B, Hkv), dtype=torch.int32, device="cuda")
+    sc = torch.empty((B, Hkv, sh.max_pages_per_seq), dtype=torch.float32, device="cuda")
+    out = torch.empty((B, Hq, D), dtype=torch.float32, device="cuda")
+    ws = torch.empty(T.tsv_workspace_bytes(sh, wl.k_max), dtype=torch.uint8, device="cuda")
+    for i, st in enumerate(wl.steps):
+        so, co, sco, oo = O.decode_step(sh, st.q, kp, vp, meta_o, wl.block_table, st.seq_lens,
+                                        wl.k_max, wl.scale, st.k_per_seq, 0, st.k_new, st.v_new)
+        T.tsv_decode_step(sh, torch.from_numpy(st.q).cuda(), WD.kv_tensor(st.k_new, sh.kv_dtype),
+                          WD.kv_tensor(st.v_new, sh.kv_dtype), d.k_pool, d.v_pool, d.meta,
+                          d.block_table, WD.i32(st.seq_lens), wl.k_max, WD.i32(st.k_per_seq), 0,
+                          wl.scale, sel, cnt, sc, out, ws)
+        torch.cuda.synchronize()
+        g = dict(meta=WD.kv_numpy(d.meta, sh.kv_dtype), sel=sel.cpu().numpy(),
+                 cnt=cnt.cpu().numpy(), scores=sc.cpu().numpy(), out=out.cpu().numpy())
+        o = dict(meta=meta_o, sel=so, cnt=co, scores=sco, out=oo)
+        err = compare(wl, g, o, step=i)
+        say(f"  step {i}: max-abs err {err:.3e}")
+    # the incrementally kept boxes equal a rebuild from the pool
+    rebuilt = torch.zeros_like(d.meta)
+    T.tsv_meta_build(sh, d.k_pool, rebuilt, d.block_table, WD.i32(wl.steps[-1].seq_lens))
+    torch.cuda.synchronize()
+    n = (wl.steps[-1].seq_lens + 15) // 16
+    a, r = WD.kv_numpy(d.meta, sh.kv_dtype), WD.kv_numpy(rebuilt, sh.kv_dtype)
+    for b in range(B):
+        phys = wl.block_table[b, :n[b]]
+        assert np.array_equal(W.storage_to_f32(a[phys], sh.kv_dtype),
+                              W.storage_to_f32(r[phys], sh.kv_dtype))
+    assert np.array_equal(WD.kv_numpy(d.k_pool, sh.kv_dtype), kp)
+    assert np.array_equal(WD.kv_numpy(d.v_pool, sh.kv_dtype), vp)

@@ -29,6 +29,8 @@ the token being decoded).
 from __future__ import annotations
 
 import math
+import os
+from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass, field, replace
 from typing import Optional
 
@@ -99,8 +101,9 @@ def to_storage(x: np.ndarray, dtype: int) -> np.ndarray:
     if dtype == F16:
         return x.astype(np.float16)
     if dtype == BF16:
-        u = x.view(np.uint32).astype(np.uint64)
-        u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+        # RNE on the bit pattern; cannot wrap for finite values or default NaNs
+        u = x.view(np.uint32)
+        u = (u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)
         return u.astype(np.uint16)
     raise ValueError(f"unknown kv dtype {dtype}")
 
@@ -220,21 +223,34 @@ def generate(spec: Spec, seed: int) -> Workload:
     dt = spec.kv_dtype
     k_pool = np.zeros((NP, Hkv, P, D), dtype=STORAGE_NP[dt])
     v_pool = np.zeros((NP, Hkv, P, D), dtype=STORAGE_NP[dt])
-    centroids = []
-    for b in range(B):
+    # every sequence draws from its own child stream, so the result does not
+    # depend on how many threads fill the pool
+    seq_seeds = np.random.SeedSequence(seed).spawn(B)
+    centroids = [None] * B
+
+    def fill(b):
+        r = np.random.Generator(np.random.PCG64(seq_seeds[b]))
         # centroids for every page the sequence will ever own (appends that
         # open a page use that page's own fresh centroid)
         nc = int(cap_pages[b])
-        c = (spec.centroid_sigma *
-             rng.standard_normal((Hkv, nc, D), dtype=np.float32))
-        centroids.append(c)
+        c = spec.centroid_sigma * r.standard_normal((Hkv, nc, D), dtype=np.float32)
+        centroids[b] = c
         npre = int((lens0[b] + P - 1) // P)        # pages holding the prefix
-        noise = rng.standard_normal((Hkv, npre, P, D), dtype=np.float32)
-        keys = c[:, :npre, None, :] + np.float32(spec.noise_sigma) * noise
-        vals = rng.standard_normal((Hkv, npre, P, D), dtype=np.float32)
+        keys = r.standard_normal((Hkv, npre, P, D), dtype=np.float32)
+        keys *= np.float32(spec.noise_sigma)
+        keys += c[:, :npre, None, :]
+        vals = r.standard_normal((Hkv, npre, P, D), dtype=np.float32)
         phys = bt[b, :npre]
         k_pool[phys] = to_storage(keys, dt).transpose(1, 0, 2, 3)
         v_pool[phys] = to_storage(vals, dt).transpose(1, 0, 2, 3)
+
+    workers = max(1, min(8, os.cpu_count() or 1, B))
+    if workers == 1:
+        for b in range(B):
+            fill(b)
+    else:
+        with ThreadPoolExecutor(workers) as ex:
+            list(ex.map(fill, range(B)))
 
     shape = Shape(B, Hq, Hkv, D, P, MP, NP, dt)
     n_first = (first_lens + P - 1) // P
