@@ -121,7 +121,6 @@ def main():
     v_new = WD.kv_tensor(st.v_new, sh.kv_dtype) if st else None
     k_max, n_sink, scale = wl.k_max, wl.n_sink, wl.scale
     B, Hq, Hkv, D, MP = sh.batch, sh.num_q_heads, sh.num_kv_heads, sh.head_dim, sh.max_pages_per_seq
-    ws_bytes = T.tsv_workspace_bytes(sh, k_max)
 
     def instance():
         d = WD.upload(wl, dev)
@@ -129,7 +128,7 @@ def main():
         d.sel = torch.empty((B, Hkv, k_max), dtype=torch.int32, device=dev)
         d.cnt = torch.empty((B, Hkv), dtype=torch.int32, device=dev)
         d.out = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
-        d.ws = torch.zeros(ws_bytes, dtype=torch.uint8, device=dev)
+        d.ws = T.new_workspace(sh, k_max, dev)
         return d
 
     def step(d):
@@ -244,7 +243,7 @@ def main():
         "step_algorithmic_bytes": nb["total"],
         "step_hbm_gbs": step_gbs,
         "step_frac_of_peak": step_gbs / PEAK_HBM_GBS,
-        "roofline": {"bound": "hbm", "kernel": "k_decode_split + k_merge",
+        "roofline": {"bound": "hbm", "kernel": "k_decode_split",
                      "achieved": dec_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": dec_gbs / PEAK_HBM_GBS, "traffic": None,
                      "algorithmic_bytes_per_launch": nb["decode_kernel"],

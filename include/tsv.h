@@ -79,7 +79,8 @@ typedef struct {
 enum {
   TSV_OK = 0,
   /* null pointer, non-positive size, Hq % Hkv != 0, k_max < 1,
-     n_sink outside [0, k_max], misaligned pointer, workspace too small */
+     n_sink outside [0, k_max], misaligned pointer, workspace too small or
+     not 256-byte aligned */
   TSV_ERR_INVALID_ARG = -1,
   /* head_dim not 64/128, page_size not 8/16/32/64, G not 1/2/4/8,
      unknown dtype, max_pages_per_seq > 4096 */
@@ -98,10 +99,13 @@ const char* tsv_status_string(int status);
    0 when the shape is invalid or unsupported. */
 size_t tsv_meta_bytes(const tsv_shape* shape);
 
-/* Bytes of scratch tsv_sparse_decode / tsv_decode_step need for rows of
-   k_max selected pages; 0 when the shape is invalid or unsupported.  The
-   workspace holds partial softmax states of the split decode and needs no
-   initialisation. */
+/* Bytes of the caller-owned scratch that tsv_select_pages,
+   tsv_sparse_decode and tsv_decode_step need for rows of k_max selected
+   pages; 0 when the shape is invalid or unsupported.  The workspace holds the
+   page-score keys, the selected pages' physical indices and the split
+   decode's partial softmax states.  It must be 256-byte aligned and needs no
+   initialisation; calls that may run at the same time (different streams)
+   need separate workspaces. */
 size_t tsv_workspace_bytes(const tsv_shape* shape, int32_t k_max);
 
 /* Rebuild the bounding box of every page p < n_b of every sequence from the
@@ -134,19 +138,21 @@ int tsv_meta_append(const tsv_shape* shape, const void* k_new,
    kept (attention-sink pages, counted inside the budget); the remaining
    min(K_b, n_b) - that slots go to the highest scores, equal scores to the
    lower logical page.  sel gets the chosen logical pages in ascending order,
-   -1 padded to k_max; sel_count the number chosen.  scores_out may be NULL. */
+   -1 padded to k_max; sel_count the number chosen.  scores_out may be NULL.
+   `workspace` of at least tsv_workspace_bytes(shape, k_max) bytes. */
 int tsv_select_pages(const tsv_shape* shape, const float* q, const void* meta,
                      const int32_t* block_table, const int32_t* seq_lens,
                      int32_t k_max, const int32_t* k_per_seq, int32_t n_sink,
                      int32_t* sel, int32_t* sel_count, float* scores_out,
-                     void* stream);
+                     void* workspace, size_t workspace_bytes, void* stream);
 
 /* Masked softmax attention of every query head over the valid tokens of its
    KV head's selected pages only (abstract: masked attention over the loaded
    pages): out = sum_t softmax(scale * q.k_t) v_t.  Tokens at or past len_b
    are never read.  Entries of sel must be pages < n_b; with sel = every page
    this is dense paged decode.  fp32 arithmetic; `workspace` of at least
-   tsv_workspace_bytes(shape, k_max) bytes. */
+   tsv_workspace_bytes(shape, k_max) bytes.  The result does not depend on
+   how the work is split: every output element is bitwise reproducible. */
 int tsv_sparse_decode(const tsv_shape* shape, const float* q,
                       const void* k_pool, const void* v_pool,
                       const int32_t* block_table, const int32_t* seq_lens,

@@ -56,7 +56,8 @@ _SIGS = {
     "tsv_workspace_bytes": ([_SP, _I], _Z),
     "tsv_meta_build": ([_SP, _P, _P, _P, _P, _P], ctypes.c_int),
     "tsv_meta_append": ([_SP, _P, _P, _P, _P, _P, _P, _P, _P], ctypes.c_int),
-    "tsv_select_pages": ([_SP, _P, _P, _P, _P, _I, _P, _I, _P, _P, _P, _P], ctypes.c_int),
+    "tsv_select_pages": ([_SP, _P, _P, _P, _P, _I, _P, _I, _P, _P, _P, _P, _Z, _P],
+                         ctypes.c_int),
     "tsv_sparse_decode": ([_SP, _P, _P, _P, _P, _P, _P, _P, _I, _F, _P, _P, _Z, _P],
                           ctypes.c_int),
     "tsv_decode_step": ([_SP, _P, _P, _P, _P, _P, _P, _P, _P, _I, _P, _I, _F, _P, _P, _P,
@@ -123,10 +124,20 @@ def tsv_meta_append(shape, k_new, v_new, k_pool, v_pool, meta, block_table, seq_
 
 
 def tsv_select_pages(shape, q, meta, block_table, seq_lens, k_max, k_per_seq, n_sink,
-                     sel, sel_count, scores_out=None, stream=None):
+                     sel, sel_count, scores_out, workspace, stream=None):
     _call("tsv_select_pages", ctypes.byref(Shape.of(shape)), _ptr(q), _ptr(meta),
           _ptr(block_table), _ptr(seq_lens), int(k_max), _ptr(k_per_seq), int(n_sink),
-          _ptr(sel), _ptr(sel_count), _ptr(scores_out), _stream(stream))
+          _ptr(sel), _ptr(sel_count), _ptr(scores_out), _ptr(workspace),
+          workspace.numel() * workspace.element_size(), _stream(stream))
+
+
+def new_workspace(shape, k_max, device="cuda"):
+    """A workspace of tsv_workspace_bytes(shape, k_max) bytes (no initialisation needed)."""
+    import torch
+    n = tsv_workspace_bytes(shape, k_max)
+    if n == 0:
+        raise ValueError("shape or k_max not supported")
+    return torch.empty(n, dtype=torch.uint8, device=device)
 
 
 def tsv_sparse_decode(shape, q, k_pool, v_pool, block_table, seq_lens, sel, sel_count,

@@ -10,10 +10,6 @@ namespace {
 
 using tsv::Dims;
 
-constexpr size_t kAlign = 256;
-
-size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
-
 bool aligned(const void* p, size_t a) {
   return (reinterpret_cast<uintptr_t>(p) % a) == 0;
 }
@@ -52,41 +48,35 @@ int check_shape(const tsv_shape* s, Dims* d) {
 
 size_t elem_bytes(const Dims& d) { return d.dt == TSV_F32 ? 4 : 2; }
 
-size_t partial_bytes(const Dims& d, int k_max) {
-  return round_up((size_t)d.B * d.Hq * tsv::decode_splits(d, k_max) *
-                  tsv::partial_stride(d) * sizeof(float));
+int check_workspace(const Dims& d, int32_t k_max, const void* ws, size_t ws_bytes) {
+  if (!ws || !aligned(ws, 256)) return TSV_ERR_INVALID_ARG;
+  if (ws_bytes < tsv::workspace_layout(d, k_max, nullptr, nullptr)) return TSV_ERR_INVALID_ARG;
+  return TSV_OK;
 }
 
-size_t sel_phys_bytes(const Dims& d, int k_max) {
-  return round_up((size_t)d.B * d.Hkv * k_max * sizeof(int32_t));
-}
-
-int check_select_args(const Dims&, const float* q, const void* meta,
+int check_select_args(const Dims& d, const float* q, const void* meta,
                       const int32_t* bt, const int32_t* seq_lens, int32_t k_max,
-                      int32_t n_sink, const int32_t* sel,
-                      const int32_t* sel_count) {
+                      int32_t n_sink, const int32_t* sel, const int32_t* sel_count,
+                      const void* ws, size_t ws_bytes) {
   if (!q || !meta || !bt || !seq_lens || !sel || !sel_count)
     return TSV_ERR_INVALID_ARG;
   if (k_max < 1 || n_sink < 0 || n_sink > k_max) return TSV_ERR_INVALID_ARG;
   if (!aligned(q, 16) || !aligned(meta, 16)) return TSV_ERR_INVALID_ARG;
-  return TSV_OK;
+  return check_workspace(d, k_max, ws, ws_bytes);
 }
 
 int check_decode_args(const Dims& d, const float* q, const void* k_pool,
                       const void* v_pool, const int32_t* bt,
                       const int32_t* seq_lens, const int32_t* sel,
                       const int32_t* sel_count, int32_t k_max, const float* out,
-                      const void* ws, size_t ws_bytes, bool need_phys) {
-  if (!q || !k_pool || !v_pool || !bt || !seq_lens || !sel || !sel_count ||
-      !out || !ws)
+                      const void* ws, size_t ws_bytes) {
+  if (!q || !k_pool || !v_pool || !bt || !seq_lens || !sel || !sel_count || !out)
     return TSV_ERR_INVALID_ARG;
   if (k_max < 1) return TSV_ERR_INVALID_ARG;
   if (!aligned(q, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16) ||
-      !aligned(out, 16) || !aligned(ws, 16))
+      !aligned(out, 16))
     return TSV_ERR_INVALID_ARG;
-  size_t need = partial_bytes(d, k_max) + (need_phys ? sel_phys_bytes(d, k_max) : 0);
-  if (ws_bytes < need) return TSV_ERR_INVALID_ARG;
-  return TSV_OK;
+  return check_workspace(d, k_max, ws, ws_bytes);
 }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? TSV_OK : TSV_ERR_HIP; }
@@ -116,7 +106,7 @@ size_t tsv_meta_bytes(const tsv_shape* shape) {
 size_t tsv_workspace_bytes(const tsv_shape* shape, int32_t k_max) {
   Dims d;
   if (check_shape(shape, &d) != TSV_OK || k_max < 1) return 0;
-  return partial_bytes(d, k_max) + sel_phys_bytes(d, k_max);
+  return tsv::workspace_layout(d, k_max, nullptr, nullptr);
 }
 
 int tsv_meta_build(const tsv_shape* shape, const void* k_pool, void* meta,
@@ -148,17 +138,18 @@ int tsv_select_pages(const tsv_shape* shape, const float* q, const void* meta,
                      const int32_t* block_table, const int32_t* seq_lens,
                      int32_t k_max, const int32_t* k_per_seq, int32_t n_sink,
                      int32_t* sel, int32_t* sel_count, float* scores_out,
-                     void* stream) {
+                     void* workspace, size_t workspace_bytes, void* stream) {
   Dims d;
   int rc = check_shape(shape, &d);
   if (rc) return rc;
   rc = check_select_args(d, q, meta, block_table, seq_lens, k_max, n_sink, sel,
-                         sel_count);
+                         sel_count, workspace, workspace_bytes);
   if (rc) return rc;
+  tsv::Workspace ws;
+  tsv::workspace_layout(d, k_max, workspace, &ws);
   return hip_status(tsv::launch_score_select(d, q, meta, block_table, seq_lens, k_max,
                                              k_per_seq, n_sink, sel, sel_count,
-                                             nullptr, scores_out,
-                                             (hipStream_t)stream));
+                                             scores_out, ws, (hipStream_t)stream));
 }
 
 int tsv_sparse_decode(const tsv_shape* shape, const float* q, const void* k_pool,
@@ -171,11 +162,12 @@ int tsv_sparse_decode(const tsv_shape* shape, const float* q, const void* k_pool
   int rc = check_shape(shape, &d);
   if (rc) return rc;
   rc = check_decode_args(d, q, k_pool, v_pool, block_table, seq_lens, sel,
-                         sel_count, k_max, out, workspace, workspace_bytes, false);
+                         sel_count, k_max, out, workspace, workspace_bytes);
   if (rc) return rc;
+  tsv::Workspace ws;
+  tsv::workspace_layout(d, k_max, workspace, &ws);
   return hip_status(tsv::launch_decode(d, q, k_pool, v_pool, block_table, seq_lens,
-                                       sel, nullptr, sel_count, k_max, scale,
-                                       static_cast<float*>(workspace), out,
+                                       sel, nullptr, sel_count, k_max, scale, ws, out,
                                        (hipStream_t)stream));
 }
 
@@ -191,15 +183,14 @@ int tsv_decode_step(const tsv_shape* shape, const float* q, const void* k_new,
   if (rc) return rc;
   if ((k_new == nullptr) != (v_new == nullptr)) return TSV_ERR_INVALID_ARG;
   rc = check_select_args(d, q, meta, block_table, seq_lens, k_max, n_sink, sel,
-                         sel_count);
+                         sel_count, workspace, workspace_bytes);
   if (rc) return rc;
   rc = check_decode_args(d, q, k_pool, v_pool, block_table, seq_lens, sel,
-                         sel_count, k_max, out, workspace, workspace_bytes, true);
+                         sel_count, k_max, out, workspace, workspace_bytes);
   if (rc) return rc;
   hipStream_t s = (hipStream_t)stream;
-  float* partials = static_cast<float*>(workspace);
-  int32_t* sel_phys = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) +
-                                                 partial_bytes(d, k_max));
+  tsv::Workspace ws;
+  tsv::workspace_layout(d, k_max, workspace, &ws);
   if (k_new) {
     rc = hip_status(tsv::launch_meta_append(d, k_new, v_new, k_pool, v_pool, meta,
                                             block_table, seq_lens, s));
@@ -207,11 +198,11 @@ int tsv_decode_step(const tsv_shape* shape, const float* q, const void* k_new,
   }
   rc = hip_status(tsv::launch_score_select(d, q, meta, block_table, seq_lens, k_max,
                                            k_per_seq, n_sink, sel, sel_count,
-                                           sel_phys, scores_out, s));
+                                           scores_out, ws, s));
   if (rc) return rc;
   return hip_status(tsv::launch_decode(d, q, k_pool, v_pool, block_table, seq_lens,
-                                       sel, sel_phys, sel_count, k_max, scale,
-                                       partials, out, s));
+                                       sel, ws.sel_phys, sel_count, k_max, scale, ws,
+                                       out, s));
 }
 
 }  // extern "C"

@@ -231,7 +231,8 @@ __global__ __launch_bounds__(256) void k_meta_append(
 }
 
 // ---------------------------------------------------------------------------
-// K1: page scoring + top-K selection, one workgroup per (sequence, KV head)
+// K1: page scoring over (unit, page chunk) workgroups; the last chunk of a
+// unit to finish selects that unit's top-K
 // ---------------------------------------------------------------------------
 //
 // Lane layout of the scoring loop: a page's box row is 2*D*bytes; each lane
@@ -239,97 +240,35 @@ __global__ __launch_bounds__(256) void k_meta_append(
 // contiguous channels, so L = D/C lanes cover a page and one wave scores
 // 64/L pages per load.  Consecutive lanes read consecutive 16-byte pieces of
 // the same row, so every wave load is a run of whole 64/128-byte segments.
+// A workgroup scores CH = waves * (64/L) * U pages with all U rows of every
+// lane in flight at once.
 //
 // Term per channel: fma(qneg, mn, qpos*mx) with qpos = max(q,0),
 // qneg = min(q,0).  One of qpos/qneg is zero, so the result is the single
 // rounding of q*mx (q >= 0) or q*mn (q < 0), which is max(fl(q*mn), fl(q*mx))
 // because mn <= mx and rounding is monotone; zero signs can differ, which
 // only shows in an all-zero sum and -0 is stored as +0.
-template <int DT, int D, int G, int NT>
-__global__ __launch_bounds__(NT) void k_score_select(
-    const float* __restrict__ q, const void* __restrict__ meta,
-    const int32_t* __restrict__ bt, const int32_t* __restrict__ seq_lens,
-    int Hq, int Hkv, int P, int MP, int NP, int k_max,
-    const int32_t* __restrict__ k_per_seq, int n_sink,
-    int32_t* __restrict__ sel, int32_t* __restrict__ sel_count,
-    int32_t* __restrict__ sel_phys, float* __restrict__ scores_out) {
-  constexpr int EB = KV<DT>::bytes, C = KV<DT>::per16, L = D / C;
-  constexpr int PPW = kWave / L, NW = NT / kWave, PPB = NW * PPW, U = 4;
-  extern __shared__ uint32_t smem[];
-  uint32_t* s_phys = smem;       // [MP]
-  uint32_t* s_key = smem + MP;   // [MP]
-  __shared__ int s_hist[256];
-  __shared__ int s_tmp[NW];
-  __shared__ int s_bc[2];
+template <int DT, int D, int G>
+struct ScoreCfg {
+  static constexpr int EB = KV<DT>::bytes, C = KV<DT>::per16, L = D / C;
+  static constexpr int PPW = kWave / L;  // pages per wave per load
+  static constexpr int U = G >= 8 ? 1 : (G >= 4 ? 2 : 4);  // rows in flight per lane
+  static constexpr int NT = 256, NW = NT / kWave;
+  static constexpr int CH = NW * PPW * U;  // pages per workgroup
+};
 
-  const int unit = blockIdx.x, b = unit / Hkv, h = unit - b * Hkv;
+// Top-K of one unit from its n order keys in LDS: the first f pages always,
+// then the R = keff - f largest keys among pages [f, n), equal keys to the
+// lower page; writes the chosen pages ascending, -1 padding and the count.
+template <int NT>
+__device__ void select_from_keys(const uint32_t* s_key, int n, int keff, int f,
+                                 int k_max, const int32_t* __restrict__ bt_row,
+                                 int NP, int32_t* __restrict__ srow,
+                                 int32_t* __restrict__ prow,
+                                 int32_t* __restrict__ count, int* s_hist,
+                                 int* s_tmp, int* s_bc) {
+  constexpr int NW = NT / kWave;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
-  const int len = clampi(seq_lens[b], 0, MP * P);
-  const int n = (len + P - 1) / P;
-  for (int p = tid; p < n; p += NT)
-    s_phys[p] = (uint32_t)clampi(bt[(size_t)b * MP + p], 0, NP - 1);
-
-  const int chunk = lane % L, slot = lane / L;
-  float qp[G][C], qn[G][C];
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    const float* qg = q + ((size_t)b * Hq + h * G + g) * D + chunk * C;
-#pragma unroll
-    for (int c = 0; c < C; c += 4) {
-      const float4 x4 = *reinterpret_cast<const float4*>(qg + c);
-      const float xs[4] = {x4.x, x4.y, x4.z, x4.w};
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        qp[g][c + k] = xs[k] > 0.f ? xs[k] : 0.f;
-        qn[g][c + k] = xs[k] < 0.f ? xs[k] : 0.f;
-      }
-    }
-  }
-  __syncthreads();
-
-  const char* mb = reinterpret_cast<const char*>(meta);
-  for (int base = 0; base < n; base += PPB * U) {
-    uint4 rmn[U], rmx[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int p = base + u * PPB + wave * PPW + slot;
-      rmn[u] = make_uint4(0, 0, 0, 0);
-      rmx[u] = rmn[u];
-      if (p < n) {
-        const size_t row = ((size_t)s_phys[p] * Hkv + h) * 2 * D + chunk * C;
-        rmn[u] = ld16(mb + row * EB);
-        rmx[u] = ld16(mb + (row + D) * EB);
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int p = base + u * PPB + wave * PPW + slot;
-      float mn[C], mx[C];
-      unpack<DT>(rmn[u], mn);
-      unpack<DT>(rmx[u], mx);
-      float best = 0.f;
-#pragma unroll
-      for (int g = 0; g < G; ++g) {
-        float t[C];
-#pragma unroll
-        for (int c = 0; c < C; ++c)
-          t[c] = __builtin_fmaf(qn[g][c], mn[c], qp[g][c] * mx[c]);
-        const float s = group_sum<L>(tree_sum<C>(t));
-        best = g == 0 ? s : fmaxf(best, s);
-      }
-      best = best == 0.f ? 0.f : best;  // -0 -> +0
-      if (p < n && chunk == 0) {
-        s_key[p] = order_key(best);
-        if (scores_out) scores_out[(size_t)unit * MP + p] = best;
-      }
-    }
-  }
-  __syncthreads();
-
-  // ---- selection: forced sink pages + top-R candidates by (score, -page) ----
-  int kb = k_per_seq ? k_per_seq[b] : k_max;
-  kb = clampi(kb, 1, k_max);
-  const int keff = min(kb, n), f = min(n_sink, keff);
   const int R = keff - f, ncand = n - f;
   const bool take_all = R >= ncand, radix = R > 0 && R < ncand;
   uint32_t tau = 0;
@@ -394,28 +333,153 @@ __global__ __launch_bounds__(NT) void k_score_select(
     for (int p = p0; p < p1; ++p) cnt_local += chosen(p, r);
   }
   int pos = block_excl_scan<NW>(cnt_local, s_tmp, &total);
-  int32_t* srow = sel + (size_t)unit * k_max;
-  int32_t* prow = sel_phys ? sel_phys + (size_t)unit * k_max : nullptr;
   {
     int r = eq_rank0;
     for (int p = p0; p < p1; ++p)
       if (chosen(p, r)) {
         if (pos < k_max) {  // total never exceeds min(K_b, n_b); kept in bounds regardless
           srow[pos] = p;
-          if (prow) prow[pos] = (int32_t)s_phys[p];
+          prow[pos] = clampi(bt_row[p], 0, NP - 1);
         }
         ++pos;
       }
   }
   for (int i = total + tid; i < k_max; i += NT) {
     srow[i] = -1;
-    if (prow) prow[i] = 0;
+    prow[i] = 0;
   }
-  if (tid == 0) sel_count[unit] = min(total, k_max);
+  if (tid == 0) *count = min(total, k_max);
+}
+
+template <int DT, int D, int G>
+__global__ __launch_bounds__(256) void k_score_select(
+    const float* __restrict__ q, const void* __restrict__ meta,
+    const int32_t* __restrict__ bt, const int32_t* __restrict__ seq_lens,
+    int Hq, int Hkv, int P, int MP, int NP, int NC, int k_max,
+    const int32_t* __restrict__ k_per_seq, int n_sink,
+    int32_t* __restrict__ sel, int32_t* __restrict__ sel_count,
+    float* __restrict__ scores_out, uint32_t* __restrict__ keys,
+    int32_t* __restrict__ sel_phys) {
+  using Cfg = ScoreCfg<DT, D, G>;
+  constexpr int EB = Cfg::EB, C = Cfg::C, L = Cfg::L, PPW = Cfg::PPW, U = Cfg::U;
+  constexpr int NT = Cfg::NT, NW = Cfg::NW, CH = Cfg::CH, PPB = NW * PPW;
+  __shared__ uint32_t s_key[CH];
+  __shared__ uint32_t s_phys[CH];
+  __shared__ int s_hist[256];
+  __shared__ int s_tmp[NW];
+  __shared__ int s_bc[2];
+
+  const int unit = blockIdx.x / NC, c = blockIdx.x - unit * NC;
+  const int b = unit / Hkv, h = unit - b * Hkv;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  const int len = clampi(seq_lens[b], 0, MP * P);
+  const int n = (len + P - 1) / P;
+  const int nchunks = (n + CH - 1) / CH;
+  if (c >= max(nchunks, 1)) return;  // whole workgroup: no pages
+  const int p_base = c * CH;
+  const int npc = min(CH, n - p_base);  // <= 0 only for an empty sequence
+  const int32_t* bt_row = bt + (size_t)b * MP;
+  for (int i = tid; i < npc; i += NT) s_phys[i] = (uint32_t)clampi(bt_row[p_base + i], 0, NP - 1);
+
+  const int chunk = lane % L, slot = lane / L;
+  float qp[G][C], qn[G][C];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const float* qg = q + ((size_t)b * Hq + h * G + g) * D + chunk * C;
+#pragma unroll
+    for (int cc = 0; cc < C; cc += 4) {
+      const float4 x4 = *reinterpret_cast<const float4*>(qg + cc);
+      const float xs[4] = {x4.x, x4.y, x4.z, x4.w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        qp[g][cc + k] = xs[k] > 0.f ? xs[k] : 0.f;
+        qn[g][cc + k] = xs[k] < 0.f ? xs[k] : 0.f;
+      }
+    }
+  }
+  __syncthreads();
+
+  const char* mb = reinterpret_cast<const char*>(meta);
+  uint4 rmn[U], rmx[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int pl = u * PPB + wave * PPW + slot;
+    rmn[u] = make_uint4(0, 0, 0, 0);
+    rmx[u] = rmn[u];
+    if (pl < npc) {
+      const size_t row = ((size_t)s_phys[pl] * Hkv + h) * 2 * D + chunk * C;
+      rmn[u] = ld16(mb + row * EB);
+      rmx[u] = ld16(mb + (row + D) * EB);
+    }
+  }
+  uint32_t* krow = keys + (size_t)unit * MP;
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int pl = u * PPB + wave * PPW + slot;
+    float mn[C], mx[C];
+    unpack<DT>(rmn[u], mn);
+    unpack<DT>(rmx[u], mx);
+    float best = 0.f;
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      float t[C];
+#pragma unroll
+      for (int cc = 0; cc < C; ++cc)
+        t[cc] = __builtin_fmaf(qn[g][cc], mn[cc], qp[g][cc] * mx[cc]);
+      const float sc = group_sum<L>(tree_sum<C>(t));
+      best = g == 0 ? sc : fmaxf(best, sc);
+    }
+    best = best == 0.f ? 0.f : best;  // -0 -> +0
+    if (pl < npc && chunk == 0) {
+      const uint32_t key = order_key(best);
+      s_key[pl] = key;
+      if (nchunks > 1) krow[p_base + pl] = key;
+      if (scores_out) scores_out[(size_t)unit * MP + p_base + pl] = best;
+    }
+  }
+
+  // a unit that fits one chunk selects right here; longer units are selected
+  // by k_select once every chunk's keys are in memory
+  if (nchunks > 1) return;
+  __syncthreads();
+  int kb = k_per_seq ? k_per_seq[b] : k_max;
+  kb = clampi(kb, 1, k_max);
+  const int keff = min(kb, n), f = min(n_sink, keff);
+  select_from_keys<NT>(s_key, n, keff, f, k_max, bt_row, NP, sel + (size_t)unit * k_max,
+                       sel_phys + (size_t)unit * k_max, sel_count + unit, s_hist, s_tmp,
+                       s_bc);
+}
+
+// Selection of the units that span several score chunks: one workgroup per
+// (sequence, KV head) loads the unit's keys into LDS and runs the same top-K.
+template <int CH>
+__global__ __launch_bounds__(256) void k_select(
+    const int32_t* __restrict__ bt, const int32_t* __restrict__ seq_lens, int Hkv,
+    int P, int MP, int NP, int k_max, const int32_t* __restrict__ k_per_seq, int n_sink,
+    const uint32_t* __restrict__ keys, int32_t* __restrict__ sel,
+    int32_t* __restrict__ sel_count, int32_t* __restrict__ sel_phys) {
+  constexpr int NT = 256, NW = NT / kWave;
+  extern __shared__ uint32_t s_key[];  // [MP]
+  __shared__ int s_hist[256];
+  __shared__ int s_tmp[NW];
+  __shared__ int s_bc[2];
+  const int unit = blockIdx.x, b = unit / Hkv;
+  const int len = clampi(seq_lens[b], 0, MP * P);
+  const int n = (len + P - 1) / P;
+  if (n <= CH) return;  // selected by the score kernel
+  const uint32_t* krow = keys + (size_t)unit * MP;
+  for (int p = threadIdx.x; p < n; p += NT) s_key[p] = krow[p];
+  __syncthreads();
+  int kb = k_per_seq ? k_per_seq[b] : k_max;
+  kb = clampi(kb, 1, k_max);
+  const int keff = min(kb, n), f = min(n_sink, keff);
+  select_from_keys<NT>(s_key, n, keff, f, k_max, bt + (size_t)b * MP, NP,
+                       sel + (size_t)unit * k_max, sel_phys + (size_t)unit * k_max,
+                       sel_count + unit, s_hist, s_tmp, s_bc);
 }
 
 // ---------------------------------------------------------------------------
-// K2: split decode over the selected-token stream
+// K2: split decode over the selected-token stream, merge by the last tile
 // ---------------------------------------------------------------------------
 //
 // The selected pages of a (sequence, KV head), in sel order, form a stream of
@@ -426,6 +490,118 @@ __global__ __launch_bounds__(NT) void k_score_select(
 // flight.  Masked slots (past the length, or past the last selected page) are
 // never loaded: their V stays zero and their logit -inf, so a NaN in an
 // unused slot cannot reach the output.
+//
+// Each tile leaves (max, sum, acc[D]) per query head in `partials`; the last
+// tile of a unit to finish (arrival counter) merges them into `out`.  A unit
+// with one tile writes `out` directly; a unit with nothing selected gets zero
+// rows from its first tile slot.
+
+// K3: merge of the tiles' partial states of one (sequence, query head) per
+// wave, for units with more than one tile.  Lane s holds tile s's (max,
+// denominator); the weighted sums are read with all of a lane's loads in
+// flight together.
+template <int D>
+__global__ __launch_bounds__(256) void k_merge(
+    const float* __restrict__ partials, const int32_t* __restrict__ sel_count, int B,
+    int Hq, int Hkv, int G, int log2P, int k_max, int S_max, int tile,
+    float* __restrict__ out) {
+  constexpr int PER = D / kWave, UNR = 8;
+  const int gw = blockIdx.x * 4 + threadIdx.x / kWave;
+  const int lane = threadIdx.x & (kWave - 1);
+  if (gw >= B * Hq) return;
+  const int b = gw / Hq, hq = gw - b * Hq, h = hq / G;
+  const int cnt = clampi(sel_count[(size_t)b * Hkv + h], 0, k_max);
+  const int ns = (int)((((long)cnt << log2P) + tile - 1) / tile);
+  if (ns <= 1) return;  // finished by the decode tile itself
+  const float* base = partials + (size_t)gw * S_max * (D + 2);
+  // global max and denominator, 64 tiles per pass
+  float M = -INFINITY;
+  for (int s0 = 0; s0 < ns; s0 += kWave) {
+    const int s = s0 + lane;
+    float m = s < ns ? base[(size_t)s * (D + 2) + D] : -INFINITY;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+    M = fmaxf(M, m);
+  }
+  if (M == -INFINITY) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) out[(size_t)gw * D + lane + kWave * i] = 0.f;
+    return;
+  }
+  float l = 0.f;
+  for (int s0 = 0; s0 < ns; s0 += kWave) {
+    const int s = s0 + lane;
+    float t = 0.f;
+    if (s < ns) {
+      const float* ps = base + (size_t)s * (D + 2);
+      t = __builtin_amdgcn_exp2f(ps[D] - M) * ps[D + 1];
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) t += __shfl_xor(t, o);
+    l += t;
+  }
+  float acc[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) acc[i] = 0.f;
+  for (int s0 = 0; s0 < ns; s0 += UNR) {
+    float w[UNR], v[UNR][PER];
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      const int s = s0 + u;
+      const float* ps = base + (size_t)min(s, ns - 1) * (D + 2);
+      w[u] = s < ns ? ps[D] : -INFINITY;
+#pragma unroll
+      for (int i = 0; i < PER; ++i) v[u][i] = ps[lane + kWave * i];
+    }
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      const float wt = __builtin_amdgcn_exp2f(w[u] - M);  // -inf state -> 0
+#pragma unroll
+      for (int i = 0; i < PER; ++i) acc[i] = __builtin_fmaf(wt, v[u][i], acc[i]);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < PER; ++i)
+    out[(size_t)gw * D + lane + kWave * i] = l > 0.f ? acc[i] / l : 0.f;
+}
+
+// End of a decode tile: s_acc[w][g][0..D) holds each wave's unnormalised
+// sum, s_acc[w][g][D] its softmax denominator, all relative to the tile max
+// s_mt[g].  A unit with one tile writes out directly; otherwise the tile's
+// (max, denominator, sum) goes to `partials` for k_merge.
+template <int D, int G, int NT, int NW>
+__device__ void finish_tile(float (*s_acc)[G][D + 1], const float* s_mt,
+                            float* __restrict__ partials, float* __restrict__ out, int b,
+                            int h, int Hq, int S_max, int split, int ns) {
+  const int tid = threadIdx.x;
+  if (ns == 1) {  // the only tile of the unit: finish here
+    for (int i = tid; i < G * D; i += NT) {
+      const int g = i / D, d = i - g * D;
+      float sum = 0.f, l = 0.f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        sum += s_acc[w][g][d];
+        l += s_acc[w][g][D];
+      }
+      out[((size_t)b * Hq + h * G + g) * D + d] = l > 0.f ? sum / l : 0.f;
+    }
+    return;
+  }
+  for (int i = tid; i < G * (D + 1); i += NT) {
+    const int g = i / (D + 1), d = i - g * (D + 1);
+    float sum = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) sum += s_acc[w][g][d];
+    float* dst = partials + (((size_t)b * Hq + h * G + g) * S_max + split) * (D + 2);
+    if (d < D) {
+      dst[d] = sum;
+    } else {
+      dst[D] = s_mt[g];
+      dst[D + 1] = sum;
+    }
+  }
+}
+
 template <int DT, int D, int G, int NT>
 __global__ __launch_bounds__(NT) void k_decode_split(
     const float* __restrict__ q, const void* __restrict__ k_pool,
@@ -433,33 +609,34 @@ __global__ __launch_bounds__(NT) void k_decode_split(
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ sel,
     const int32_t* __restrict__ sel_phys, const int32_t* __restrict__ sel_count,
     int Hq, int Hkv, int log2P, int MP, int NP, int k_max, int S_max,
-    float qscale, float* __restrict__ partials) {
+    float qscale, float* __restrict__ partials, float* __restrict__ out) {
   constexpr int EB = KV<DT>::bytes, C = KV<DT>::per16, L = D / C;
   constexpr int SPW = kWave / L, NW = NT / kWave, TPI = NW * SPW, J = 4;
   constexpr int TILE = J * TPI;
-  constexpr int MAXPG = TILE / 8 + 1;  // pages a tile can touch (P >= 8)
+  constexpr int MAXPG = TILE / 8;  // pages a tile can touch (P >= 8)
   __shared__ int s_lp[MAXPG];
   __shared__ uint32_t s_ph[MAXPG];
   __shared__ float s_red[NW][G];
   __shared__ float s_acc[NW][G][D + 1];
+  __shared__ float s_mt[G];
 
   const int P = 1 << log2P;
   const int unit = blockIdx.x / S_max, split = blockIdx.x - unit * S_max;
   const int b = unit / Hkv, h = unit - b * Hkv;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
-  const int cnt = clampi(sel_count[unit], 0, k_max);
   const long t0 = (long)split * TILE;
-  if (t0 >= ((long)cnt << log2P)) return;  // whole workgroup: no work
-  const int len = clampi(seq_lens[b], 0, MP * P);
-  const int e0 = (int)(t0 >> log2P);  // first sel entry of the tile
-  const int npg = min(cnt - e0, max(1, TILE >> log2P));
-  if (tid < npg) {
+  const int e0 = (int)(t0 >> log2P);                        // < k_max by the grid
+  const int ecap = min(max(1, TILE >> log2P), k_max - e0);  // sel entries in reach
+  // selection entries, count and query are independent loads: issue together
+  if (tid < ecap) {
     const int lp = sel[(size_t)unit * k_max + e0 + tid];
     const int ph = sel_phys ? sel_phys[(size_t)unit * k_max + e0 + tid]
                             : bt[(size_t)b * MP + clampi(lp, 0, MP - 1)];
     s_lp[tid] = lp;
     s_ph[tid] = (uint32_t)clampi(ph, 0, NP - 1);
   }
+  const int cnt = clampi(sel_count[unit], 0, k_max);
+  const int len = clampi(seq_lens[b], 0, MP * P);
   const int chunk = lane % L, slot = lane / L;
   float qs[G][C];
 #pragma unroll
@@ -474,7 +651,13 @@ __global__ __launch_bounds__(NT) void k_decode_split(
       qs[g][c + 3] = x4.w * qscale;
     }
   }
+  if (t0 >= ((long)cnt << log2P)) {  // whole workgroup: no work
+    if (cnt == 0 && split == 0)
+      for (int i = tid; i < G * D; i += NT) out[((size_t)b * Hq + h * G) * D + i] = 0.f;
+    return;
+  }
   __syncthreads();
+  const int npg = min(cnt - e0, ecap);
 
   const char* kb = reinterpret_cast<const char*>(k_pool);
   const char* vb = reinterpret_cast<const char*>(v_pool);
@@ -568,55 +751,238 @@ __global__ __launch_bounds__(NT) void k_decode_split(
       if (chunk == 0) s_acc[wave][g][D] = ls[g];
     }
   }
-  __syncthreads();
-  for (int i = tid; i < G * (D + 1); i += NT) {
-    const int g = i / (D + 1), d = i - g * (D + 1);
-    float s = 0.f;
+  if (tid == 0) {
 #pragma unroll
-    for (int w = 0; w < NW; ++w) s += s_acc[w][g][d];
-    float* dst = partials + (((size_t)b * Hq + h * G + g) * S_max + split) * (D + 2);
-    if (d < D) {
-      dst[d] = s;
-    } else {
-      dst[D] = mt[g];
-      dst[D + 1] = s;
-    }
+    for (int g = 0; g < G; ++g) s_mt[g] = mt[g];
   }
+  __syncthreads();
+  finish_tile<D, G, NT, NW>(s_acc, s_mt, partials, out, b, h, Hq, S_max, split,
+                            (int)((((long)cnt << log2P) + TILE - 1) / TILE));
 }
 
 // ---------------------------------------------------------------------------
-// K3: merge of the tiles' partial softmax states, one wave per (seq, q head)
+// K2 for grouped-query heads (G = 4, 8) on 16-bit KV: both contractions on
+// MFMA (v_mfma_f32_16x16x32_{bf16,f16})
 // ---------------------------------------------------------------------------
-template <int D>
-__global__ __launch_bounds__(256) void k_merge(
-    const float* __restrict__ partials, const int32_t* __restrict__ sel_count,
-    int B, int Hq, int Hkv, int G, int log2P, int k_max, int S_max, int tile,
-    float* __restrict__ out) {
-  constexpr int PER = D / kWave;
-  const int gw = blockIdx.x * 4 + threadIdx.x / kWave;
-  const int lane = threadIdx.x & (kWave - 1);
-  if (gw >= B * Hq) return;
-  const int b = gw / Hq, hq = gw - b * Hq, h = hq / G;
-  const int cnt = clampi(sel_count[(size_t)b * Hkv + h], 0, k_max);
-  const int ns = (int)((((long)cnt << log2P) + tile - 1) / tile);
-  const float* base = partials + (size_t)gw * S_max * (D + 2);
-  float M = -INFINITY;
-  for (int s = 0; s < ns; ++s) M = fmaxf(M, base[(size_t)s * (D + 2) + D]);
-  float acc[PER], l = 0.f;
+//
+// Per wave, 32 stream tokens as two 16-row tiles.
+//   logits^T[token][g] = K[token][:] . q[g][:]
+//     A = K rows straight from the pool (lane: token n16, 8 channels at
+//     32*ch + 8*c4), B = q^T; q is split into hi + lo 16-bit parts so the
+//     product keeps ~16 more mantissa bits than one 16-bit operand would.
+//     Lane (n16, c4) ends with the logits of head g = n16 for tokens
+//     4*c4 + r of each tile.
+//   out[g][d] += sum_token p[g][token] * V[token][d]
+//     A = p (hi + lo parts): the lane's own 8 probabilities are exactly the
+//     A fragment when the 32 contraction slots are ordered
+//     (tile0 rows 4c4..4c4+3, tile1 rows 4c4..4c4+3); B = V in the same slot
+//     order, read column-wise from the wave's V rows staged in LDS (rows
+//     padded by 16 bytes so the four lane groups hit disjoint banks).
+// Rows of the 16-row fragments beyond G carry zero queries and are never
+// stored.  Masked tokens are never loaded: their V rows are zero in LDS and
+// their logits -inf, so p = 0 multiplies a finite zero.
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef short s16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+template <int DT>
+struct Mma;
+template <>
+struct Mma<DT_BF16> {
+  typedef bf16x8_t vec;
+  typedef __bf16 elem;
+  static constexpr float kPScale = 1.f;
+  static __device__ __forceinline__ f32x4_t mma(vec a, vec b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+};
+template <>
+struct Mma<DT_F16> {
+  typedef f16x8_t vec;
+  typedef _Float16 elem;
+  // probabilities are scaled by 2^12 before the f16 split so that their low
+  // parts stay normal numbers; the sum is scaled back exactly afterwards
+  static constexpr float kPScale = 4096.f;
+  static __device__ __forceinline__ f32x4_t mma(vec a, vec b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+  }
+};
+
+template <int DT>
+__device__ __forceinline__ void split_hi_lo(float x, typename Mma<DT>::elem& hi,
+                                            typename Mma<DT>::elem& lo) {
+  using E = typename Mma<DT>::elem;
+  hi = (E)x;
+  lo = (E)(x - (float)hi);
+}
+
+template <int DT, int D, int G>
+__global__ __launch_bounds__(256) void k_decode_mfma(
+    const float* __restrict__ q, const void* __restrict__ k_pool,
+    const void* __restrict__ v_pool, const int32_t* __restrict__ bt,
+    const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ sel,
+    const int32_t* __restrict__ sel_phys, const int32_t* __restrict__ sel_count,
+    int Hq, int Hkv, int log2P, int MP, int NP, int k_max, int S_max,
+    float qscale, float* __restrict__ partials, float* __restrict__ out) {
+  using M = Mma<DT>;
+  using vec = typename M::vec;
+  constexpr int NT = 256, NW = NT / kWave, WT = 32, TILE = NW * WT;
+  constexpr int NCH = D / 32;   // 32-channel chunks of the logit contraction
+  constexpr int NDT = D / 16;   // 16-channel tiles of the output
+  constexpr int ROW = D + 8;    // LDS row stride in 16-bit elements
+  constexpr int LR = D / 8;     // lanes per V row (16 bytes each)
+  constexpr int RPI = kWave / LR, NVL = WT / RPI;
+  constexpr int MAXPG = TILE / 8;
+  static_assert(G <= 16, "one 16-row fragment holds the query group");
+  __shared__ int s_lp[MAXPG];
+  __shared__ uint32_t s_ph[MAXPG];
+  __shared__ __align__(16) uint16_t s_v[NW][WT][ROW];
+  __shared__ float s_red[NW][16];
+  __shared__ float s_acc[NW][G][D + 1];
+  __shared__ float s_mt[G];
+
+  const int P = 1 << log2P;
+  const int unit = blockIdx.x / S_max, split = blockIdx.x - unit * S_max;
+  const int b = unit / Hkv, h = unit - b * Hkv;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  const int n16 = lane & 15, c4 = lane >> 4;
+  const long t0 = (long)split * TILE;
+  const int e0 = (int)(t0 >> log2P);
+  const int ecap = min(max(1, TILE >> log2P), k_max - e0);
+  if (tid < ecap) {
+    const int lp = sel[(size_t)unit * k_max + e0 + tid];
+    const int ph = sel_phys ? sel_phys[(size_t)unit * k_max + e0 + tid]
+                            : bt[(size_t)b * MP + clampi(lp, 0, MP - 1)];
+    s_lp[tid] = lp;
+    s_ph[tid] = (uint32_t)clampi(ph, 0, NP - 1);
+  }
+  const int cnt = clampi(sel_count[unit], 0, k_max);
+  const int len = clampi(seq_lens[b], 0, MP * P);
+  // B operand of the logits: column g = n16, 8 channels per chunk
+  vec qhi[NCH], qlo[NCH];
+  {
+    const bool has = n16 < G;
+    const float* qg = q + ((size_t)b * Hq + h * G + (has ? n16 : 0)) * D + 8 * c4;
 #pragma unroll
-  for (int i = 0; i < PER; ++i) acc[i] = 0.f;
-  if (M != -INFINITY) {
-    for (int s = 0; s < ns; ++s) {
-      const float* ps = base + (size_t)s * (D + 2);
-      const float w = __builtin_amdgcn_exp2f(ps[D] - M);  // -inf state -> 0
-      l = __builtin_fmaf(w, ps[D + 1], l);
+    for (int ch = 0; ch < NCH; ++ch) {
+      const float4 a = *reinterpret_cast<const float4*>(qg + 32 * ch);
+      const float4 c = *reinterpret_cast<const float4*>(qg + 32 * ch + 4);
+      const float xs[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
 #pragma unroll
-      for (int i = 0; i < PER; ++i) acc[i] = __builtin_fmaf(w, ps[lane + kWave * i], acc[i]);
+      for (int j = 0; j < 8; ++j) {
+        typename M::elem hi, lo;
+        split_hi_lo<DT>(has ? xs[j] : 0.f, hi, lo);
+        qhi[ch][j] = hi;
+        qlo[ch][j] = lo;
+      }
     }
   }
+  if (t0 >= ((long)cnt << log2P)) {  // whole workgroup: no work
+    if (cnt == 0 && split == 0)
+      for (int i = tid; i < G * D; i += NT) out[((size_t)b * Hq + h * G) * D + i] = 0.f;
+    return;
+  }
+  __syncthreads();
+  const int npg = min(cnt - e0, ecap);
+  // pool element offset of wave-local token `tw`, or -1 when masked
+  auto token_off = [&](int tw) -> long {
+    const long ts = t0 + wave * WT + tw;
+    const int e = (int)(ts >> log2P) - e0;
+    const int st = (int)(ts & (P - 1));
+    if (e >= npg) return -1;
+    const int lp = s_lp[e];
+    if (lp < 0 || lp * P + st >= len) return -1;
+    return (long)((((size_t)s_ph[e] * Hkv + h) * P + st) * D);
+  };
+
+  const char* kb = reinterpret_cast<const char*>(k_pool);
+  const char* vb = reinterpret_cast<const char*>(v_pool);
+  uint4 kr[2][NCH];
 #pragma unroll
-  for (int i = 0; i < PER; ++i)
-    out[(size_t)gw * D + lane + kWave * i] = l > 0.f ? acc[i] / l : 0.f;
+  for (int i = 0; i < 2; ++i) {
+    const long off = token_off(16 * i + n16);
+#pragma unroll
+    for (int ch = 0; ch < NCH; ++ch)
+      kr[i][ch] = off >= 0 ? ld16(kb + (off + 32 * ch + 8 * c4) * 2) : make_uint4(0, 0, 0, 0);
+  }
+  uint4 vr[NVL];
+#pragma unroll
+  for (int u = 0; u < NVL; ++u) {
+    const long off = token_off(u * RPI + lane / LR);
+    vr[u] = off >= 0 ? ld16(vb + (off + (lane % LR) * 8) * 2) : make_uint4(0, 0, 0, 0);
+  }
+#pragma unroll
+  for (int u = 0; u < NVL; ++u)
+    *reinterpret_cast<uint4*>(&s_v[wave][u * RPI + lane / LR][(lane % LR) * 8]) = vr[u];
+
+  // logits of head n16 for tokens 4*c4 + r of tile i, log2 units
+  float z[2][4];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ch = 0; ch < NCH; ++ch) {
+      const vec a = __builtin_bit_cast(vec, kr[i][ch]);
+      acc = M::mma(a, qhi[ch], acc);
+      acc = M::mma(a, qlo[ch], acc);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) z[i][r] = token_off(16 * i + 4 * c4 + r) >= 0 ? acc[r] * qscale : -INFINITY;
+  }
+  float m = fmaxf(fmaxf(fmaxf(z[0][0], z[0][1]), fmaxf(z[0][2], z[0][3])),
+                  fmaxf(fmaxf(z[1][0], z[1][1]), fmaxf(z[1][2], z[1][3])));
+  m = fmaxf(m, __shfl_xor(m, 16));
+  m = fmaxf(m, __shfl_xor(m, 32));
+  if (lane < 16) s_red[wave][lane] = m;
+  __syncthreads();  // also publishes the V rows in LDS
+  float mt = s_red[0][n16];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) mt = fmaxf(mt, s_red[w][n16]);
+  const float ms = mt == -INFINITY ? 0.f : mt;
+  if (wave == 0 && lane < G) s_mt[lane] = mt;
+
+  // probabilities: the A fragment of the second contraction
+  vec phi, plo;
+  float lsum = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const float p = __builtin_amdgcn_exp2f(z[j >> 2][j & 3] - ms);
+    lsum += p;
+    typename M::elem hi, lo;
+    split_hi_lo<DT>(p * M::kPScale, hi, lo);
+    phi[j] = hi;
+    plo[j] = lo;
+  }
+  lsum += __shfl_xor(lsum, 16);
+  lsum += __shfl_xor(lsum, 32);
+  f32x4_t o[NDT];
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) {
+    s16x8_t vv;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int row = (j < 4) ? (4 * c4 + j) : (16 + 4 * c4 + (j - 4));
+      vv[j] = (short)s_v[wave][row][16 * dt + n16];
+    }
+    const vec bv = __builtin_bit_cast(vec, vv);
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+    acc = M::mma(phi, bv, acc);
+    acc = M::mma(plo, bv, acc);
+    o[dt] = acc;
+  }
+  // out fragment: head 4*c4 + r, channel 16*dt + n16
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int g = 4 * c4 + r;
+      if (g < G) s_acc[wave][g][16 * dt + n16] = o[dt][r] * (1.f / M::kPScale);
+    }
+  if (lane < G) s_acc[wave][lane][D] = lsum;
+  __syncthreads();
+  finish_tile<D, G, NT, NW>(s_acc, s_mt, partials, out, b, h, Hq, S_max, split,
+                            (int)((((long)cnt << log2P) + TILE - 1) / TILE));
 }
 
 // ---------------------------------------------------------------------------
@@ -656,7 +1022,6 @@ hipError_t by_dt_d_g(const Dims& d, Fn&& fn) {
   });
 }
 
-constexpr int kSelectThreads = 256;
 constexpr int kDecodeThreads = 256;
 
 int ilog2(int x) {
@@ -665,9 +1030,17 @@ int ilog2(int x) {
   return r;
 }
 
+size_t round_up(size_t x) { return (x + 255) / 256 * 256; }
+
 }  // namespace
 
+// Grouped-query heads on 16-bit KV take the MFMA decode (128-token tiles).
+bool use_mfma_decode(const Dims& d) {
+  return d.dt != DT_F32 && (d.G == 4 || d.G == 8);
+}
+
 int decode_tile_tokens(const Dims& d) {
+  if (use_mfma_decode(d)) return 128;
   const int bytes = d.dt == DT_F32 ? 4 : 2;
   const int C = 16 / bytes, L = d.D / C, SPW = kWave / L;
   return 4 * (kDecodeThreads / kWave) * SPW;
@@ -677,6 +1050,22 @@ int decode_splits(const Dims& d, int k_max) {
   const long stream = (long)k_max * d.P;
   const int tile = decode_tile_tokens(d);
   return (int)((stream + tile - 1) / tile);
+}
+
+size_t workspace_layout(const Dims& d, int k_max, void* base, Workspace* ws) {
+  const size_t units = (size_t)d.B * d.Hkv;
+  const size_t o_keys = 0;
+  const size_t o_phys = o_keys + round_up(units * d.MP * sizeof(uint32_t));
+  const size_t o_part = o_phys + round_up(units * k_max * sizeof(int32_t));
+  const size_t total = o_part + round_up((size_t)d.B * d.Hq * decode_splits(d, k_max) *
+                                         partial_stride(d) * sizeof(float));
+  if (base && ws) {
+    char* c = static_cast<char*>(base);
+    ws->keys = reinterpret_cast<uint32_t*>(c + o_keys);
+    ws->sel_phys = reinterpret_cast<int32_t*>(c + o_phys);
+    ws->partials = reinterpret_cast<float*>(c + o_part);
+  }
+  return total;
 }
 
 hipError_t launch_meta_build(const Dims& d, const void* k_pool, void* meta,
@@ -708,17 +1097,22 @@ hipError_t launch_meta_append(const Dims& d, const void* k_new,
 hipError_t launch_score_select(const Dims& d, const float* q, const void* meta,
                                const int32_t* bt, const int32_t* seq_lens,
                                int k_max, const int32_t* k_per_seq, int n_sink,
-                               int32_t* sel, int32_t* sel_count,
-                               int32_t* sel_phys, float* scores_out,
-                               hipStream_t s) {
+                               int32_t* sel, int32_t* sel_count, float* scores_out,
+                               const Workspace& ws, hipStream_t s) {
   return by_dt_d_g(d, [&](auto DT, auto HD, auto GG) -> hipError_t {
     constexpr int dt = decltype(DT)::value, hd = decltype(HD)::value,
                   g = decltype(GG)::value;
-    const size_t shmem = 2 * sizeof(uint32_t) * (size_t)d.MP;
-    hipLaunchKernelGGL((k_score_select<dt, hd, g, kSelectThreads>), dim3(d.B * d.Hkv),
-                       dim3(kSelectThreads), shmem, s, q, meta, bt, seq_lens, d.Hq,
-                       d.Hkv, d.P, d.MP, d.NP, k_max, k_per_seq, n_sink, sel,
-                       sel_count, sel_phys, scores_out);
+    using Cfg = ScoreCfg<dt, hd, g>;
+    const int NC = (d.MP + Cfg::CH - 1) / Cfg::CH;
+    hipLaunchKernelGGL((k_score_select<dt, hd, g>), dim3(d.B * d.Hkv * NC), dim3(Cfg::NT), 0,
+                       s, q, meta, bt, seq_lens, d.Hq, d.Hkv, d.P, d.MP, d.NP, NC, k_max,
+                       k_per_seq, n_sink, sel, sel_count, scores_out, ws.keys, ws.sel_phys);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || NC == 1) return e;
+    // units longer than one chunk are selected once all their keys exist
+    hipLaunchKernelGGL((k_select<Cfg::CH>), dim3(d.B * d.Hkv), dim3(256),
+                       sizeof(uint32_t) * (size_t)d.MP, s, bt, seq_lens, d.Hkv, d.P, d.MP,
+                       d.NP, k_max, k_per_seq, n_sink, ws.keys, sel, sel_count, ws.sel_phys);
     return hipGetLastError();
   });
 }
@@ -727,28 +1121,38 @@ hipError_t launch_decode(const Dims& d, const float* q, const void* k_pool,
                          const void* v_pool, const int32_t* bt,
                          const int32_t* seq_lens, const int32_t* sel,
                          const int32_t* sel_phys, const int32_t* sel_count,
-                         int k_max, float scale, float* partials, float* out,
+                         int k_max, float scale, const Workspace& ws, float* out,
                          hipStream_t s) {
   const int S_max = decode_splits(d, k_max);
-  const int tile = decode_tile_tokens(d);
   const int log2P = ilog2(d.P);
   const float qscale = scale * 1.44269504088896340736f;  // fold log2(e)
+  const bool mfma = use_mfma_decode(d);
   hipError_t e = by_dt_d_g(d, [&](auto DT, auto HD, auto GG) -> hipError_t {
     constexpr int dt = decltype(DT)::value, hd = decltype(HD)::value,
                   g = decltype(GG)::value;
+    if constexpr (dt != DT_F32 && (g == 4 || g == 8)) {
+      if (mfma) {
+        hipLaunchKernelGGL((k_decode_mfma<dt, hd, g>), dim3(d.B * d.Hkv * S_max), dim3(256),
+                           0, s, q, k_pool, v_pool, bt, seq_lens, sel, sel_phys, sel_count,
+                           d.Hq, d.Hkv, log2P, d.MP, d.NP, k_max, S_max, qscale,
+                           ws.partials, out);
+        return hipGetLastError();
+      }
+    }
     hipLaunchKernelGGL((k_decode_split<dt, hd, g, kDecodeThreads>),
                        dim3(d.B * d.Hkv * S_max), dim3(kDecodeThreads), 0, s, q,
                        k_pool, v_pool, bt, seq_lens, sel, sel_phys, sel_count, d.Hq,
-                       d.Hkv, log2P, d.MP, d.NP, k_max, S_max, qscale, partials);
+                       d.Hkv, log2P, d.MP, d.NP, k_max, S_max, qscale, ws.partials, out);
     return hipGetLastError();
   });
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || S_max == 1) return e;
   const int waves = d.B * d.Hq;
+  const int tile = decode_tile_tokens(d);
   if (d.D == 64)
-    hipLaunchKernelGGL(k_merge<64>, dim3((waves + 3) / 4), dim3(256), 0, s, partials,
+    hipLaunchKernelGGL(k_merge<64>, dim3((waves + 3) / 4), dim3(256), 0, s, ws.partials,
                        sel_count, d.B, d.Hq, d.Hkv, d.G, log2P, k_max, S_max, tile, out);
   else
-    hipLaunchKernelGGL(k_merge<128>, dim3((waves + 3) / 4), dim3(256), 0, s, partials,
+    hipLaunchKernelGGL(k_merge<128>, dim3((waves + 3) / 4), dim3(256), 0, s, ws.partials,
                        sel_count, d.B, d.Hq, d.Hkv, d.G, log2P, k_max, S_max, tile, out);
   return hipGetLastError();
 }

@@ -23,6 +23,15 @@ int decode_splits(const Dims& d, int k_max);
 // Partial-state floats per (sequence, query head, split).
 inline int partial_stride(const Dims& d) { return d.D + 2; }
 
+// Regions of the caller's workspace (no initialisation needed).
+struct Workspace {
+  uint32_t* keys;      // [B*Hkv][MP] order keys of the page scores
+  int32_t* sel_phys;   // [B*Hkv][k_max] physical page of each selection
+  float* partials;     // [B*Hq][splits][D+2] tile softmax states
+};
+// Total workspace bytes; with `base` non-null also fills `ws`.
+size_t workspace_layout(const Dims& d, int k_max, void* base, Workspace* ws);
+
 hipError_t launch_meta_build(const Dims& d, const void* k_pool, void* meta,
                              const int32_t* bt, const int32_t* seq_lens,
                              hipStream_t s);
@@ -32,21 +41,21 @@ hipError_t launch_meta_append(const Dims& d, const void* k_new,
                               void* meta, const int32_t* bt,
                               const int32_t* seq_lens, hipStream_t s);
 
-// sel_phys (nullable): physical page of every selected entry, consumed by
-// the decode so it skips the block-table lookup.
+// Scores every page, keeps the top pages; also fills ws.sel_phys.
 hipError_t launch_score_select(const Dims& d, const float* q, const void* meta,
                                const int32_t* bt, const int32_t* seq_lens,
-                               int k_max, const int32_t* k_per_seq,
-                               int n_sink, int32_t* sel, int32_t* sel_count,
-                               int32_t* sel_phys, float* scores_out,
-                               hipStream_t s);
+                               int k_max, const int32_t* k_per_seq, int n_sink,
+                               int32_t* sel, int32_t* sel_count, float* scores_out,
+                               const Workspace& ws, hipStream_t s);
 
-// Split decode (partials into `partials`) followed by the merge into `out`.
+// Split decode; units with several tiles are merged by a second kernel.
+// sel_phys (nullable): physical page of every selected entry, so the decode
+// skips the block-table lookup.
 hipError_t launch_decode(const Dims& d, const float* q, const void* k_pool,
                          const void* v_pool, const int32_t* bt,
                          const int32_t* seq_lens, const int32_t* sel,
                          const int32_t* sel_phys, const int32_t* sel_count,
-                         int k_max, float scale, float* partials, float* out,
+                         int k_max, float scale, const Workspace& ws, float* out,
                          hipStream_t s);
 
 }  // namespace tsv

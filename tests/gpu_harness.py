@@ -58,7 +58,7 @@ def gpu_run(wl, k_max=None, k_per_seq="wl", n_sink=None, step=0, separate=False)
     cnt = torch.full((B, Hkv), -7, dtype=torch.int32, device="cuda")
     sc = torch.full((B, Hkv, MP), float("nan"), dtype=torch.float32, device="cuda")
     out = torch.full((B, Hq, D), float("nan"), dtype=torch.float32, device="cuda")
-    ws = torch.empty(T.tsv_workspace_bytes(sh, k_max), dtype=torch.uint8, device="cuda")
+    ws = T.new_workspace(sh, k_max)
     k_new = v_new = None
     if wl.steps:
         st = wl.steps[step]
@@ -79,7 +79,7 @@ def gpu_run(wl, k_max=None, k_per_seq="wl", n_sink=None, step=0, separate=False)
             T.tsv_meta_append(sh, k_new, v_new, d.k_pool, d.v_pool, d.meta, d.block_table,
                               seq_lens)
         T.tsv_select_pages(sh, q, d.meta, d.block_table, seq_lens, k_max, kps, n_sink, sel,
-                           cnt, sc)
+                           cnt, sc, ws)
         T.tsv_sparse_decode(sh, q, d.k_pool, d.v_pool, d.block_table, seq_lens, sel, cnt,
                             k_max, wl.scale, out, ws)
     else:

@@ -90,27 +90,32 @@ def test_bad_shapes_rejected_before_any_hip_call(tsv, kw, status):
     s = shape(**kw)
     fake = ctypes.c_void_p(1 << 20)  # never dereferenced: rejected first
     rc = tsv._lib.tsv_select_pages(ctypes.byref(s), fake, fake, fake, fake, 4, None, 0,
-                                   fake, fake, None, None)
+                                   fake, fake, None, fake, 1 << 30, None)
     assert rc == status
 
 
 def test_bad_arguments_rejected_before_any_hip_call(tsv):
     s = shape()
     f = ctypes.c_void_p(1 << 20)
+    big = 1 << 30
     L = tsv._lib
     # null required pointers
-    assert L.tsv_select_pages(ctypes.byref(s), None, f, f, f, 4, None, 0, f, f, None, None) == -1
+    assert L.tsv_select_pages(ctypes.byref(s), None, f, f, f, 4, None, 0, f, f, None, f, big, None) == -1
     assert L.tsv_meta_build(ctypes.byref(s), f, None, f, f, None) == -1
     assert L.tsv_meta_append(ctypes.byref(s), f, None, f, f, f, f, f, None) == -1
     # k_max / n_sink
-    assert L.tsv_select_pages(ctypes.byref(s), f, f, f, f, 0, None, 0, f, f, None, None) == -1
-    assert L.tsv_select_pages(ctypes.byref(s), f, f, f, f, 4, None, 5, f, f, None, None) == -1
-    assert L.tsv_select_pages(ctypes.byref(s), f, f, f, f, 4, None, -1, f, f, None, None) == -1
+    assert L.tsv_select_pages(ctypes.byref(s), f, f, f, f, 0, None, 0, f, f, None, f, big, None) == -1
+    assert L.tsv_select_pages(ctypes.byref(s), f, f, f, f, 4, None, 5, f, f, None, f, big, None) == -1
+    assert L.tsv_select_pages(ctypes.byref(s), f, f, f, f, 4, None, -1, f, f, None, f, big, None) == -1
     # misaligned q
     mis = ctypes.c_void_p((1 << 20) + 4)
-    assert L.tsv_select_pages(ctypes.byref(s), mis, f, f, f, 4, None, 0, f, f, None, None) == -1
-    # workspace too small
+    assert L.tsv_select_pages(ctypes.byref(s), mis, f, f, f, 4, None, 0, f, f, None, f, big, None) == -1
+    # workspace too small or misaligned
     need = L.tsv_workspace_bytes(ctypes.byref(s), 4)
+    assert L.tsv_select_pages(ctypes.byref(s), f, f, f, f, 4, None, 0, f, f, None, f, need - 1,
+                              None) == -1
+    assert L.tsv_select_pages(ctypes.byref(s), f, f, f, f, 4, None, 0, f, f, None,
+                              ctypes.c_void_p((1 << 20) + 64), need, None) == -1
     assert L.tsv_sparse_decode(ctypes.byref(s), f, f, f, f, f, f, f, 4, ctypes.c_float(0.1), f,
                                f, need // 2, None) == -1
     assert L.tsv_decode_step(ctypes.byref(s), f, f, f, f, f, f, f, f, 4, None, 0,

@@ -145,7 +145,7 @@ def test_ragged_appends_seventeen_steps():
     cnt = torch.empty((B, Hkv), dtype=torch.int32, device="cuda")
     sc = torch.empty((B, Hkv, sh.max_pages_per_seq), dtype=torch.float32, device="cuda")
     out = torch.empty((B, Hq, D), dtype=torch.float32, device="cuda")
-    ws = torch.empty(T.tsv_workspace_bytes(sh, wl.k_max), dtype=torch.uint8, device="cuda")
+    ws = T.new_workspace(sh, wl.k_max)
     for i, st in enumerate(wl.steps):
         so, co, sco, oo = O.decode_step(sh, st.q, kp, vp, meta_o, wl.block_table, st.seq_lens,
                                         wl.k_max, wl.scale, st.k_per_seq, 0, st.k_new, st.v_new)
