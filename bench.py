@@ -2,21 +2,28 @@
 
 A step is one tsv_decode_step over one batch: [append one token per sequence]
 -> score every page's box against the query -> keep the top-K pages -> masked
-softmax attention over the kept pages only.  Inputs are seeded synthetic
-tensors with the decode shapes of the pages' models (TinyServe, "Query-Aware
-Cache Selection for Efficient LLM Serving"), resident in HBM before the timed
-region.  R copies of the pool/metadata are rotated so that every step reads
-HBM rather than the 256 MB Infinity Cache.
+softmax attention over the kept pages only (TinyServe, "Query-Aware Cache
+Selection for Efficient LLM Serving": abstract, method details).  Inputs are
+seeded synthetic tensors with the decode shapes of the pages' models,
+resident in HBM before the timed region.  R copies of the pool and metadata
+are rotated so that every step reads HBM rather than the 256 MB Infinity
+Cache.  Steps are replayed from a HIP graph (--eager: launched one by one).
 
 Prints one JSON line:
   value        (sequence x query head) / s of the whole step
-  roofline     the split-decode kernel's algorithmic bytes / its mean duration
-               (HIP events around each launch), against 8 TB/s
+  roofline     the step kernel's algorithmic bytes / its mean duration (HIP
+               events around the graph-replayed steps on their stream) against
+               8 TB/s; `traffic` = HBM bytes per launch from rocprofv3 counters
+               when they were taken on the current kernel source, else null
   cpu_baseline the CPU oracle (single thread) on a bounded sample of the step
+
+--copy-calibrate MB only runs a plain device copy of MB megabytes (the
+reference kernel for scaling the HBM byte counters) and exits.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import math
 import os
@@ -44,6 +51,22 @@ DESCR = {
     "ragged": "ragged serving mix: B=64, 32/8 heads, D=128, lengths U[512,16384], page 16, "
               "budget min(64, 20%), fp16 KV, shared shuffled pool, 1 append per step",
 }
+KERNEL_SOURCES = [os.path.join(ROOT, "query_aware_sparse_bbox_amd", "csrc", f)
+                  for f in ("tsv_kernels.hip", "tsv_api.hip", "tsv_launch.h")]
+
+# HBM bytes per k_step launch from `rocprofv3 --pmc FETCH_SIZE` and `--pmc
+# WRITE_SIZE` runs of this script, each divided by the same counter's reading
+# per byte of a plain device copy (--copy-calibrate).  Valid only for the
+# kernel source they were taken on (sha256 of KERNEL_SOURCES, first 16 hex).
+TRAFFIC = {}
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 # ---------------------------------------------------------------------------
@@ -69,8 +92,7 @@ def step_bytes(wl, lens, sel, cnt):
     table = int(n.sum()) * 4
     append = sh.batch * sh.num_kv_heads * (2 * D * e + 2 * 2 * D * e) if wl.steps else 0
     return dict(meta=meta, kv=kv, q_out=qo, table=table, append=append,
-                total=meta + kv + qo + table + append,
-                decode_kernel=kv + sh.batch * sh.num_q_heads * D * 4)
+                total=meta + kv + qo + table + append)
 
 
 def parse():
@@ -82,8 +104,27 @@ def parse():
     ap.add_argument("--rotate", type=int, default=0, help="pool copies (0: auto, >=512 MB)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="CPU-oracle baseline budget (0 disables it)")
-    ap.add_argument("--graph", action="store_true", help="replay the steps from a HIP graph")
+    ap.add_argument("--eager", action="store_true", help="launch steps one by one (no graph)")
+    ap.add_argument("--copy-calibrate", type=float, default=0.0, metavar="MB",
+                    help="only run a plain device copy of MB megabytes, 5 times, and exit")
     return ap.parse_args()
+
+
+def copy_calibrate(mb):
+    import torch
+    n = int(mb * 1e6) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(5):
+        dst.copy_(src)
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / 5
+    print(json.dumps({"copy_bytes_each_way": n * 4, "ms": ms,
+                      "gbs_read_plus_write": 2 * n * 4 / (ms * 1e-3) / 1e9}), flush=True)
 
 
 def main():
@@ -97,10 +138,14 @@ def main():
 
     import torch
 
+    torch.cuda.set_device(0)
+    if args.copy_calibrate > 0:
+        copy_calibrate(args.copy_calibrate)
+        return
+
     import query_aware_sparse_bbox_amd as T
     from workloads import device as WD
 
-    torch.cuda.set_device(0)
     dev = "cuda"
     t_gen = time.time()
     wl = W.make(args.config)
@@ -111,7 +156,6 @@ def main():
     kps_np = st.k_per_seq if st else wl.k_per_seq
     print(f"[bench] {args.config}: {sh} generated in {time.time() - t_gen:.1f}s", flush=True)
 
-    # shared small inputs
     bt = WD.i32(wl.block_table)
     lens = WD.i32(lens_np)
     lens_pre = WD.i32(lens_np - 1) if st else lens
@@ -120,7 +164,8 @@ def main():
     k_new = WD.kv_tensor(st.k_new, sh.kv_dtype) if st else None
     v_new = WD.kv_tensor(st.v_new, sh.kv_dtype) if st else None
     k_max, n_sink, scale = wl.k_max, wl.n_sink, wl.scale
-    B, Hq, Hkv, D, MP = sh.batch, sh.num_q_heads, sh.num_kv_heads, sh.head_dim, sh.max_pages_per_seq
+    B, Hq, Hkv, D = sh.batch, sh.num_q_heads, sh.num_kv_heads, sh.head_dim
+    launches = T.tsv_decode_step_launches(sh, k_max, st is not None)
 
     def instance():
         d = WD.upload(wl, dev)
@@ -138,40 +183,60 @@ def main():
     first = instance()
     step(first)
     torch.cuda.synchronize()
+    ref_sel, ref_out = first.sel.clone(), first.out.clone()
     nb = step_bytes(wl, lens_np, first.sel.cpu().numpy(), first.cnt.cpu().numpy())
     R = args.rotate or max(2, math.ceil(512e6 / nb["total"]))
     insts = [first] + [instance() for _ in range(R - 1)]
     torch.cuda.synchronize()
-    print(f"[bench] {R} rotating instances, {nb['total'] / 1e6:.2f} MB algorithmic per step",
-          flush=True)
+    print(f"[bench] {R} rotating instances, {nb['total'] / 1e6:.2f} MB algorithmic per step, "
+          f"{launches} launch(es) per step", flush=True)
 
     stream = torch.cuda.current_stream()
     K, Wm = args.steps, args.warmup
-    graph = None
-    if args.graph:
-        # one graph holding R consecutive steps (one per instance)
+
+    def capture(ds):
         s = torch.cuda.Stream()
         s.wait_stream(stream)
         with torch.cuda.stream(s):
-            for d in insts:
+            for d in ds:
                 step(d)
         stream.wait_stream(s)
         torch.cuda.synchronize()
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            for d in insts:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for d in ds:
                 step(d)
         torch.cuda.synchronize()
+        return g
+
+    graphs = {}
 
     def run(nsteps):
-        if graph is not None:
-            for _ in range(nsteps // R):
-                graph.replay()
-            for i in range(nsteps % R):
-                step(insts[i])
-        else:
+        """Exactly nsteps steps, instance i % R for step i."""
+        if args.eager:
             for i in range(nsteps):
                 step(insts[i % R])
+            return
+        for _ in range(nsteps // R):
+            graphs["full"].replay()
+        rem = nsteps % R
+        if rem:
+            if rem not in graphs:
+                graphs[rem] = capture(insts[:rem])
+            graphs[rem].replay()
+
+    if not args.eager:
+        graphs["full"] = capture(insts)
+        for r in {K % R, Wm % R} - {0}:
+            graphs[r] = capture(insts[:r])
+        # a replayed step reproduces the eager one bit for bit
+        first.sel.fill_(-5)
+        first.out.fill_(float("nan"))
+        graphs["full"].replay()
+        torch.cuda.synchronize()
+        assert torch.equal(first.sel, ref_sel), "graph replay changed the selection"
+        assert torch.equal(first.out.view(torch.int32), ref_out.view(torch.int32)), \
+            "graph replay changed the output"
 
     run(Wm)
     torch.cuda.synchronize()
@@ -184,23 +249,6 @@ def main():
     wall = time.perf_counter() - wall0
     ms_step = t0.elapsed_time(t1) / K
     print(f"[bench] step {ms_step * 1e3:.2f} us (wall {wall / K * 1e6:.2f} us/step)", flush=True)
-
-    # dominant kernel: the split decode (+ its merge), timed per launch with events
-    sel_cnt = [(d.sel, d.cnt) for d in insts]
-    torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(K)]
-    for i in range(K):
-        d = insts[i % R]
-        ev[i][0].record(stream)
-        T.tsv_sparse_decode(sh, q, d.k_pool, d.v_pool, bt, lens, d.sel, d.cnt, k_max, scale,
-                            d.out, d.ws)
-        ev[i][1].record(stream)
-    torch.cuda.synchronize()
-    dec_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
-    dec_gbs = nb["decode_kernel"] / (dec_ms * 1e-3) / 1e9
-    print(f"[bench] decode phase {dec_ms * 1e3:.2f} us/launch, {dec_gbs:.0f} GB/s", flush=True)
-    del sel_cnt
 
     # CPU oracle baseline (single thread) on a bounded sample of the same step
     cpu = None
@@ -218,11 +266,16 @@ def main():
         cpu = {"value": B * Hq * reps / t_cpu, "unit": "(seq·head)/s", "cores": 1,
                "kind": "oracle",
                "sample": f"{reps} full decode step(s) of the same workload "
-                         f"({t_cpu:.1f} s, single-threaded C oracle, metadata prebuilt)"}
+                         f"({t_cpu:.1f} s, single-threaded C oracle, boxes prebuilt)"}
         print(f"[bench] cpu oracle {t_cpu / reps * 1e3:.1f} ms/step", flush=True)
 
     value = B * Hq / (ms_step * 1e-3)
     step_gbs = nb["total"] / (ms_step * 1e-3) / 1e9
+    src = source_hash()
+    tr = TRAFFIC.get(args.config)
+    traffic = tr["bytes_per_launch"] if tr and tr["source"] == src and launches == 1 else None
+    kernel = "k_step (whole step: append, score, select, decode)" if launches == 1 else \
+        f"tsv_decode_step ({launches} kernels)"
     line = {
         "metric": METRIC,
         "value": value,
@@ -239,15 +292,16 @@ def main():
         "config": {"workload": f"{args.config}: {DESCR[args.config]}", "kv_dtype":
                    W.DTYPE_NAMES[sh.kv_dtype], "batch": B, "q_heads": Hq, "kv_heads": Hkv,
                    "head_dim": D, "page_size": sh.page_size, "k_max": k_max,
-                   "rotating_instances": R, "graph": bool(args.graph)},
+                   "rotating_instances": R, "graph": not args.eager},
         "step_algorithmic_bytes": nb["total"],
-        "step_hbm_gbs": step_gbs,
-        "step_frac_of_peak": step_gbs / PEAK_HBM_GBS,
-        "roofline": {"bound": "hbm", "kernel": "k_decode_split",
-                     "achieved": dec_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": dec_gbs / PEAK_HBM_GBS, "traffic": None,
-                     "algorithmic_bytes_per_launch": nb["decode_kernel"],
-                     "mean_launch_us": dec_ms * 1e3},
+        "step_bytes_breakdown": {k: v for k, v in nb.items() if k != "total"},
+        "roofline": {"bound": "hbm", "kernel": kernel,
+                     "achieved": step_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": step_gbs / PEAK_HBM_GBS, "traffic": traffic,
+                     "algorithmic_bytes_per_launch": nb["total"],
+                     "mean_launch_us": ms_step * 1e3 / max(launches, 1) if launches == 1
+                     else None,
+                     "kernel_source": src},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

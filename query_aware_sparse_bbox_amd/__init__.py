@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(_HERE, "libtsv.so")
 if not os.path.exists(LIB_PATH):
     raise ImportError(
         f"{LIB_PATH} is not built; build it with "
-        "`python -m query_aware_sparse_bbox_amd.build` (hipcc, gfx950)")
+        "`python query_aware_sparse_bbox_amd/build.py` (hipcc, gfx950)")
 
 _lib = ctypes.CDLL(LIB_PATH)
 
@@ -25,8 +25,8 @@ TSV_F32, TSV_F16, TSV_BF16 = 0, 1, 2
 TSV_OK, TSV_ERR_INVALID_ARG, TSV_ERR_UNSUPPORTED, TSV_ERR_HIP = 0, -1, -2, -3
 
 EXPORTS = ("tsv_version", "tsv_status_string", "tsv_meta_bytes", "tsv_workspace_bytes",
-           "tsv_meta_build", "tsv_meta_append", "tsv_select_pages", "tsv_sparse_decode",
-           "tsv_decode_step")
+           "tsv_decode_step_launches", "tsv_meta_build", "tsv_meta_append",
+           "tsv_select_pages", "tsv_sparse_decode", "tsv_decode_step")
 
 
 class TsvError(RuntimeError):
@@ -54,6 +54,7 @@ _SIGS = {
     "tsv_status_string": ([ctypes.c_int], ctypes.c_char_p),
     "tsv_meta_bytes": ([_SP], _Z),
     "tsv_workspace_bytes": ([_SP, _I], _Z),
+    "tsv_decode_step_launches": ([_SP, _I, _I], ctypes.c_int),
     "tsv_meta_build": ([_SP, _P, _P, _P, _P, _P], ctypes.c_int),
     "tsv_meta_append": ([_SP, _P, _P, _P, _P, _P, _P, _P, _P], ctypes.c_int),
     "tsv_select_pages": ([_SP, _P, _P, _P, _P, _I, _P, _I, _P, _P, _P, _P, _Z, _P],
@@ -109,6 +110,11 @@ def tsv_meta_bytes(shape) -> int:
 
 def tsv_workspace_bytes(shape, k_max: int) -> int:
     return _lib.tsv_workspace_bytes(ctypes.byref(Shape.of(shape)), int(k_max))
+
+
+def tsv_decode_step_launches(shape, k_max: int, with_append: bool) -> int:
+    return _lib.tsv_decode_step_launches(ctypes.byref(Shape.of(shape)), int(k_max),
+                                         int(bool(with_append)))
 
 
 def tsv_meta_build(shape, k_pool, meta, block_table, seq_lens, stream=None):

@@ -289,155 +289,218 @@ struct ScoreCfg {
   static constexpr int PB = NW * PPW * U;  // pages per batch
 };
 
-// Lanes below this one that have their bit set in `mask`.
-__device__ __forceinline__ int lanes_below(unsigned long long mask) {
-  return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
-                                   __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0));
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xF, 0xF, false);
 }
 
-// Top-K of one unit, run by a single wave: the first f pages always, then
-// the R = keff - f largest keys among pages [f, n) (equal keys: lower page
-// first), found by an 8-bit-digit radix search over an LDS histogram.  Keys
-// are visited as rows of 64 pages (lane l takes page j*64 + l); KC rows at a
-// time are read into registers with all reads in flight before the first
-// histogram update, so a pass costs one LDS round trip per KC rows.  Output
-// slots come from per-row ballots (pages ascend row by row, lane by lane),
-// so no scan sits in the loops.  Writes the chosen pages in ascending order,
-// -1 padding to k_max, their physical pages and the count.
-constexpr int kSelectRows = 8;
+// Reduction of x over the 64 lanes with an associative, commutative,
+// idempotent op: DPP inside each 16-lane row, then the four row results
+// read as scalars.  Wave-uniform result.
+template <class Op>
+__device__ __forceinline__ uint32_t wave_reduce(uint32_t x, Op op) {
+  x = op(x, dpp_u<kQuadXor1>(x));
+  x = op(x, dpp_u<kQuadXor2>(x));
+  x = op(x, dpp_u<kRowHalfMirror>(x));
+  x = op(x, dpp_u<kRowMirror>(x));
+  const uint32_t r0 = __builtin_amdgcn_readlane(x, 0), r1 = __builtin_amdgcn_readlane(x, 16);
+  const uint32_t r2 = __builtin_amdgcn_readlane(x, 32), r3 = __builtin_amdgcn_readlane(x, 48);
+  return op(op(r0, r1), op(r2, r3));
+}
 
-__device__ __forceinline__ void select_wave(const uint32_t* s_key, const uint32_t* s_phys, int n, int keff,
-                            int f, int k_max, int32_t* __restrict__ srow,
-                            int32_t* __restrict__ prow, int32_t* __restrict__ count,
-                            int* s_hist) {
-  constexpr int KC = kSelectRows;
-  const int lane = threadIdx.x & (kWave - 1);
-  const int rows = (n + kWave - 1) / kWave;
+// LDS scratch of select_block (s_red[0] / s_red[1] must hold all-ones / zero,
+// written before a barrier that precedes the call).
+template <int NT>
+struct SelectLds {
+  int hist[256];
+  int red[8];
+  int scan[NT / 64];
+};
+
+// Top-K of one row by a whole workgroup.  Pages [0, f) are always kept; the
+// other R = keff - f slots take the largest order keys among pages [f, n),
+// equal keys lowest page first.
+//
+// Thread t owns the m = ceil(n/NT) consecutive pages [t*m, t*m + m) and keeps
+// their keys in registers.  The threshold is found most-significant digit
+// first: the bits every candidate shares are fixed at once (block AND / OR),
+// then 8-bit digits are resolved with an LDS histogram (a wave's most common
+// digit is added once) until the boundary bucket is taken whole or no bits
+// are left.  One block-wide scan of packed (kept-above, equal-to-threshold)
+// counts then gives every thread its output slots, so the pages come out in
+// ascending order without sorting.
+//
+// Leaves the kept pages, ascending, in LDS: s_key[0..cnt) logical pages,
+// s_phys[0..cnt) physical pages, and returns cnt.  With srow non-null also
+// writes the logical pages to srow (-1 padded to k_max), the physical pages
+// to prow (if non-null) and the count to *count.  Ends with a barrier.
+template <int NT>
+__device__ __forceinline__ int select_block(uint32_t* s_key, uint32_t* s_phys, int n,
+                                            int keff, int f, int k_max,
+                                            int32_t* __restrict__ srow,
+                                            int32_t* __restrict__ prow,
+                                            int32_t* __restrict__ count, SelectLds<NT>& sl) {
+  constexpr int NW = NT / kWave, MAXM = kMaxPagesPerSeq / NT;
+  static_assert(NT >= 256, "one histogram bin per thread is cleared");
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  const int m = (n + NT - 1) / NT;
+  const int p0 = tid * m, nl = max(n - 1, 0);
   const int R = keff - f, ncand = n - f;
   const bool take_all = R >= ncand, radix = R > 0 && R < ncand;
-  const int nl = max(n - 1, 0);
-  uint32_t tau = 0;
+  uint32_t kk[MAXM], ph[MAXM];
+#pragma unroll
+  for (int i = 0; i < MAXM; ++i) {
+    if (i >= m) break;
+    const int pc = min(p0 + i, nl);
+    kk[i] = s_key[pc];
+    ph[i] = s_phys[pc];
+  }
+  auto is_cand = [&](int i) {
+    const int p = p0 + i;
+    return i < m && p < n && p >= f;
+  };
+  uint32_t tmask = 0, tau = 0;  // (key & tmask) > tau: kept; == tau: the first `need`
   int need = 0;
   if (radix) {
-    uint32_t prefix = 0, pmask = 0;
+    uint32_t a = ~0u, o = 0u;
+#pragma unroll
+    for (int i = 0; i < MAXM; ++i) {
+      if (i >= m) break;  // m is uniform
+      if (is_cand(i)) {
+        a &= kk[i];
+        o |= kk[i];
+      }
+    }
+    a = wave_reduce(a, [](uint32_t u, uint32_t v) { return u & v; });
+    o = wave_reduce(o, [](uint32_t u, uint32_t v) { return u | v; });
+    if (lane == 0) {
+      atomicAnd(reinterpret_cast<unsigned*>(&sl.red[0]), a);
+      atomicOr(reinterpret_cast<unsigned*>(&sl.red[1]), o);
+    }
+    __syncthreads();
+    a = (uint32_t)sl.red[0];
+    o = (uint32_t)sl.red[1];
     int remaining = R;
-    for (int shift = 24; shift >= 0; shift -= 8) {
+    if (a == o) {  // every candidate has the same key: lowest pages win
+      tmask = ~0u;
+      tau = a;
+    } else {
+      int top = 31 - __clz(a ^ o);
+      tmask = top == 31 ? 0u : ~((2u << top) - 1u);
+      tau = a & tmask;
+      for (;;) {
+        const int width = min(8, top + 1), shift = top + 1 - width;
+        const uint32_t dmask = (1u << width) - 1u;
+        const int nb = 1 << width;
+        if (tid < 256) sl.hist[tid] = 0;
+        __syncthreads();
 #pragma unroll
-      for (int j = 0; j < 4; ++j) s_hist[lane + kWave * j] = 0;
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-      __builtin_amdgcn_wave_barrier();
-      for (int c0 = 0; c0 < rows; c0 += KC) {
-        uint32_t kk[KC];
-#pragma unroll
-        for (int r = 0; r < KC; ++r) kk[r] = s_key[min((c0 + r) * kWave + lane, nl)];
-#pragma unroll
-        for (int r = 0; r < KC; ++r) {
-          const int p = (c0 + r) * kWave + lane;
-          if (p < n && p >= f && (kk[r] & pmask) == prefix)
-            atomicAdd(&s_hist[(kk[r] >> shift) & 255], 1);
+        for (int i = 0; i < MAXM; ++i) {
+          if (i >= m) break;
+          const bool in = is_cand(i) && (kk[i] & tmask) == tau;
+          const int d = in ? (int)((kk[i] >> shift) & dmask) : -1;
+          const unsigned long long act = __ballot(in);
+          if (act) {
+            const int src = __ffsll(act) - 1;
+            const int dl = __builtin_amdgcn_readlane(d, src);
+            const unsigned long long same = __ballot(d == dl);
+            if (lane == src) atomicAdd(&sl.hist[dl], (int)__popcll(same));
+            else if (in && d != dl) atomicAdd(&sl.hist[d], 1);
+          }
         }
-      }
-      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup");
-      __builtin_amdgcn_wave_barrier();
-      int c[4], sum = 0;
+        __syncthreads();
+        if (wave == 0) {
+          int c[4], sum = 0;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        c[j] = s_hist[255 - 4 * lane - j];
-        sum += c[j];
-      }
-      int before = wave_incl_scan(sum, lane) - sum;  // keys in higher digits
-      int found = -1, rem = 0;
+          for (int j = 0; j < 4; ++j) {
+            const int bin = nb - 1 - 4 * lane - j;
+            c[j] = bin >= 0 ? sl.hist[bin] : 0;
+            sum += c[j];
+          }
+          int before = wave_incl_scan(sum, lane) - sum;  // keys in higher digits
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        if (before < remaining && before + c[j] >= remaining) {
-          found = 255 - 4 * lane - j;
-          rem = remaining - before;
+          for (int j = 0; j < 4; ++j) {
+            if (before < remaining && before + c[j] >= remaining) {
+              sl.red[2] = nb - 1 - 4 * lane - j;
+              sl.red[3] = remaining - before;
+              sl.red[4] = c[j];
+            }
+            before += c[j];
+          }
         }
-        before += c[j];
+        __syncthreads();
+        const int dg = sl.red[2], cb = sl.red[4];
+        remaining = sl.red[3];
+        tau |= (uint32_t)dg << shift;
+        tmask |= dmask << shift;
+        if (remaining == cb || shift == 0) break;
+        top = shift - 1;
       }
-      const int src = __ffsll((unsigned long long)__ballot(found >= 0)) - 1;
-      const int dgt = __shfl(found, src);
-      remaining = __shfl(rem, src);
-      prefix |= (uint32_t)dgt << shift;
-      pmask |= 0xFFu << shift;
-      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup");
-      __builtin_amdgcn_wave_barrier();
     }
-    tau = prefix;
-    need = remaining;  // keys equal to tau to take, lowest pages first
+    need = remaining;
   }
-  int eq_seen = 0, base = 0;
-  for (int c0 = 0; c0 < rows; c0 += KC) {
-    uint32_t kk[KC], ph[KC];
+  auto flags = [&](int i, bool& keep, bool& eq) {
+    const int p = p0 + i;
+    const bool valid = i < m && p < n;
+    const bool cand = valid && p >= f;
+    const uint32_t km = kk[i] & tmask;
+    eq = radix && cand && km == tau;
+    keep = (valid && p < f) || (cand && (take_all || (radix && km > tau)));
+  };
+  int nkeep = 0, neq = 0;
 #pragma unroll
-    for (int r = 0; r < KC; ++r) {
-      const int pc = min((c0 + r) * kWave + lane, nl);
-      kk[r] = s_key[pc];
-      ph[r] = s_phys[pc];
-    }
+  for (int i = 0; i < MAXM; ++i) {
+    if (i >= m) break;
+    bool keep, eq;
+    flags(i, keep, eq);
+    nkeep += keep;
+    neq += eq;
+  }
+  int tot;
+  const int ex = block_excl_scan<NW>((neq << 16) | nkeep, sl.scan, &tot);
+  int eqi = ex >> 16;
+  int pos = (ex & 0xffff) + min(eqi, need);
 #pragma unroll
-    for (int r = 0; r < KC; ++r) {
-      const int p = (c0 + r) * kWave + lane;
-      const bool cand = p < n && p >= f;
-      const bool eq = radix && cand && kk[r] == tau;
-      const unsigned long long eqm = __ballot(eq);
-      const bool ch = (p < n && p < f) ||
-                      (cand && (radix ? (kk[r] > tau ||
-                                         (eq && eq_seen + lanes_below(eqm) < need))
-                                      : take_all));
-      const unsigned long long chm = __ballot(ch);
-      const int pos = base + lanes_below(chm);
-      if (ch && pos < k_max) {  // the count never exceeds min(K_b, n_b); kept in bounds
-        srow[pos] = p;
-        prow[pos] = (int32_t)ph[r];
+  for (int i = 0; i < MAXM; ++i) {
+    if (i >= m) break;
+    bool keep, eq;
+    flags(i, keep, eq);
+    if (eq) keep = eqi++ < need;
+    if (keep) {
+      if (pos < k_max) {  // never false: the count is at most min(K_b, n_b)
+        if (srow) srow[pos] = p0 + i;
+        if (prow) prow[pos] = (int32_t)ph[i];
+        s_key[pos] = (uint32_t)(p0 + i);
+        s_phys[pos] = ph[i];
       }
-      eq_seen += __popcll(eqm);
-      base += __popcll(chm);
+      ++pos;
     }
   }
-  const int total = min(base, k_max);
-  for (int i = total + lane; i < k_max; i += kWave) {
-    srow[i] = -1;
-    prow[i] = 0;
+  const int total = min((tot & 0xffff) + min(tot >> 16, need), k_max);
+  if (srow) {
+    for (int i = total + tid; i < k_max; i += NT) {
+      srow[i] = -1;
+      if (prow) prow[i] = 0;
+    }
+    if (tid == 0) *count = total;
   }
-  if (lane == 0) *count = total;
+  __syncthreads();
+  return total;
 }
 
-// One workgroup per (unit, split): scores batches split, split + NS, ...
-// of the unit's pages.  With NS == 1 the keys stay in LDS and wave 0 selects
-// at the end; otherwise the keys go to the workspace for k_select.
-template <int G>
-constexpr int score_min_waves() { return G == 4 ? 4 : 1; }
-
-template <int DT, int D, int G, int NTH>
-__global__ __launch_bounds__(NTH, score_min_waves<G>()) void k_score_select(
-    const float* __restrict__ q, const void* __restrict__ meta,
-    const int32_t* __restrict__ bt, const int32_t* __restrict__ seq_lens,
-    int Hq, int Hkv, int P, int MP, int NP, int NS, int k_max,
-    const int32_t* __restrict__ k_per_seq, int n_sink,
-    int32_t* __restrict__ sel, int32_t* __restrict__ sel_count,
-    float* __restrict__ scores_out, uint32_t* __restrict__ keys,
-    int32_t* __restrict__ sel_phys) {
-  using Cfg = ScoreCfg<DT, D, G, NTH>;
+// Scores batches bstart, bstart + bstride, ... of one unit's n pages into
+// s_key (order keys).  s_phys holds the unit's block-table row.  No barrier.
+template <int DT, int D, int G, int NT>
+__device__ __forceinline__ void score_pages(const float* __restrict__ q,
+                                            const void* __restrict__ meta,
+                                            const uint32_t* s_phys, int b, int h, int Hq,
+                                            int Hkv, int n, int bstart, int bstride,
+                                            uint32_t* s_key) {
+  using Cfg = ScoreCfg<DT, D, G, NT>;
   constexpr int EB = Cfg::EB, C = Cfg::C, L = Cfg::L, PPW = Cfg::PPW, U = Cfg::U;
-  constexpr int NT = Cfg::NT, NW = Cfg::NW, PB = Cfg::PB;
-  extern __shared__ uint32_t smem[];
-  uint32_t* s_phys = smem;       // [MP] physical page of every logical page
-  uint32_t* s_key = smem + MP;   // [MP] order keys (NS == 1)
-  __shared__ int s_hist[256];
-
-  const int unit = blockIdx.x / NS, split = blockIdx.x - unit * NS;
-  const int b = unit / Hkv, h = unit - b * Hkv;
-  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
-  // the whole block-table row (MP entries, all allocated) is staged without
-  // waiting for the length, so both loads share one memory latency
-  const int32_t* bt_row = bt + (size_t)b * MP;
-  stage_row<4>(bt_row, MP, NT, s_phys, [NP](int32_t e) { return (uint32_t)clampi(e, 0, NP - 1); });
-  const int len = clampi(seq_lens[b], 0, MP * P);
-  const int n = (len + P - 1) / P;
+  constexpr int NW = Cfg::NW, PB = Cfg::PB;
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   const int nbatch = (n + PB - 1) / PB;
-  if (split > 0 && split >= nbatch) return;  // whole workgroup: no pages
-
   const int chunk = lane % L, slot = lane / L;
   float qp[G][C], qn[G][C];
 #pragma unroll
@@ -454,8 +517,6 @@ __global__ __launch_bounds__(NTH, score_min_waves<G>()) void k_score_select(
       }
     }
   }
-  __syncthreads();
-
   const char* mb = reinterpret_cast<const char*>(meta);
   // masked lanes read a valid row (page n-1) and drop it: no branches around
   // the loads, so the compiler's load counters track both buffers exactly
@@ -489,19 +550,66 @@ __global__ __launch_bounds__(NTH, score_min_waves<G>()) void k_score_select(
       if (p < n && chunk == 0) s_key[p] = order_key(best);
     }
   };
-  uint4 amn[U], amx[U], bmn[U], bmx[U];
-  int bi = split;
-  if (bi < nbatch) load_batch(bi, amn, amx);
-  while (bi < nbatch) {
-    const int nx = bi + NS;
-    if (nx < nbatch) load_batch(nx, bmn, bmx);
-    score_batch(bi, amn, amx);
-    if (nx >= nbatch) break;
-    const int nx2 = nx + NS;
-    if (nx2 < nbatch) load_batch(nx2, amn, amx);
-    score_batch(nx, bmn, bmx);
-    bi = nx2;
+  // a ring of DEPTH batches in flight: batch bi's slot is refilled with
+  // batch bi + DEPTH*bstride right after bi is scored (indices past the
+  // last batch reload the last one, so the loads need no branch)
+  constexpr int DEPTH = U == 1 ? 4 : 2;
+  if (bstart >= nbatch) return;
+  uint4 rmn[DEPTH][U], rmx[DEPTH][U];
+#pragma unroll
+  for (int i = 0; i < DEPTH; ++i)
+    if (i == 0 || bstart + i * bstride < nbatch) load_batch(bstart + i * bstride, rmn[i], rmx[i]);
+  for (int base = bstart; base < nbatch; base += DEPTH * bstride) {
+#pragma unroll
+    for (int i = 0; i < DEPTH; ++i) {
+      const int bi = base + i * bstride;
+      if (bi < nbatch) score_batch(bi, rmn[i], rmx[i]);
+      if (base + DEPTH * bstride < nbatch)
+        load_batch(min(bi + DEPTH * bstride, nbatch - 1), rmn[i], rmx[i]);
+    }
   }
+}
+
+// One workgroup per (unit, split): scores batches split, split + NS, ...
+// of the unit's pages.  With NS == 1 the keys stay in LDS and the workgroup
+// selects at the end; otherwise the keys go to the workspace for k_select.
+template <int G>
+constexpr int score_min_waves() { return 1; }
+
+template <int DT, int D, int G, int NTH>
+__global__ __launch_bounds__(NTH, score_min_waves<G>()) void k_score_select(
+    const float* __restrict__ q, const void* __restrict__ meta,
+    const int32_t* __restrict__ bt, const int32_t* __restrict__ seq_lens,
+    int Hq, int Hkv, int P, int MP, int NP, int NS, int k_max,
+    const int32_t* __restrict__ k_per_seq, int n_sink,
+    int32_t* __restrict__ sel, int32_t* __restrict__ sel_count,
+    float* __restrict__ scores_out, uint32_t* __restrict__ keys,
+    int32_t* __restrict__ sel_phys) {
+  using Cfg = ScoreCfg<DT, D, G, NTH>;
+  constexpr int NT = Cfg::NT, PB = Cfg::PB;
+  extern __shared__ uint32_t smem[];
+  uint32_t* s_phys = smem;       // [MP] physical page of every logical page
+  uint32_t* s_key = smem + MP;   // [MP] order keys (NS == 1)
+  __shared__ SelectLds<NT> sl;
+
+  const int unit = blockIdx.x / NS, split = blockIdx.x - unit * NS;
+  const int b = unit / Hkv, h = unit - b * Hkv;
+  const int tid = threadIdx.x;
+  if (tid == 0) {
+    sl.red[0] = -1;
+    sl.red[1] = 0;
+  }
+  // the whole block-table row (MP entries, all allocated) is staged without
+  // waiting for the length, so both loads share one memory latency
+  const int32_t* bt_row = bt + (size_t)b * MP;
+  stage_row<4>(bt_row, MP, NT, s_phys, [NP](int32_t e) { return (uint32_t)clampi(e, 0, NP - 1); });
+  const int len = clampi(seq_lens[b], 0, MP * P);
+  const int kb = clampi(k_per_seq ? k_per_seq[b] : k_max, 1, k_max);
+  const int n = (len + P - 1) / P;
+  const int nbatch = (n + PB - 1) / PB;
+  if (split > 0 && split >= nbatch) return;  // whole workgroup: no pages
+  __syncthreads();
+  score_pages<DT, D, G, NT>(q, meta, s_phys, b, h, Hq, Hkv, n, split, NS, s_key);
   __syncthreads();
   // this workgroup's pages: keys for k_select (split rows), optional scores
   if (NS > 1 || scores_out) {
@@ -517,38 +625,42 @@ __global__ __launch_bounds__(NTH, score_min_waves<G>()) void k_score_select(
         }
       }
   }
-  if (NS > 1 || wave != 0) return;
-  int kb = k_per_seq ? k_per_seq[b] : k_max;
-  kb = clampi(kb, 1, k_max);
+  if (NS > 1) return;
   const int keff = min(kb, n), f = min(n_sink, keff);
-  select_wave(s_key, s_phys, n, keff, f, k_max, sel + (size_t)unit * k_max,
-              sel_phys + (size_t)unit * k_max, sel_count + unit, s_hist);
+  select_block<NT>(s_key, s_phys, n, keff, f, k_max, sel + (size_t)unit * k_max,
+                   sel_phys + (size_t)unit * k_max, sel_count + unit, sl);
 }
 
-// Selection of units scored by several workgroups: one wave per (sequence,
-// KV head) loads the unit's keys and block-table row into LDS.
-__global__ __launch_bounds__(64) void k_select(
+// Selection of units scored by several workgroups: one workgroup per
+// (sequence, KV head) loads the unit's keys and block-table row into LDS.
+constexpr int kSelectThreads = 256;
+
+__global__ __launch_bounds__(kSelectThreads) void k_select(
     const int32_t* __restrict__ bt, const int32_t* __restrict__ seq_lens, int Hkv, int P,
     int MP, int NP, int k_max, const int32_t* __restrict__ k_per_seq, int n_sink,
     const uint32_t* __restrict__ keys, int32_t* __restrict__ sel,
     int32_t* __restrict__ sel_count, int32_t* __restrict__ sel_phys) {
+  constexpr int NT = kSelectThreads;
   extern __shared__ uint32_t smem[];
   uint32_t* s_phys = smem;      // [MP]
   uint32_t* s_key = smem + MP;  // [MP]
-  __shared__ int s_hist[256];
+  __shared__ SelectLds<NT> sl;
   const int unit = blockIdx.x, b = unit / Hkv;
-  stage_row<16>(reinterpret_cast<const int32_t*>(keys + (size_t)unit * MP), MP, kWave, s_key,
-                [](int32_t k) { return (uint32_t)k; });
-  stage_row<16>(bt + (size_t)b * MP, MP, kWave, s_phys,
-                [NP](int32_t e) { return (uint32_t)clampi(e, 0, NP - 1); });
+  if (threadIdx.x == 0) {
+    sl.red[0] = -1;
+    sl.red[1] = 0;
+  }
+  stage_row<8>(reinterpret_cast<const int32_t*>(keys + (size_t)unit * MP), MP, NT, s_key,
+               [](int32_t k) { return (uint32_t)k; });
+  stage_row<8>(bt + (size_t)b * MP, MP, NT, s_phys,
+               [NP](int32_t e) { return (uint32_t)clampi(e, 0, NP - 1); });
   const int len = clampi(seq_lens[b], 0, MP * P);
+  const int kb = clampi(k_per_seq ? k_per_seq[b] : k_max, 1, k_max);
   const int n = (len + P - 1) / P;
   __syncthreads();
-  int kb = k_per_seq ? k_per_seq[b] : k_max;
-  kb = clampi(kb, 1, k_max);
   const int keff = min(kb, n), f = min(n_sink, keff);
-  select_wave(s_key, s_phys, n, keff, f, k_max, sel + (size_t)unit * k_max,
-              sel_phys + (size_t)unit * k_max, sel_count + unit, s_hist);
+  select_block<NT>(s_key, s_phys, n, keff, f, k_max, sel + (size_t)unit * k_max,
+                   sel_phys + (size_t)unit * k_max, sel_count + unit, sl);
 }
 
 // ---------------------------------------------------------------------------
@@ -702,49 +814,103 @@ __device__ __forceinline__ void merge_slot_state(float (&m)[G], float (&l)[G],
   }
 }
 
-// One workgroup per (sequence, KV head, split); a split is TPW consecutive
-// tiles of TILE stream tokens.  Every lane slot keeps a running (max, sum,
-// acc) over its tokens; tile t+1's K/V loads are issued before tile t is
-// processed.  Slots and waves are merged once, at the end.
-template <int DT, int D, int G, int NT>
-__global__ __launch_bounds__(NT) void k_decode_split(
-    const float* __restrict__ q, const void* __restrict__ k_pool,
-    const void* __restrict__ v_pool, const int32_t* __restrict__ bt,
-    const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ sel,
-    const int32_t* __restrict__ sel_phys, const int32_t* __restrict__ sel_count,
-    int Hq, int Hkv, int log2P, int MP, int NP, int k_max, int S_max, int TPW,
-    float qscale, float* __restrict__ partials, float* __restrict__ out) {
-  constexpr int EB = KV<DT>::bytes, C = KV<DT>::per16, L = D / C;
-  constexpr int SPW = kWave / L, NW = NT / kWave, TPI = NW * SPW, J = 4;
-  constexpr int TILE = J * TPI;
-  constexpr int MAXE = kMaxTilesPerSplit * TILE / 8;  // sel entries of a split (P >= 8)
-  __shared__ int s_lp[MAXE];
-  __shared__ uint32_t s_ph[MAXE];
-  __shared__ float s_acc[NW][G][D + 1];
-  __shared__ float s_mw[NW][G];
-
-  const int P = 1 << log2P;
-  const int unit = blockIdx.x / S_max, split = blockIdx.x - unit * S_max;
-  const int b = unit / Hkv, h = unit - b * Hkv;
-  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
-  const long span = (long)TPW * TILE;
-  const long t0 = (long)split * span;
-  const int e0 = (int)(t0 >> log2P);                                  // < k_max by the grid
-  const int ecap = (int)min(max(1L, span >> log2P), (long)(k_max - e0));  // <= MAXE
-  for (int i = tid; i < ecap; i += NT) {
-    const int lp = sel[(size_t)unit * k_max + e0 + i];
-    const int ph = sel_phys ? sel_phys[(size_t)unit * k_max + e0 + i]
-                            : bt[(size_t)b * MP + clampi(lp, 0, MP - 1)];
-    s_lp[i] = lp;
-    s_ph[i] = (uint32_t)clampi(ph, 0, NP - 1);
+// Selected-token stream of one (sequence, KV head): entry e of the list
+// (e0 + e in sel order) is logical page s_lp[e] at physical page s_ph[e];
+// token ts of the stream is slot ts mod P of entry ts / P - e0, and exists
+// when it lies before the sequence length.  npg entries are listed.
+struct TokenList {
+  const int* lp;
+  const uint32_t* ph;
+  int npg, e0, len, log2P, Hkv, h, D;
+  // pool element offset of stream token ts, or -1 when it does not exist
+  __device__ __forceinline__ long off(long ts) const {
+    const int P = 1 << log2P;
+    const int e = (int)(ts >> log2P) - e0;
+    const int st = (int)(ts & (P - 1));
+    const int ec = min(e, npg - 1);
+    const int l = lp[ec];
+    if (e >= npg || l < 0 || l * P + st >= len) return -1;
+    return (long)((((size_t)ph[ec] * Hkv + h) * P + st) * D);
   }
-  const int cnt = clampi(sel_count[unit], 0, k_max);
-  const int len = clampi(seq_lens[b], 0, MP * P);
+  // slot 0 of the first entry: a token that exists (masked loads read it)
+  __device__ __forceinline__ long safe() const {
+    return (long)((((size_t)ph[0] * Hkv + h) << log2P) * D);
+  }
+};
+
+// The 16 stream tokens [tw, tw + 16) of one MFMA wave step (tw a multiple of
+// 16) lie in one list entry when P >= 16 and in two consecutive entries when
+// P == 8.  All fields are wave-uniform: token t of the step is at pool
+// offset base0 + t*D (t < split, valid if t < lim0) or base1 + (t-split)*D
+// (valid if t - split < lim1).
+struct StepMap {
+  long base0, base1;
+  int split, lim0, lim1, D;
+  __device__ __forceinline__ long off(int t) const {
+    const bool first = t < split;
+    const int tt = first ? t : t - split;
+    const bool ok = tt < (first ? lim0 : lim1);
+    return ok ? (first ? base0 : base1) + (long)tt * D : -1;
+  }
+};
+
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+// Map of the step starting at stream token tw.
+__device__ __forceinline__ StepMap step_map(const TokenList& tl, long tw) {
+  const int P = 1 << tl.log2P;
+  const int e = (int)(tw >> tl.log2P) - tl.e0;
+  const int st0 = (int)(tw & (P - 1));
+  StepMap m;
+  m.split = min(16, P - st0);
+  m.D = tl.D;
+  m.lim0 = 0;
+  m.lim1 = 0;
+  m.base0 = m.base1 = 0;
+  const int ec = uniform(clampi(e, 0, tl.npg - 1));
+  const int l0 = uniform(tl.lp[ec]);
+  const int p0 = uniform((int)tl.ph[ec]);
+  if (e < tl.npg && l0 >= 0) m.lim0 = clampi(tl.len - (l0 * P + st0), 0, m.split);
+  m.base0 = (long)((((size_t)p0 * tl.Hkv + tl.h) * P + st0) * tl.D);
+  if (m.split < 16) {
+    const int ec1 = uniform(clampi(e + 1, 0, tl.npg - 1));
+    const int l1 = uniform(tl.lp[ec1]);
+    const int p1 = uniform((int)tl.ph[ec1]);
+    if (e + 1 < tl.npg && l1 >= 0) m.lim1 = clampi(tl.len - l1 * P, 0, 16 - m.split);
+    m.base1 = (long)((((size_t)p1 * tl.Hkv + tl.h) * P) * tl.D);
+  }
+  return m;
+}
+
+// VALU decode of stream tokens [t0, t_end) by the NT threads of a
+// workgroup, in tiles of TILE tokens.  Every lane slot keeps a running (max,
+// sum, acc) over its tokens; tile t+1's K/V loads are issued before tile t is
+// processed.  Ends with each wave's state in s_acc[wave] / s_mw[wave] (no
+// barrier).
+template <int DT, int D, int G, int NT>
+struct ValuDecode {
+  static constexpr int EB = KV<DT>::bytes, C = KV<DT>::per16, L = D / C;
+  // loads in flight per lane and buffer: 16-wave workgroups hold half as many
+  static constexpr int SPW = kWave / L, NW = NT / kWave, TPI = NW * SPW, J = NT >= 1024 ? 2 : 4;
+  static constexpr int TILE = J * TPI;
+};
+
+template <int DT, int D, int G, int NT>
+__device__ __forceinline__ void valu_decode_range(const float* __restrict__ qg0,
+                                                  const char* __restrict__ kb,
+                                                  const char* __restrict__ vb,
+                                                  const TokenList& tl, long t0, long t_end,
+                                                  float qscale, float (*s_acc)[G][D + 1],
+                                                  float (*s_mw)[G]) {
+  using VD = ValuDecode<DT, D, G, NT>;
+  constexpr int EB = VD::EB, C = VD::C, L = VD::L, SPW = VD::SPW, TPI = VD::TPI, J = VD::J;
+  constexpr int TILE = VD::TILE;
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   const int chunk = lane % L, slot = lane / L;
   float qs[G][C];
 #pragma unroll
   for (int g = 0; g < G; ++g) {
-    const float* qg = q + ((size_t)b * Hq + h * G + g) * D + chunk * C;
+    const float* qg = qg0 + (size_t)g * D + chunk * C;
 #pragma unroll
     for (int c = 0; c < C; c += 4) {
       const float4 x4 = *reinterpret_cast<const float4*>(qg + c);
@@ -754,33 +920,14 @@ __global__ __launch_bounds__(NT) void k_decode_split(
       qs[g][c + 3] = x4.w * qscale;
     }
   }
-  const long t_all = (long)cnt << log2P;
-  const long t_end = min(t_all, t0 + span);
-  if (t0 >= t_end) {  // whole workgroup: no work
-    if (cnt == 0 && split == 0)
-      for (int i = tid; i < G * D; i += NT) out[((size_t)b * Hq + h * G) * D + i] = 0.f;
-    return;
-  }
-  __syncthreads();
-  const int npg = min(cnt - e0, ecap);
   const int ntiles = (int)((t_end - t0 + TILE - 1) / TILE);
-
-  const char* kb = reinterpret_cast<const char*>(k_pool);
-  const char* vb = reinterpret_cast<const char*>(v_pool);
-  // masked slots read slot 0 of the first selected page (always a valid
-  // token) and are dropped by `ok`: the loads need no branches
-  const size_t safe_off = (((size_t)s_ph[0] * Hkv + h) * P) * D + chunk * C;
+  const long safe_off = tl.safe() + chunk * C;
   auto load_tile = [&](int it, uint4 (&kr)[J], uint4 (&vr)[J], bool (&ok)[J]) {
 #pragma unroll
     for (int j = 0; j < J; ++j) {
-      const long ts = t0 + (long)it * TILE + j * TPI + wave * SPW + slot;
-      const int e = (int)(ts >> log2P) - e0;
-      const int st = (int)(ts & (P - 1));
-      const int ec = min(e, npg - 1);
-      const int lp = s_lp[ec];
-      ok[j] = e < npg && lp >= 0 && lp * P + st < len;
-      const size_t off =
-          ok[j] ? (((size_t)s_ph[ec] * Hkv + h) * P + st) * D + chunk * C : safe_off;
+      const long o = tl.off(t0 + (long)it * TILE + j * TPI + wave * SPW + slot);
+      ok[j] = o >= 0;
+      const long off = ok[j] ? o + chunk * C : safe_off;
       kr[j] = ld16(kb + off * EB);
       vr[j] = ld16(vb + off * EB);
     }
@@ -838,7 +985,7 @@ __global__ __launch_bounds__(NT) void k_decode_split(
   {
     uint4 ka[J], va[J], kb2[J], vb2[J];
     bool oka[J], okb[J];
-    load_tile(0, ka, va, oka);
+    if (ntiles > 0) load_tile(0, ka, va, oka);
     for (int it = 0; it < ntiles; it += 2) {
       if (it + 1 < ntiles) load_tile(it + 1, kb2, vb2, okb);
       process(ka, va, oka);
@@ -862,6 +1009,66 @@ __global__ __launch_bounds__(NT) void k_decode_split(
       }
     }
   }
+}
+
+// Stages sel entries [e0, e0 + ecap) of a unit (logical page, physical
+// page) into LDS for a split decode workgroup.
+__device__ __forceinline__ void stage_split_list(const int32_t* __restrict__ sel,
+                                                 const int32_t* __restrict__ sel_phys,
+                                                 const int32_t* __restrict__ bt, int unit,
+                                                 int b, int MP, int NP, int k_max, int e0,
+                                                 int ecap, int nt, int* s_lp, uint32_t* s_ph) {
+  for (int i = threadIdx.x; i < ecap; i += nt) {
+    const int lp = sel[(size_t)unit * k_max + e0 + i];
+    const int ph = sel_phys ? sel_phys[(size_t)unit * k_max + e0 + i]
+                            : bt[(size_t)b * MP + clampi(lp, 0, MP - 1)];
+    s_lp[i] = lp;
+    s_ph[i] = (uint32_t)clampi(ph, 0, NP - 1);
+  }
+}
+
+// One workgroup per (sequence, KV head, split); a split is TPW consecutive
+// tiles of the selected-token stream.  Slots and waves are merged once, at
+// the end; a unit covered by one split writes `out`, others leave partial
+// states for k_merge.
+template <int DT, int D, int G, int NT>
+__global__ __launch_bounds__(NT) void k_decode_split(
+    const float* __restrict__ q, const void* __restrict__ k_pool,
+    const void* __restrict__ v_pool, const int32_t* __restrict__ bt,
+    const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ sel,
+    const int32_t* __restrict__ sel_phys, const int32_t* __restrict__ sel_count,
+    int Hq, int Hkv, int log2P, int MP, int NP, int k_max, int S_max, int TPW,
+    float qscale, float* __restrict__ partials, float* __restrict__ out) {
+  using VD = ValuDecode<DT, D, G, NT>;
+  constexpr int NW = VD::NW, TILE = VD::TILE;
+  constexpr int MAXE = kMaxTilesPerSplit * TILE / 8;  // sel entries of a split (P >= 8)
+  __shared__ int s_lp[MAXE];
+  __shared__ uint32_t s_ph[MAXE];
+  __shared__ float s_acc[NW][G][D + 1];
+  __shared__ float s_mw[NW][G];
+
+  const int unit = blockIdx.x / S_max, split = blockIdx.x - unit * S_max;
+  const int b = unit / Hkv, h = unit - b * Hkv;
+  const long span = (long)TPW * TILE;
+  const long t0 = (long)split * span;
+  const int e0 = (int)(t0 >> log2P);                                  // < k_max by the grid
+  const int ecap = (int)min(max(1L, span >> log2P), (long)(k_max - e0));  // <= MAXE
+  stage_split_list(sel, sel_phys, bt, unit, b, MP, NP, k_max, e0, ecap, NT, s_lp, s_ph);
+  const int cnt = clampi(sel_count[unit], 0, k_max);
+  const int len = clampi(seq_lens[b], 0, MP << log2P);
+  const long t_all = (long)cnt << log2P;
+  const long t_end = min(t_all, t0 + span);
+  if (t0 >= t_end) {  // whole workgroup: no work
+    if (cnt == 0 && split == 0)
+      for (int i = threadIdx.x; i < G * D; i += NT) out[((size_t)b * Hq + h * G) * D + i] = 0.f;
+    return;
+  }
+  __syncthreads();
+  const TokenList tl{s_lp, s_ph, min(cnt - e0, ecap), e0, len, log2P, Hkv, h, D};
+  valu_decode_range<DT, D, G, NT>(q + ((size_t)b * Hq + h * G) * D,
+                                  reinterpret_cast<const char*>(k_pool),
+                                  reinterpret_cast<const char*>(v_pool), tl, t0, t_end, qscale,
+                                  s_acc, s_mw);
   __syncthreads();
   finish_split<D, G, NT, NW>(s_acc, s_mw, partials, out, b, h, Hq, S_max, split,
                              (int)((t_all + span - 1) / span));
@@ -869,11 +1076,9 @@ __global__ __launch_bounds__(NT) void k_decode_split(
 
 // ---------------------------------------------------------------------------
 // K2 for grouped-query heads (G = 4, 8) on 16-bit KV: both contractions on
-// MFMA, streamed 16 tokens per wave step
+// MFMA, 16 tokens per wave step
 // ---------------------------------------------------------------------------
 //
-// A workgroup's four waves walk its split in steps of 64 tokens, 16 per wave,
-// keeping a running (max, sum, out) per query head across steps.
 //   logits^T[token][g] = K[token][:] . q[g][:]   (v_mfma_f32_16x16x32)
 //     A = K rows straight from the pool (lane: token n16, 8 channels at
 //     32*ch + 8*c4), B = q^T; q is split into hi + lo 16-bit parts so the
@@ -882,13 +1087,15 @@ __global__ __launch_bounds__(NT) void k_decode_split(
 //     4*c4 + r.
 //   out[g][d] += sum_token p[g][token] * V[token][d]   (v_mfma_f32_16x16x16)
 //     A = p (hi + lo parts): the lane's 4 probabilities are exactly its A
-//     fragment; B = V read column-wise from the wave's 16 V rows staged in
-//     LDS (rows padded by 16 bytes so the four lane groups hit disjoint
-//     banks).
+//     fragment.  B needs 4 consecutive tokens of one channel per lane: lane
+//     (n16, c4) loads the W = D/16 channels W*n16 .. W*n16 + W-1 of tokens
+//     4*c4 .. 4*c4 + 3 (four 8- or 16-byte loads, whole rows per wave load)
+//     and v_perm packs channel W*n16 + e of the four tokens into the B
+//     fragment of output tile e, so V never goes through LDS.  Output tile e
+//     holds channel W*n16 + e in column n16.
 // Rows of the 16-row fragments beyond G carry zero queries and are never
 // stored.  Masked tokens read a valid token's row and are then dropped: their
-// V rows are zero in LDS and their logits -inf, so p = 0 multiplies a finite
-// zero.
+// logits are -inf, so p = 0 multiplies finite values.
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
@@ -936,55 +1143,40 @@ __device__ __forceinline__ void split_hi_lo(float x, typename Mma<DT>::elem& hi,
   lo = (E)(x - (float)hi);
 }
 
-template <int DT, int D, int G>
-__global__ __launch_bounds__(256, 3) void k_decode_mfma(
-    const float* __restrict__ q, const void* __restrict__ k_pool,
-    const void* __restrict__ v_pool, const int32_t* __restrict__ bt,
-    const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ sel,
-    const int32_t* __restrict__ sel_phys, const int32_t* __restrict__ sel_count,
-    int Hq, int Hkv, int log2P, int MP, int NP, int k_max, int S_max, int TPW,
-    float qscale, float* __restrict__ partials, float* __restrict__ out) {
+template <int DT, int D>
+struct MfmaDecode {
+  static constexpr int WS = 16;         // tokens per wave step
+  static constexpr int NCH = D / 32;    // 32-channel chunks (logits: K, output: V)
+  static constexpr int NDT = D / 16;    // 16-channel tiles of the output
+};
+
+// MFMA decode of stream tokens [t0, t_end) by the NW waves of a workgroup.
+// 16-token steps are dealt round-robin to the waves; a wave takes its steps
+// CH at a time (a chunk): the chunk's K and V loads are all issued together,
+// one chunk ahead of the arithmetic, and the running softmax state is
+// rescaled once per chunk.  Ends with each wave's state in s_acc[wave] /
+// s_mw[wave] (no barrier).
+template <int DT, int D, int G, int NW, int CH>
+__device__ __forceinline__ void mfma_decode_range(const float* __restrict__ qg0,
+                                                  const char* __restrict__ kb,
+                                                  const char* __restrict__ vb,
+                                                  const TokenList& tl, long t0, long t_end,
+                                                  float qscale, float (*s_acc)[G][D + 1],
+                                                  float (*s_mw)[G]) {
   using M = Mma<DT>;
+  using MD = MfmaDecode<DT, D>;
   using vec8 = typename M::vec8;
   using vec4 = typename M::vec4;
   using E = typename M::elem;
-  constexpr int NT = 256, NW = NT / kWave, WS = 16, TILE = NW * WS;
-  constexpr int NCH = D / 32;   // 32-channel chunks of the logit contraction
-  constexpr int NDT = D / 16;   // 16-channel tiles of the output
-  constexpr int ROW = D + 8;    // LDS row stride in 16-bit elements
-  constexpr int LR = D / 8;     // lanes per V row (16 bytes each)
-  constexpr int RPI = kWave / LR, NVL = WS / RPI;
-  constexpr int MAXE = kMaxTilesPerSplit * TILE / 8;
+  constexpr int WS = MD::WS, NCH = MD::NCH, NDT = MD::NDT;
   static_assert(G <= 16, "one 16-row fragment holds the query group");
-  __shared__ int s_lp[MAXE];
-  __shared__ uint32_t s_ph[MAXE];
-  __shared__ __align__(16) uint16_t s_v[NW][WS][ROW];
-  __shared__ float s_acc[NW][G][D + 1];
-  __shared__ float s_mw[NW][G];
-
-  const int P = 1 << log2P;
-  const int unit = blockIdx.x / S_max, split = blockIdx.x - unit * S_max;
-  const int b = unit / Hkv, h = unit - b * Hkv;
-  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   const int n16 = lane & 15, c4 = lane >> 4;
-  const long span = (long)TPW * TILE;
-  const long t0 = (long)split * span;
-  const int e0 = (int)(t0 >> log2P);
-  const int ecap = (int)min(max(1L, span >> log2P), (long)(k_max - e0));
-  for (int i = tid; i < ecap; i += NT) {
-    const int lp = sel[(size_t)unit * k_max + e0 + i];
-    const int ph = sel_phys ? sel_phys[(size_t)unit * k_max + e0 + i]
-                            : bt[(size_t)b * MP + clampi(lp, 0, MP - 1)];
-    s_lp[i] = lp;
-    s_ph[i] = (uint32_t)clampi(ph, 0, NP - 1);
-  }
-  const int cnt = clampi(sel_count[unit], 0, k_max);
-  const int len = clampi(seq_lens[b], 0, MP * P);
   // B operand of the logits: column g = n16, 8 channels per chunk
   vec8 qhi[NCH], qlo[NCH];
   {
     const bool has = n16 < G;
-    const float* qg = q + ((size_t)b * Hq + h * G + (has ? n16 : 0)) * D + 8 * c4;
+    const float* qg = qg0 + (size_t)(has ? n16 : 0) * D + 8 * c4;
 #pragma unroll
     for (int ch = 0; ch < NCH; ++ch) {
       const float4 a = *reinterpret_cast<const float4*>(qg + 32 * ch);
@@ -999,69 +1191,72 @@ __global__ __launch_bounds__(256, 3) void k_decode_mfma(
       }
     }
   }
-  const long t_all = (long)cnt << log2P;
-  const long t_end = min(t_all, t0 + span);
-  if (t0 >= t_end) {  // whole workgroup: no work
-    if (cnt == 0 && split == 0)
-      for (int i = tid; i < G * D; i += NT) out[((size_t)b * Hq + h * G) * D + i] = 0.f;
-    return;
-  }
-  __syncthreads();
-  const int npg = min(cnt - e0, ecap);
-  const int nsteps = (int)((t_end - t0 + TILE - 1) / TILE);
-  // pool element offset of split-local token `t`, or -1 when masked
-  auto token_off = [&](long t) -> long {
-    const long ts = t0 + t;
-    const int e = (int)(ts >> log2P) - e0;
-    const int st = (int)(ts & (P - 1));
-    const int ec = min(e, npg - 1);
-    const int lp = s_lp[ec];
-    if (e >= npg || lp < 0 || lp * P + st >= len) return -1;
-    return (long)((((size_t)s_ph[ec] * Hkv + h) * P + st) * D);
+  const long nsteps = (t_end - t0 + WS - 1) / WS;
+  const int mine = nsteps > wave ? (int)((nsteps - wave + NW - 1) / NW) : 0;
+  const long safe_off = tl.safe();
+  constexpr int VW = D / 32;  // dwords of V per token and lane (W = 2*VW channels)
+  struct Chunk {
+    uint4 k[CH][NCH];          // token n16, channels 32*ch + 8*c4 .. + 7
+    uint32_t v[CH][4][VW];     // token 4*c4 + j, channels W*n16 .. W*n16 + W-1
   };
-  // masked tokens read slot 0 of the first selected page (a valid token)
-  const long safe_off = (long)((((size_t)s_ph[0] * Hkv + h) * P) * D);
-  const char* kb = reinterpret_cast<const char*>(k_pool);
-  const char* vb = reinterpret_cast<const char*>(v_pool);
-
+  auto tw_of = [&](int i) { return t0 + (long)(wave + (long)i * NW) * WS; };
+  // the chunk of the wave's steps i0 .. i0+CH-1 (clamped to its last step,
+  // so the loads need no branch; masked tokens read a token that exists)
+  auto load = [&](int i0, Chunk& c) {
+#pragma unroll
+    for (int cc = 0; cc < CH; ++cc) {
+      const StepMap sm = step_map(tl, tw_of(min(i0 + cc, mine - 1)));
+      const long ko = sm.off(n16);
+#pragma unroll
+      for (int ch = 0; ch < NCH; ++ch)
+        c.k[cc][ch] = ld16(kb + ((ko >= 0 ? ko : safe_off) + 32 * ch + 8 * c4) * 2);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const long vo = sm.off(4 * c4 + j);
+        const char* vp = vb + ((vo >= 0 ? vo : safe_off) + 2 * VW * n16) * 2;
+        if constexpr (VW == 2) {
+          const uint2 x = *reinterpret_cast<const uint2*>(vp);
+          c.v[cc][j][0] = x.x;
+          c.v[cc][j][1] = x.y;
+        } else {
+          const uint4 x = ld16(vp);
+          c.v[cc][j][0] = x.x;
+          c.v[cc][j][1] = x.y;
+          c.v[cc][j][2] = x.z;
+          c.v[cc][j][3] = x.w;
+        }
+      }
+    }
+  };
   float m_run = -INFINITY, l_run = 0.f;  // head g = n16
   f32x4_t o[NDT];
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt) o[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  for (int it = 0; it < nsteps; ++it) {
-    const long tw = (long)it * TILE + wave * WS;  // the wave's first token
-    const long koff = token_off(tw + n16);
-    uint4 kr[NCH];
+  auto compute = [&](int i0, const Chunk& c) {
+    // logits of head n16 for tokens 4*c4 + r of each step, log2 units;
+    // tokens that do not exist (or steps past the wave's last) get -inf
+    float z[CH][4];
 #pragma unroll
-    for (int ch = 0; ch < NCH; ++ch)
-      kr[ch] = ld16(kb + ((koff >= 0 ? koff : safe_off) + 32 * ch + 8 * c4) * 2);
-    uint4 vr[NVL];
-    bool vok[NVL];
+    for (int cc = 0; cc < CH; ++cc) {
 #pragma unroll
-    for (int u = 0; u < NVL; ++u) {
-      const long off = token_off(tw + u * RPI + lane / LR);
-      vok[u] = off >= 0;
-      vr[u] = ld16(vb + ((vok[u] ? off : safe_off) + (lane % LR) * 8) * 2);
+      for (int r = 0; r < 4; ++r) z[cc][r] = -INFINITY;
+      if (i0 + cc >= mine) continue;  // padding of the wave's last chunk
+      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ch = 0; ch < NCH; ++ch) {
+        const vec8 a = __builtin_bit_cast(vec8, c.k[cc][ch]);
+        acc = M::mma32(a, qhi[ch], acc);
+        acc = M::mma32(a, qlo[ch], acc);
+      }
+      const StepMap sm = step_map(tl, tw_of(i0 + cc));
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (sm.off(4 * c4 + r) >= 0) z[cc][r] = acc[r] * qscale;
     }
-    // the previous step's reads of s_v are issued before these writes
-    // (LDS requests of one wave complete in order)
-    __builtin_amdgcn_wave_barrier();
+    float tm = -INFINITY;
 #pragma unroll
-    for (int u = 0; u < NVL; ++u)
-      *reinterpret_cast<uint4*>(&s_v[wave][u * RPI + lane / LR][(lane % LR) * 8]) =
-          vok[u] ? vr[u] : make_uint4(0, 0, 0, 0);
-    // logits of head n16 for tokens 4*c4 + r, log2 units
-    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ch = 0; ch < NCH; ++ch) {
-      const vec8 a = __builtin_bit_cast(vec8, koff >= 0 ? kr[ch] : make_uint4(0, 0, 0, 0));
-      acc = M::mma32(a, qhi[ch], acc);
-      acc = M::mma32(a, qlo[ch], acc);
-    }
-    float z[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) z[r] = token_off(tw + 4 * c4 + r) >= 0 ? acc[r] * qscale : -INFINITY;
-    float tm = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
+    for (int cc = 0; cc < CH; ++cc)
+      tm = fmaxf(tm, fmaxf(fmaxf(z[cc][0], z[cc][1]), fmaxf(z[cc][2], z[cc][3])));
     tm = fmaxf(tm, __shfl_xor(tm, 16));
     tm = fmaxf(tm, __shfl_xor(tm, 32));
     const float mn = fmaxf(m_run, tm);
@@ -1069,56 +1264,236 @@ __global__ __launch_bounds__(256, 3) void k_decode_mfma(
     const float ms = mn == -INFINITY ? 0.f : mn;
     m_run = mn;
     l_run *= alpha;
-    // output rows are heads 4*c4 + r: their factors come from lanes 4*c4 + r
+    // output rows are heads 4*c4 + r: their factors sit in lanes 4*c4 + r
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const float ar = __shfl(alpha, 4 * c4 + r);
+      float ag[4];
+#pragma unroll
+      for (int cg = 0; cg < 4; ++cg)
+        ag[cg] = 4 * cg + r < G
+                     ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), 4 * cg + r))
+                     : 1.f;
+      const float ar = c4 == 0 ? ag[0] : c4 == 1 ? ag[1] : c4 == 2 ? ag[2] : ag[3];
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) o[dt][r] *= ar;
     }
-    vec4 phi, plo;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float pz = __builtin_amdgcn_exp2f(z[r] - ms);
-      l_run += pz;
-      E hi, lo;
-      split_hi_lo<DT>(pz * M::kPScale, hi, lo);
-      if constexpr (DT == DT_BF16) {
-        phi[r] = M::bits(hi);
-        plo[r] = M::bits(lo);
-      } else {
-        phi[r] = hi;
-        plo[r] = lo;
+    for (int cc = 0; cc < CH; ++cc) {
+      if (i0 + cc >= mine) break;
+      vec4 phi, plo;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float pz = __builtin_amdgcn_exp2f(z[cc][r] - ms);
+        l_run += pz;
+        E hi, lo;
+        split_hi_lo<DT>(pz * M::kPScale, hi, lo);
+        if constexpr (DT == DT_BF16) {
+          phi[r] = M::bits(hi);
+          plo[r] = M::bits(lo);
+        } else {
+          phi[r] = hi;
+          plo[r] = lo;
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < NDT; ++e) {
+        // channel W*n16 + e of tokens 4*c4 + 0..3: the low (e even) or high
+        // half of dword e/2 of each token
+        const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+        const uint32_t(&w)[4][VW] = c.v[cc];
+        const uint2 frag = {__builtin_amdgcn_perm(w[1][e >> 1], w[0][e >> 1], sel),
+                            __builtin_amdgcn_perm(w[3][e >> 1], w[2][e >> 1], sel)};
+        const vec4 bv = __builtin_bit_cast(vec4, frag);
+        o[e] = M::mma16(phi, bv, o[e]);
+        o[e] = M::mma16(plo, bv, o[e]);
       }
     }
-    __builtin_amdgcn_wave_barrier();
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) {
-      s16x4_t vv;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) vv[j] = (short)s_v[wave][4 * c4 + j][16 * dt + n16];
-      const vec4 bv = __builtin_bit_cast(vec4, vv);
-      o[dt] = M::mma16(phi, bv, o[dt]);
-      o[dt] = M::mma16(plo, bv, o[dt]);
+  };
+  if (mine > 0) {
+    Chunk ca, cb;
+    load(0, ca);
+    for (int i = 0; i < mine; i += 2 * CH) {
+      load(i + CH, cb);
+      compute(i, ca);
+      if (i + CH >= mine) break;
+      load(i + 2 * CH, ca);
+      compute(i + CH, cb);
     }
   }
   l_run += __shfl_xor(l_run, 16);
   l_run += __shfl_xor(l_run, 32);
-  // out fragment: head 4*c4 + r, channel 16*dt + n16
+  // out fragment: head 4*c4 + r, channel W*n16 + e
 #pragma unroll
-  for (int dt = 0; dt < NDT; ++dt)
+  for (int e = 0; e < NDT; ++e)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int g = 4 * c4 + r;
-      if (g < G) s_acc[wave][g][16 * dt + n16] = o[dt][r] * (1.f / M::kPScale);
+      if (g < G) s_acc[wave][g][NDT * n16 + e] = o[e][r] * (1.f / M::kPScale);
     }
   if (lane < G) {
     s_acc[wave][lane][D] = l_run;
     s_mw[wave][lane] = m_run;
   }
+}
+
+// Split decode workgroup for grouped-query heads on 16-bit KV: four waves,
+// splits of TPW steps of 64 tokens.
+template <int DT, int D, int G>
+__global__ __launch_bounds__(256, D == 128 ? 2 : 3) void k_decode_mfma(
+    const float* __restrict__ q, const void* __restrict__ k_pool,
+    const void* __restrict__ v_pool, const int32_t* __restrict__ bt,
+    const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ sel,
+    const int32_t* __restrict__ sel_phys, const int32_t* __restrict__ sel_count,
+    int Hq, int Hkv, int log2P, int MP, int NP, int k_max, int S_max, int TPW,
+    float qscale, float* __restrict__ partials, float* __restrict__ out) {
+  constexpr int NT = 256, NW = NT / kWave, TILE = NW * MfmaDecode<DT, D>::WS;
+  constexpr int MAXE = kMaxTilesPerSplit * TILE / 8;
+  __shared__ int s_lp[MAXE];
+  __shared__ uint32_t s_ph[MAXE];
+  __shared__ float s_acc[NW][G][D + 1];
+  __shared__ float s_mw[NW][G];
+
+  const int unit = blockIdx.x / S_max, split = blockIdx.x - unit * S_max;
+  const int b = unit / Hkv, h = unit - b * Hkv;
+  const long span = (long)TPW * TILE;
+  const long t0 = (long)split * span;
+  const int e0 = (int)(t0 >> log2P);
+  const int ecap = (int)min(max(1L, span >> log2P), (long)(k_max - e0));
+  stage_split_list(sel, sel_phys, bt, unit, b, MP, NP, k_max, e0, ecap, NT, s_lp, s_ph);
+  const int cnt = clampi(sel_count[unit], 0, k_max);
+  const int len = clampi(seq_lens[b], 0, MP << log2P);
+  const long t_all = (long)cnt << log2P;
+  const long t_end = min(t_all, t0 + span);
+  if (t0 >= t_end) {  // whole workgroup: no work
+    if (cnt == 0 && split == 0)
+      for (int i = threadIdx.x; i < G * D; i += NT) out[((size_t)b * Hq + h * G) * D + i] = 0.f;
+    return;
+  }
+  __syncthreads();
+  const TokenList tl{s_lp, s_ph, min(cnt - e0, ecap), e0, len, log2P, Hkv, h, D};
+  mfma_decode_range<DT, D, G, NW, 1>(q + ((size_t)b * Hq + h * G) * D,
+                                  reinterpret_cast<const char*>(k_pool),
+                                  reinterpret_cast<const char*>(v_pool), tl, t0, t_end, qscale,
+                                  s_acc, s_mw);
   __syncthreads();
   finish_split<D, G, NT, NW>(s_acc, s_mw, partials, out, b, h, Hq, S_max, split,
                              (int)((t_all + span - 1) / span));
+}
+
+// ---------------------------------------------------------------------------
+// The whole decode step of one (sequence, KV head) in one workgroup
+// ---------------------------------------------------------------------------
+//
+// [append the new token] -> score every page -> block-wide top-K -> decode
+// the kept pages' tokens with all waves -> combine the waves -> out.  No
+// state crosses workgroups, so the step is one launch with no merge pass; the
+// selection stays in LDS between the phases (it is also written to sel /
+// sel_count for the caller).
+template <int DT, int D, int G>
+constexpr bool step_uses_mfma() { return DT != DT_F32 && (G == 4 || G == 8); }
+
+// Dynamic LDS of k_step: block-table row and keys (MP words each, rounded to
+// 4), then the decode staging area.
+template <int DT, int D, int G, int NT>
+constexpr size_t step_decode_lds() {
+  constexpr int NW = NT / kWave;
+  return (size_t)NW * G * (D + 1) * 4;
+}
+
+// 4-wave workgroups are meant to run two to a CU: at most 256 registers each
+// (fp32 groups of eight heads excepted: their VALU decode needs more)
+template <int DT, int D, int G, int NT>
+constexpr int step_min_blocks() { return NT == 256 && (G <= 4 || DT != DT_F32) ? 2 : 1; }
+
+template <int DT, int D, int G, int NT>
+__global__ __launch_bounds__(NT, (step_min_blocks<DT, D, G, NT>())) void k_step(
+    const float* __restrict__ q, const void* __restrict__ k_new,
+    const void* __restrict__ v_new, void* __restrict__ k_pool, void* __restrict__ v_pool,
+    void* __restrict__ meta, const int32_t* __restrict__ bt,
+    const int32_t* __restrict__ seq_lens, int Hq, int Hkv, int log2P, int MP, int NP,
+    int k_max, const int32_t* __restrict__ k_per_seq, int n_sink, float qscale,
+    int32_t* __restrict__ sel, int32_t* __restrict__ sel_count,
+    float* __restrict__ scores_out, float* __restrict__ out) {
+  constexpr int NW = NT / kWave;
+  constexpr bool MF = step_uses_mfma<DT, D, G>();
+  extern __shared__ __align__(16) uint32_t smem[];
+  const int MPa = (MP + 3) & ~3;
+  uint32_t* s_phys = smem;
+  uint32_t* s_key = smem + MPa;
+  char* dec = reinterpret_cast<char*>(smem + 2 * MPa);
+  __shared__ SelectLds<NT> sl;
+  __shared__ float s_mw[NW][G];
+
+  const int unit = blockIdx.x, b = unit / Hkv, h = unit - b * Hkv;
+  const int tid = threadIdx.x;
+  const int P = 1 << log2P;
+  if (tid == 0) {
+    sl.red[0] = -1;
+    sl.red[1] = 0;
+  }
+  const int32_t* bt_row = bt + (size_t)b * MP;
+  stage_row<4>(bt_row, MP, NT, s_phys, [NP](int32_t e) { return (uint32_t)clampi(e, 0, NP - 1); });
+  const int len = clampi(seq_lens[b], 0, MP * P);
+  const int kb = clampi(k_per_seq ? k_per_seq[b] : k_max, 1, k_max);
+  const int n = (len + P - 1) >> log2P;
+  if (k_new != nullptr && len >= 1 && tid < D) {
+    // the new token is slot (len-1) mod P of page (len-1)/P; its box widens
+    // (or opens, on slot 0) before any box of the row is read
+    const int pos = len - 1, p = pos >> log2P, slot = pos & (P - 1);
+    const size_t phys = (size_t)clampi(bt_row[p], 0, NP - 1);
+    const size_t i = ((size_t)b * Hkv + h) * D + tid;
+    const uint32_t kb = load_elem<DT>(k_new, i), vb = load_elem<DT>(v_new, i);
+    const size_t dst = ((phys * Hkv + h) * P + slot) * D + tid;
+    store_elem<DT>(k_pool, dst, kb);
+    store_elem<DT>(v_pool, dst, vb);
+    const size_t m = ((phys * Hkv + h) * 2) * D + tid;
+    if (slot == 0) {
+      store_elem<DT>(meta, m, kb);
+      store_elem<DT>(meta, m + D, kb);
+    } else {
+      const float k = elem_to_f32<DT>(kb);
+      if (k < elem_to_f32<DT>(load_elem<DT>(meta, m))) store_elem<DT>(meta, m, kb);
+      if (k > elem_to_f32<DT>(load_elem<DT>(meta, m + D))) store_elem<DT>(meta, m + D, kb);
+    }
+  }
+  __syncthreads();  // block-table row staged; the appended token visible to the workgroup
+  score_pages<DT, D, G, NT>(q, meta, s_phys, b, h, Hq, Hkv, n, 0, 1, s_key);
+  __syncthreads();
+  if (scores_out) {
+    float* srow_out = scores_out + (size_t)unit * MP;
+    for (int p = tid; p < n; p += NT) srow_out[p] = key_to_score(s_key[p]);
+  }
+  const int keff = min(kb, n), f = min(n_sink, keff);
+  // the selection stays in LDS; it is written out at the end, so that no
+  // barrier before the decode waits for those stores
+  const int cnt = select_block<NT>(s_key, s_phys, n, keff, f, k_max, nullptr, nullptr, nullptr, sl);
+  int32_t* srow = sel + (size_t)unit * k_max;
+  float* orow = out + ((size_t)b * Hq + h * G) * D;
+  if (cnt == 0) {
+    for (int i = tid; i < G * D; i += NT) orow[i] = 0.f;
+    for (int i = tid; i < k_max; i += NT) srow[i] = -1;
+    if (tid == 0) sel_count[unit] = 0;
+    return;
+  }
+  const TokenList tl{reinterpret_cast<const int*>(s_key), s_phys, cnt, 0, len, log2P, Hkv, h, D};
+  const float* qg0 = q + ((size_t)b * Hq + h * G) * D;
+  const char* kbp = reinterpret_cast<const char*>(k_pool);
+  const char* vbp = reinterpret_cast<const char*>(v_pool);
+  const long t_end = (long)cnt << log2P;
+  typedef float AccRow[G][D + 1];
+  AccRow* s_acc = reinterpret_cast<AccRow*>(dec);
+  if constexpr (MF) {
+    mfma_decode_range<DT, D, G, NW, D == 64 ? 4 : 2>(qg0, kbp, vbp, tl, 0, t_end, qscale,
+                                                     s_acc, s_mw);
+    __syncthreads();
+    finish_split<D, G, NT, NW>(s_acc, s_mw, nullptr, out, b, h, Hq, 1, 0, 1);
+  } else {
+    valu_decode_range<DT, D, G, NT>(qg0, kbp, vbp, tl, 0, t_end, qscale, s_acc, s_mw);
+    __syncthreads();
+    finish_split<D, G, NT, NW>(s_acc, s_mw, nullptr, out, b, h, Hq, 1, 0, 1);
+  }
+  for (int i = tid; i < k_max; i += NT) srow[i] = i < cnt ? (int32_t)s_key[i] : -1;
+  if (tid == 0) sel_count[unit] = cnt;
 }
 
 // ---------------------------------------------------------------------------
@@ -1273,10 +1648,65 @@ hipError_t launch_score_select(const Dims& d, const float* q, const void* meta,
                          ws.sel_phys);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || NS == 1) return e;
-    hipLaunchKernelGGL(k_select, dim3(units), dim3(kWave), 2 * sizeof(uint32_t) * (size_t)d.MP,
+    hipLaunchKernelGGL(k_select, dim3(units), dim3(kSelectThreads),
+                       2 * sizeof(uint32_t) * (size_t)d.MP,
                        s, bt, seq_lens, d.Hkv, d.P, d.MP, d.NP, k_max, k_per_seq, n_sink,
                        ws.keys, sel, sel_count, ws.sel_phys);
     return hipGetLastError();
+  });
+}
+
+// Threads of a k_step workgroup.  Rows that fill the chip twice over get 4
+// waves each, so two rows share a CU and one row's select / combine phases
+// overlap the other's streaming; fewer rows get 8 waves, and single-head
+// groups (whose scoring keeps only two query rows in registers) 16 while the
+// rows alone do not fill the chip.
+int step_threads(const Dims& d) {
+  const long units = (long)d.B * d.Hkv;
+  if (units >= 512) return 256;
+  return d.G == 1 && units <= 256 ? 1024 : 512;
+}
+
+size_t step_lds_bytes(const Dims& d) {
+  const int nt = step_threads(d);
+  size_t dec = 0;
+  (void)by_dt_d_g(d, [&](auto DT, auto HD, auto GG) -> hipError_t {
+    constexpr int dt = decltype(DT)::value, hd = decltype(HD)::value,
+                  g = decltype(GG)::value;
+    dec = nt == 256 ? step_decode_lds<dt, hd, g, 256>() : step_decode_lds<dt, hd, g, 512>();
+    if constexpr (g == 1)
+      if (nt == 1024) dec = step_decode_lds<dt, hd, g, 1024>();
+    return hipSuccess;
+  });
+  return (size_t)2 * ((d.MP + 3) & ~3) * sizeof(uint32_t) + dec;
+}
+
+bool step_fits(const Dims& d) { return step_lds_bytes(d) <= kStepMaxLds; }
+
+hipError_t launch_step(const Dims& d, const float* q, const void* k_new, const void* v_new,
+                       void* k_pool, void* v_pool, void* meta, const int32_t* bt,
+                       const int32_t* seq_lens, int k_max, const int32_t* k_per_seq,
+                       int n_sink, float scale, int32_t* sel, int32_t* sel_count,
+                       float* scores_out, float* out, hipStream_t s) {
+  const int nt = step_threads(d);
+  const size_t lds = step_lds_bytes(d);
+  if (lds > kStepMaxLds) return hipErrorInvalidValue;
+  const int log2P = ilog2(d.P);
+  const float qscale = scale * 1.44269504088896340736f;  // fold log2(e)
+  const dim3 grid(d.B * d.Hkv);
+  return by_dt_d_g(d, [&](auto DT, auto HD, auto GG) -> hipError_t {
+    constexpr int dt = decltype(DT)::value, hd = decltype(HD)::value,
+                  g = decltype(GG)::value;
+    auto go = [&](auto NTc) -> hipError_t {
+      constexpr int nthr = decltype(NTc)::value;
+      hipLaunchKernelGGL((k_step<dt, hd, g, nthr>), grid, dim3(nthr), lds, s, q, k_new, v_new,
+                         k_pool, v_pool, meta, bt, seq_lens, d.Hq, d.Hkv, log2P, d.MP, d.NP,
+                         k_max, k_per_seq, n_sink, qscale, sel, sel_count, scores_out, out);
+      return hipGetLastError();
+    };
+    if constexpr (g == 1)
+      if (nt == 1024) return go(IC<1024>{});
+    return nt == 256 ? go(IC<256>{}) : go(IC<512>{});
   });
 }
 

@@ -16,7 +16,11 @@ HEADER = os.path.join(ROOT, "include", "tsv.h")
 
 @pytest.fixture(scope="module")
 def tsv():
-    from query_aware_sparse_bbox_amd import build as b
+    import importlib.util
+    path = os.path.join(ROOT, "query_aware_sparse_bbox_amd", "build.py")
+    spec = importlib.util.spec_from_file_location("tsv_build", path)
+    b = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(b)
     if not os.path.exists(b.LIB):
         b.build()
     import query_aware_sparse_bbox_amd as m
@@ -78,6 +82,19 @@ def test_sizes(tsv):
     assert tsv.tsv_workspace_bytes(s, 0) == 0
     assert tsv.tsv_meta_bytes(shape(head_dim=96)) == 0
     assert tsv.tsv_meta_bytes(shape(num_q_heads=7)) == 0
+
+
+def test_decode_step_launch_plan(tsv):
+    # short block-table rows: the whole step of a row fits one workgroup
+    assert tsv.tsv_decode_step_launches(shape(), 8, True) == 1
+    assert tsv.tsv_decode_step_launches(shape(), 8, False) == 1
+    # 8 query heads of 128 channels need more staging than one workgroup's
+    # 64 KiB; 4096-entry rows with such staging too: the phases run apart
+    big = shape(head_dim=128, num_q_heads=16, num_kv_heads=2, max_pages_per_seq=4096)
+    assert tsv.tsv_decode_step_launches(big, 64, True) in (3, 4)
+    assert tsv.tsv_decode_step_launches(big, 64, False) in (2, 3)
+    assert tsv.tsv_decode_step_launches(shape(head_dim=96), 8, True) == 0
+    assert tsv.tsv_decode_step_launches(shape(), 0, True) == 0
 
 
 @pytest.mark.parametrize("kw,status", [

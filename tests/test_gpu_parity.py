@@ -78,11 +78,100 @@ def test_all_pages_is_dense_attention():
 
 
 def test_three_calls_equal_fused_step():
-    wl = W.make("ragged", batch=8, lens_range=(100, 4000))
-    a = gpu_run(wl)
-    b = gpu_run(wl, separate=True)
-    for k in ("sel", "cnt", "out", "meta", "k_pool", "v_pool"):
-        assert np.array_equal(a[k], b[k]), k
+    """tsv_meta_append + tsv_select_pages + tsv_sparse_decode give the same
+    selection, boxes and pools as tsv_decode_step; both outputs are within
+    tolerance of the oracle (their summation orders differ)."""
+    import query_aware_sparse_bbox_amd as T
+
+    for name, kw in [("ragged", dict(batch=8, lens_range=(100, 4000))),
+                     ("tinyllama", dict(batch=4, context=2000)),
+                     ("llama_long", dict(batch=2, context=6000))]:
+        wl = W.make(name, **kw)
+        say(f"[case] three calls vs one step: {name} {kw} launches="
+            f"{T.tsv_decode_step_launches(wl.shape, wl.k_max, bool(wl.steps))}")
+        o = oracle_run(wl)
+        a = gpu_run(wl)
+        b = gpu_run(wl, separate=True)
+        for k in ("sel", "cnt", "meta", "k_pool", "v_pool", "scores"):
+            assert np.array_equal(a[k].view(np.uint8), b[k].view(np.uint8)), k
+        compare(wl, a, o)
+        compare(wl, b, o)
+
+
+def test_one_launch_and_phased_paths_both_covered():
+    """The five configurations take the one-launch step; 4096-entry block
+    table rows with a group of eight 128-channel heads take the phased path
+    (row staging plus the group's combine area exceed 64 KiB)."""
+    import query_aware_sparse_bbox_amd as T
+
+    for name in W.CONFIG_ORDER:
+        wl = W.make(name)
+        assert T.tsv_decode_step_launches(wl.shape, wl.k_max, bool(wl.steps)) == 1, name
+    wl = W.make("ragged", batch=2, lens_range=(65500, 65535), kv_dtype=W.BF16, num_q_heads=64)
+    assert wl.shape.max_pages_per_seq >= 4064
+    assert T.tsv_decode_step_launches(wl.shape, wl.k_max, True) == 4
+    _case(wl)
+
+
+def test_longest_block_table_row():
+    """4096 pages per row: the largest row the library accepts, every thread
+    of the selection owning several pages."""
+    wl = W.make("llama_long", batch=1, num_q_heads=4, num_kv_heads=4, context=131072)
+    assert wl.shape.max_pages_per_seq == 4096
+    _case(wl)
+    wl = W.make("llama_long", batch=1, num_q_heads=2, num_kv_heads=2, context=131072 - 77,
+                budget=("fixed", 200))
+    _case(wl)
+
+
+def test_graph_replay_matches_eager():
+    """The step captured in a HIP graph and replayed several times, with eager
+    work and synchronisations between replays, equals the eager step."""
+    import torch
+
+    import query_aware_sparse_bbox_amd as T
+    from workloads import device as WD
+
+    wl = W.make("ragged", batch=8, lens_range=(100, 3000))
+    sh = wl.shape
+    st = wl.steps[0]
+    d = WD.upload(wl)
+    T.tsv_meta_build(sh, d.k_pool, d.meta, d.block_table, WD.i32(st.seq_lens - 1))
+    B, Hq, Hkv, D = sh.batch, sh.num_q_heads, sh.num_kv_heads, sh.head_dim
+    args = dict(q=torch.from_numpy(st.q).cuda(), k_new=WD.kv_tensor(st.k_new, sh.kv_dtype),
+                v_new=WD.kv_tensor(st.v_new, sh.kv_dtype), lens=WD.i32(st.seq_lens),
+                kps=WD.i32(st.k_per_seq))
+    sel = torch.empty((B, Hkv, wl.k_max), dtype=torch.int32, device="cuda")
+    cnt = torch.empty((B, Hkv), dtype=torch.int32, device="cuda")
+    out = torch.empty((B, Hq, D), dtype=torch.float32, device="cuda")
+    ws = T.new_workspace(sh, wl.k_max)
+
+    def step():
+        T.tsv_decode_step(sh, args["q"], args["k_new"], args["v_new"], d.k_pool, d.v_pool,
+                          d.meta, d.block_table, args["lens"], wl.k_max, args["kps"], 0,
+                          wl.scale, sel, cnt, None, out, ws)
+
+    step()
+    torch.cuda.synchronize()
+    ref = (sel.clone(), cnt.clone(), out.clone())
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for i in range(4):
+        sel.fill_(-5)
+        out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        say(f"  replay {i}")
+        assert torch.equal(sel, ref[0]) and torch.equal(cnt, ref[1])
+        assert torch.equal(out.view(torch.int32), ref[2].view(torch.int32))
 
 
 def test_bitwise_deterministic():
