@@ -109,11 +109,13 @@ size_t tsv_meta_bytes(const tsv_shape* shape);
 size_t tsv_workspace_bytes(const tsv_shape* shape, int32_t k_max);
 
 /* Kernel launches one tsv_decode_step makes for `shape` (with_append != 0:
-   with k_new / v_new): 1 when the whole step of a (sequence, KV head) runs
-   in one workgroup, which needs the block-table row and the decode staging
-   to fit 64 KiB of local memory; otherwise 3 or 4 (append, score and
-   select, split decode, merge).  0 when the shape is invalid or
-   unsupported.  Informational: results do not depend on it. */
+   with k_new / v_new).  1 or 2 when the whole step of a (sequence, KV head)
+   runs in workgroups of its own, which needs the block-table row and the
+   decode staging to fit 64 KiB of local memory: 1 when each row has one
+   workgroup, 2 when B*Hkv is small enough that each row is spread over
+   several workgroups and a merge pass follows.  Otherwise 3 or 4 (append,
+   score and select, split decode, merge).  0 when the shape is invalid or
+   unsupported.  Informational only. */
 int tsv_decode_step_launches(const tsv_shape* shape, int32_t k_max, int32_t with_append);
 
 /* Rebuild the bounding box of every page p < n_b of every sequence from the
@@ -174,11 +176,11 @@ int tsv_sparse_decode(const tsv_shape* shape, const float* q,
    in one pass over the cache).  Arguments and results as in the three calls
    above: sel, sel_count and scores_out are identical to tsv_select_pages';
    out agrees with tsv_sparse_decode within the rounding of a different
-   summation order.  Where tsv_decode_step_launches() is 1 the step is one
-   kernel with one workgroup per (sequence, KV head), which appends, scores,
-   selects and attends without touching the workspace (it is still
-   required).  As for tsv_meta_append, the page receiving the new token must
-   belong to one sequence only. */
+   summation order.  Where tsv_decode_step_launches() is 1 or 2, each
+   (sequence, KV head) is handled by workgroups of its own that append,
+   score, select and attend in one kernel (plus a merge of the split partial
+   states when 2).  As for tsv_meta_append, the page receiving the new token
+   must belong to one sequence only. */
 int tsv_decode_step(const tsv_shape* shape, const float* q, const void* k_new,
                     const void* v_new, void* k_pool, void* v_pool, void* meta,
                     const int32_t* block_table, const int32_t* seq_lens,

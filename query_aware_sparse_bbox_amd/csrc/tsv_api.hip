@@ -112,7 +112,7 @@ size_t tsv_workspace_bytes(const tsv_shape* shape, int32_t k_max) {
 int tsv_decode_step_launches(const tsv_shape* shape, int32_t k_max, int32_t with_append) {
   Dims d;
   if (check_shape(shape, &d) != TSV_OK || k_max < 1) return 0;
-  if (tsv::step_fits(d)) return 1;
+  if (tsv::step_fits(d)) return tsv::step_splits(d, k_max) > 1 ? 2 : 1;
   return (with_append ? 1 : 0) + 1 + 1 + (tsv::decode_splits(d, k_max) > 1 ? 1 : 0);
 }
 
@@ -196,12 +196,12 @@ int tsv_decode_step(const tsv_shape* shape, const float* q, const void* k_new,
                          sel_count, k_max, out, workspace, workspace_bytes);
   if (rc) return rc;
   hipStream_t s = (hipStream_t)stream;
-  if (tsv::step_fits(d))  // one launch: every row's whole step in one workgroup
-    return hip_status(tsv::launch_step(d, q, k_new, v_new, k_pool, v_pool, meta,
-                                       block_table, seq_lens, k_max, k_per_seq, n_sink,
-                                       scale, sel, sel_count, scores_out, out, s));
   tsv::Workspace ws;
   tsv::workspace_layout(d, k_max, workspace, &ws);
+  if (tsv::step_fits(d))  // every row's whole step in its own workgroup(s)
+    return hip_status(tsv::launch_step(d, q, k_new, v_new, k_pool, v_pool, meta,
+                                       block_table, seq_lens, k_max, k_per_seq, n_sink,
+                                       scale, sel, sel_count, scores_out, ws, out, s));
   if (k_new) {
     rc = hip_status(tsv::launch_meta_append(d, k_new, v_new, k_pool, v_pool, meta,
                                             block_table, seq_lens, s));

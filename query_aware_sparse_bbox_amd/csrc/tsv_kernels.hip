@@ -681,6 +681,16 @@ __global__ __launch_bounds__(kSelectThreads) void k_select(
 // with one tile writes `out` directly; a unit with nothing selected gets zero
 // rows from its first tile slot.
 
+// Token span of one split when a row's t_all selected tokens are spread over
+// at most S workgroups of at least `minspan` tokens each (a multiple of 16,
+// so every split starts on a 16-token step).  Depends on the row's data only,
+// never on the launch width.
+__device__ __forceinline__ long step_span(long t_all, int S, int minspan) {
+  const long se = min((long)S, max(1L, t_all / minspan));
+  const long per = (t_all + se - 1) / se;
+  return max(16L, (per + 15) & ~15L);
+}
+
 // K3: merge of the tiles' partial states of one (sequence, query head) per
 // wave, for units with more than one tile.  Lane s holds tile s's (max,
 // denominator); the weighted sums are read with all of a lane's loads in
@@ -688,7 +698,7 @@ __global__ __launch_bounds__(kSelectThreads) void k_select(
 template <int D>
 __global__ __launch_bounds__(256) void k_merge(
     const float* __restrict__ partials, const int32_t* __restrict__ sel_count, int B,
-    int Hq, int Hkv, int G, int log2P, int k_max, int S_max, int tile,
+    int Hq, int Hkv, int G, int log2P, int k_max, int S_max, int tile, int minspan,
     float* __restrict__ out) {
   constexpr int PER = D / kWave, UNR = 8;
   const int gw = blockIdx.x * 4 + threadIdx.x / kWave;
@@ -696,7 +706,10 @@ __global__ __launch_bounds__(256) void k_merge(
   if (gw >= B * Hq) return;
   const int b = gw / Hq, hq = gw - b * Hq, h = hq / G;
   const int cnt = clampi(sel_count[(size_t)b * Hkv + h], 0, k_max);
-  const int ns = (int)((((long)cnt << log2P) + tile - 1) / tile);
+  // splits of `tile` tokens, or (tile == 0) of step_span(t_all, S_max, minspan)
+  const long t_all = (long)cnt << log2P;
+  const long span = tile > 0 ? tile : step_span(t_all, S_max, minspan);
+  const int ns = (int)((t_all + span - 1) / span);
   if (ns <= 1) return;  // finished by the decode tile itself
   const float* base = partials + (size_t)gw * S_max * (D + 2);
   // global max and denominator, 64 tiles per pass
@@ -838,46 +851,50 @@ struct TokenList {
   }
 };
 
-// The 16 stream tokens [tw, tw + 16) of one MFMA wave step (tw a multiple of
-// 16) lie in one list entry when P >= 16 and in two consecutive entries when
-// P == 8.  All fields are wave-uniform: token t of the step is at pool
-// offset base0 + t*D (t < split, valid if t < lim0) or base1 + (t-split)*D
-// (valid if t - split < lim1).
-struct StepMap {
-  long base0, base1;
-  int split, lim0, lim1, D;
-  __device__ __forceinline__ long off(int t) const {
-    const bool first = t < split;
-    const int tt = first ? t : t - split;
-    const bool ok = tt < (first ? lim0 : lim1);
-    return ok ? (first ? base0 : base1) + (long)tt * D : -1;
-  }
-};
-
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
-// Map of the step starting at stream token tw.
-__device__ __forceinline__ StepMap step_map(const TokenList& tl, long tw) {
+__device__ __forceinline__ long uniform64(long x) {
+  const int lo = __builtin_amdgcn_readfirstlane((int)(x & 0xffffffffL));
+  const int hi = __builtin_amdgcn_readfirstlane((int)(x >> 32));
+  return ((long)hi << 32) | (unsigned)lo;
+}
+
+// The 16 stream tokens [tw, tw + 16) of one MFMA wave step (tw a multiple of
+// 16, 16-bit KV) lie in one list entry when P >= 16 and in two consecutive
+// entries when P == 8.  Wave-uniform: token t < split sits at k0/v0 + t*D
+// elements and exists if t < lim0; token t >= split at k1/v1 + (t-split)*D,
+// existing if t - split < lim1.  Slots that do not exist are still inside
+// their page (or in a listed page), so reading them is in bounds.
+struct StepMap {
+  const char *k0, *k1, *v0, *v1;
+  int split, lim0, lim1;
+};
+
+__device__ __forceinline__ StepMap step_map(const TokenList& tl, const char* kb, const char* vb,
+                                            long tw) {
   const int P = 1 << tl.log2P;
-  const int e = (int)(tw >> tl.log2P) - tl.e0;
-  const int st0 = (int)(tw & (P - 1));
+  const int e = uniform((int)(tw >> tl.log2P) - tl.e0);
+  const int st0 = uniform((int)(tw & (P - 1)));
   StepMap m;
   m.split = min(16, P - st0);
-  m.D = tl.D;
-  m.lim0 = 0;
-  m.lim1 = 0;
-  m.base0 = m.base1 = 0;
-  const int ec = uniform(clampi(e, 0, tl.npg - 1));
+  const int ec = clampi(e, 0, tl.npg - 1);
   const int l0 = uniform(tl.lp[ec]);
   const int p0 = uniform((int)tl.ph[ec]);
-  if (e < tl.npg && l0 >= 0) m.lim0 = clampi(tl.len - (l0 * P + st0), 0, m.split);
-  m.base0 = (long)((((size_t)p0 * tl.Hkv + tl.h) * P + st0) * tl.D);
+  m.lim0 = uniform(e < tl.npg && l0 >= 0 ? clampi(tl.len - (l0 * P + st0), 0, m.split) : 0);
+  const size_t b0 = ((((size_t)p0 * tl.Hkv + tl.h) << tl.log2P) + st0) * tl.D * 2;
+  m.k0 = kb + b0;
+  m.v0 = vb + b0;
+  m.lim1 = 0;
+  m.k1 = m.k0;
+  m.v1 = m.v0;
   if (m.split < 16) {
-    const int ec1 = uniform(clampi(e + 1, 0, tl.npg - 1));
+    const int ec1 = clampi(e + 1, 0, tl.npg - 1);
     const int l1 = uniform(tl.lp[ec1]);
     const int p1 = uniform((int)tl.ph[ec1]);
-    if (e + 1 < tl.npg && l1 >= 0) m.lim1 = clampi(tl.len - l1 * P, 0, 16 - m.split);
-    m.base1 = (long)((((size_t)p1 * tl.Hkv + tl.h) * P) * tl.D);
+    m.lim1 = uniform(e + 1 < tl.npg && l1 >= 0 ? clampi(tl.len - l1 * P, 0, 16 - m.split) : 0);
+    const size_t b1 = (((size_t)p1 * tl.Hkv + tl.h) << tl.log2P) * tl.D * 2;
+    m.k1 = kb + b1;
+    m.v1 = vb + b1;
   }
   return m;
 }
@@ -925,8 +942,9 @@ __device__ __forceinline__ void valu_decode_range(const float* __restrict__ qg0,
   auto load_tile = [&](int it, uint4 (&kr)[J], uint4 (&vr)[J], bool (&ok)[J]) {
 #pragma unroll
     for (int j = 0; j < J; ++j) {
-      const long o = tl.off(t0 + (long)it * TILE + j * TPI + wave * SPW + slot);
-      ok[j] = o >= 0;
+      const long ts = t0 + (long)it * TILE + j * TPI + wave * SPW + slot;
+      const long o = tl.off(ts);
+      ok[j] = o >= 0 && ts < t_end;  // the list may go on past this range
       const long off = ok[j] ? o + chunk * C : safe_off;
       kr[j] = ld16(kb + off * EB);
       vr[j] = ld16(vb + off * EB);
@@ -1079,15 +1097,22 @@ __global__ __launch_bounds__(NT) void k_decode_split(
 // MFMA, 16 tokens per wave step
 // ---------------------------------------------------------------------------
 //
-//   logits^T[token][g] = K[token][:] . q[g][:]   (v_mfma_f32_16x16x32)
+// Both fp32 operands that meet a 16-bit KV operand (q, and the
+// probabilities p) are split into hi + lo 16-bit parts, so the products keep
+// ~16 more mantissa bits than one 16-bit operand would.  A group has G <= 8
+// heads, so the two parts share one MFMA: hi in fragment rows/columns
+// 0 .. G-1, lo in 8 .. 8+G-1.
+//   logits^T[token][c] = K[token][:] . Q[c][:]   (v_mfma_f32_16x16x32)
 //     A = K rows straight from the pool (lane: token n16, 8 channels at
-//     32*ch + 8*c4), B = q^T; q is split into hi + lo 16-bit parts so the
-//     product keeps ~16 more mantissa bits than one 16-bit operand would.
-//     Lane (n16, c4) ends with the logits of head g = n16 for tokens
-//     4*c4 + r.
-//   out[g][d] += sum_token p[g][token] * V[token][d]   (v_mfma_f32_16x16x16)
-//     A = p (hi + lo parts): the lane's 4 probabilities are exactly its A
-//     fragment.  B needs 4 consecutive tokens of one channel per lane: lane
+//     32*ch + 8*c4), B = Q^T with column c = q_hi of head c (c < 8) or q_lo
+//     of head c - 8.  Lane (n16, c4) ends with the partial logits of column
+//     n16 for tokens 4*c4 + r; one DPP row rotation by 8 adds the partner
+//     column, so lanes n16 and n16 ^ 8 both hold the logits of head n16 & 7.
+//   out[c][d] += sum_token P[c][token] * V[token][d]   (v_mfma_f32_16x16x16)
+//     A = P with row c = p_hi of head c (c < 8) or p_lo of head c - 8: the
+//     lane's 4 probabilities, split, are exactly its A fragment.  Rows c and
+//     c + 8 are added once, at the end.  B needs 4 consecutive tokens of one
+//     channel per lane: lane
 //     (n16, c4) loads the W = D/16 channels W*n16 .. W*n16 + W-1 of tokens
 //     4*c4 .. 4*c4 + 3 (four 8- or 16-byte loads, whole rows per wave load)
 //     and v_perm packs channel W*n16 + e of the four tokens into the B
@@ -1154,8 +1179,9 @@ struct MfmaDecode {
 // 16-token steps are dealt round-robin to the waves; a wave takes its steps
 // CH at a time (a chunk): the chunk's K and V loads are all issued together,
 // one chunk ahead of the arithmetic, and the running softmax state is
-// rescaled once per chunk.  Ends with each wave's state in s_acc[wave] /
-// s_mw[wave] (no barrier).
+// rescaled once per chunk.  Page lookups are wave-uniform (scalar), each
+// lane keeps one K and one V address per step.  Ends with each wave's state
+// in s_acc[wave] / s_mw[wave] (no barrier).
 template <int DT, int D, int G, int NW, int CH>
 __device__ __forceinline__ void mfma_decode_range(const float* __restrict__ qg0,
                                                   const char* __restrict__ kb,
@@ -1169,14 +1195,18 @@ __device__ __forceinline__ void mfma_decode_range(const float* __restrict__ qg0,
   using vec4 = typename M::vec4;
   using E = typename M::elem;
   constexpr int WS = MD::WS, NCH = MD::NCH, NDT = MD::NDT;
-  static_assert(G <= 16, "one 16-row fragment holds the query group");
-  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  constexpr int VW = D / 32;  // dwords of V per token and lane (W = 2*VW channels)
+  static_assert(G <= 8, "hi and lo parts of the group share one 16-row fragment");
+  const int lane = threadIdx.x & (kWave - 1), wave = uniform(threadIdx.x / kWave);
   const int n16 = lane & 15, c4 = lane >> 4;
-  // B operand of the logits: column g = n16, 8 channels per chunk
-  vec8 qhi[NCH], qlo[NCH];
+  const int head = n16 & 7;           // head of fragment row / column n16
+  const bool has = head < G, lo_part = n16 >= 8;
+  t0 = uniform64(t0);
+  t_end = uniform64(t_end);
+  // B operand of the logits: column n16, 8 channels per chunk
+  vec8 qf[NCH];
   {
-    const bool has = n16 < G;
-    const float* qg = qg0 + (size_t)(has ? n16 : 0) * D + 8 * c4;
+    const float* qg = qg0 + (size_t)(has ? head : 0) * D + 8 * c4;
 #pragma unroll
     for (int ch = 0; ch < NCH; ++ch) {
       const float4 a = *reinterpret_cast<const float4*>(qg + 32 * ch);
@@ -1186,40 +1216,43 @@ __device__ __forceinline__ void mfma_decode_range(const float* __restrict__ qg0,
       for (int j = 0; j < 8; ++j) {
         E hi, lo;
         split_hi_lo<DT>(has ? xs[j] : 0.f, hi, lo);
-        qhi[ch][j] = hi;
-        qlo[ch][j] = lo;
+        qf[ch][j] = lo_part ? lo : hi;
       }
     }
   }
-  const long nsteps = (t_end - t0 + WS - 1) / WS;
-  const int mine = nsteps > wave ? (int)((nsteps - wave + NW - 1) / NW) : 0;
-  const long safe_off = tl.safe();
-  constexpr int VW = D / 32;  // dwords of V per token and lane (W = 2*VW channels)
+  const int nsteps = uniform((int)((t_end - t0 + WS - 1) / WS));
+  const int mine = nsteps > wave ? (nsteps - wave + NW - 1) / NW : 0;
+  // per-lane byte offsets: K row n16 (8 channels at 8*c4), V rows 4*c4 .. +3
+  // (W channels at W*n16)
+  const int k_lane = (n16 * D + 8 * c4) * 2;
+  const int v_lane = 2 * VW * n16 * 2;
   struct Chunk {
     uint4 k[CH][NCH];          // token n16, channels 32*ch + 8*c4 .. + 7
     uint32_t v[CH][4][VW];     // token 4*c4 + j, channels W*n16 .. W*n16 + W-1
+    int vlim[CH];              // tokens 4*c4 + j with j < vlim exist
   };
-  auto tw_of = [&](int i) { return t0 + (long)(wave + (long)i * NW) * WS; };
   // the chunk of the wave's steps i0 .. i0+CH-1 (clamped to its last step,
-  // so the loads need no branch; masked tokens read a token that exists)
+  // so the loads need no branch)
   auto load = [&](int i0, Chunk& c) {
 #pragma unroll
     for (int cc = 0; cc < CH; ++cc) {
-      const StepMap sm = step_map(tl, tw_of(min(i0 + cc, mine - 1)));
-      const long ko = sm.off(n16);
+      const int i = min(i0 + cc, mine - 1);
+      const StepMap sm = step_map(tl, kb, vb, t0 + (long)(wave + i * NW) * WS);
+      const char* kp = n16 < sm.split ? sm.k0 + k_lane : sm.k1 + (k_lane - sm.split * D * 2);
 #pragma unroll
-      for (int ch = 0; ch < NCH; ++ch)
-        c.k[cc][ch] = ld16(kb + ((ko >= 0 ? ko : safe_off) + 32 * ch + 8 * c4) * 2);
+      for (int ch = 0; ch < NCH; ++ch) c.k[cc][ch] = ld16(kp + 64 * ch);
+      const bool first = 4 * c4 < sm.split;
+      const char* vp = (first ? sm.v0 : sm.v1 - sm.split * D * 2) + 4 * c4 * D * 2 + v_lane;
+      c.vlim[cc] = i0 + cc < mine ? (first ? sm.lim0 - 4 * c4 : sm.lim1 - (4 * c4 - sm.split))
+                                  : 0;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const long vo = sm.off(4 * c4 + j);
-        const char* vp = vb + ((vo >= 0 ? vo : safe_off) + 2 * VW * n16) * 2;
         if constexpr (VW == 2) {
-          const uint2 x = *reinterpret_cast<const uint2*>(vp);
+          const uint2 x = *reinterpret_cast<const uint2*>(vp + j * D * 2);
           c.v[cc][j][0] = x.x;
           c.v[cc][j][1] = x.y;
         } else {
-          const uint4 x = ld16(vp);
+          const uint4 x = ld16(vp + j * D * 2);
           c.v[cc][j][0] = x.x;
           c.v[cc][j][1] = x.y;
           c.v[cc][j][2] = x.z;
@@ -1228,12 +1261,12 @@ __device__ __forceinline__ void mfma_decode_range(const float* __restrict__ qg0,
       }
     }
   };
-  float m_run = -INFINITY, l_run = 0.f;  // head g = n16
+  float m_run = -INFINITY, l_run = 0.f;  // head n16 & 7
   f32x4_t o[NDT];
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt) o[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   auto compute = [&](int i0, const Chunk& c) {
-    // logits of head n16 for tokens 4*c4 + r of each step, log2 units;
+    // logits of head n16 & 7 for tokens 4*c4 + r of each step, log2 units;
     // tokens that do not exist (or steps past the wave's last) get -inf
     float z[CH][4];
 #pragma unroll
@@ -1243,15 +1276,14 @@ __device__ __forceinline__ void mfma_decode_range(const float* __restrict__ qg0,
       if (i0 + cc >= mine) continue;  // padding of the wave's last chunk
       f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ch = 0; ch < NCH; ++ch) {
-        const vec8 a = __builtin_bit_cast(vec8, c.k[cc][ch]);
-        acc = M::mma32(a, qhi[ch], acc);
-        acc = M::mma32(a, qlo[ch], acc);
-      }
-      const StepMap sm = step_map(tl, tw_of(i0 + cc));
+      for (int ch = 0; ch < NCH; ++ch)
+        acc = M::mma32(__builtin_bit_cast(vec8, c.k[cc][ch]), qf[ch], acc);
+      const int lim = has ? c.vlim[cc] : 0;
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        if (sm.off(4 * c4 + r) >= 0) z[cc][r] = acc[r] * qscale;
+      for (int r = 0; r < 4; ++r) {
+        const float zr = acc[r] + dpp<kRowRor8>(acc[r]);  // hi + lo columns
+        z[cc][r] = r < lim ? zr * qscale : -INFINITY;
+      }
     }
     float tm = -INFINITY;
 #pragma unroll
@@ -1264,48 +1296,47 @@ __device__ __forceinline__ void mfma_decode_range(const float* __restrict__ qg0,
     const float ms = mn == -INFINITY ? 0.f : mn;
     m_run = mn;
     l_run *= alpha;
-    // output rows are heads 4*c4 + r: their factors sit in lanes 4*c4 + r
+    // output row 4*c4 + r belongs to head (4*c4 + r) & 7, whose factor sits
+    // in lane (4*c4 + r) & 7
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      float ag[4];
-#pragma unroll
-      for (int cg = 0; cg < 4; ++cg)
-        ag[cg] = 4 * cg + r < G
-                     ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), 4 * cg + r))
-                     : 1.f;
-      const float ar = c4 == 0 ? ag[0] : c4 == 1 ? ag[1] : c4 == 2 ? ag[2] : ag[3];
+      const float a0 = r < G ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), r))
+                             : 1.f;
+      const float a1 = 4 + r < G
+                           ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), 4 + r))
+                           : 1.f;
+      const float ar = (c4 & 1) ? a1 : a0;
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) o[dt][r] *= ar;
     }
 #pragma unroll
     for (int cc = 0; cc < CH; ++cc) {
       if (i0 + cc >= mine) break;
-      vec4 phi, plo;
+      vec4 pa;  // row n16: p_hi (n16 < 8) or p_lo (n16 >= 8) of head n16 & 7
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const float pz = __builtin_amdgcn_exp2f(z[cc][r] - ms);
         l_run += pz;
         E hi, lo;
         split_hi_lo<DT>(pz * M::kPScale, hi, lo);
-        if constexpr (DT == DT_BF16) {
-          phi[r] = M::bits(hi);
-          plo[r] = M::bits(lo);
-        } else {
-          phi[r] = hi;
-          plo[r] = lo;
-        }
+        if constexpr (DT == DT_BF16) pa[r] = M::bits(lo_part ? lo : hi);
+        else pa[r] = lo_part ? lo : hi;
       }
+      // V of tokens that do not exist is zeroed (their slots may hold
+      // anything; p = 0 alone would not silence a NaN)
+      uint32_t w[4][VW];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int x = 0; x < VW; ++x) w[j][x] = j < c.vlim[cc] ? c.v[cc][j][x] : 0u;
 #pragma unroll
       for (int e = 0; e < NDT; ++e) {
         // channel W*n16 + e of tokens 4*c4 + 0..3: the low (e even) or high
         // half of dword e/2 of each token
         const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-        const uint32_t(&w)[4][VW] = c.v[cc];
         const uint2 frag = {__builtin_amdgcn_perm(w[1][e >> 1], w[0][e >> 1], sel),
                             __builtin_amdgcn_perm(w[3][e >> 1], w[2][e >> 1], sel)};
-        const vec4 bv = __builtin_bit_cast(vec4, frag);
-        o[e] = M::mma16(phi, bv, o[e]);
-        o[e] = M::mma16(plo, bv, o[e]);
+        o[e] = M::mma16(pa, __builtin_bit_cast(vec4, frag), o[e]);
       }
     }
   };
@@ -1322,13 +1353,15 @@ __device__ __forceinline__ void mfma_decode_range(const float* __restrict__ qg0,
   }
   l_run += __shfl_xor(l_run, 16);
   l_run += __shfl_xor(l_run, 32);
-  // out fragment: head 4*c4 + r, channel W*n16 + e
+  // out fragment: row 4*c4 + r, channel W*n16 + e; rows g (c4 < 2) and
+  // g + 8 (c4 + 2) hold the hi and lo parts of head g
 #pragma unroll
   for (int e = 0; e < NDT; ++e)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
+      const float sum = o[e][r] + __shfl_xor(o[e][r], 32);
       const int g = 4 * c4 + r;
-      if (g < G) s_acc[wave][g][NDT * n16 + e] = o[e][r] * (1.f / M::kPScale);
+      if (g < G) s_acc[wave][g][NDT * n16 + e] = sum * (1.f / M::kPScale);
     }
   if (lane < G) {
     s_acc[wave][lane][D] = l_run;
@@ -1389,6 +1422,9 @@ __global__ __launch_bounds__(256, D == 128 ? 2 : 3) void k_decode_mfma(
 // state crosses workgroups, so the step is one launch with no merge pass; the
 // selection stays in LDS between the phases (it is also written to sel /
 // sel_count for the caller).
+// A split of a row covers at least this many 16-token steps per wave.
+constexpr int kStepMinSpanSteps = 2;
+
 template <int DT, int D, int G>
 constexpr bool step_uses_mfma() { return DT != DT_F32 && (G == 4 || G == 8); }
 
@@ -1410,10 +1446,10 @@ __global__ __launch_bounds__(NT, (step_min_blocks<DT, D, G, NT>())) void k_step(
     const float* __restrict__ q, const void* __restrict__ k_new,
     const void* __restrict__ v_new, void* __restrict__ k_pool, void* __restrict__ v_pool,
     void* __restrict__ meta, const int32_t* __restrict__ bt,
-    const int32_t* __restrict__ seq_lens, int Hq, int Hkv, int log2P, int MP, int NP,
-    int k_max, const int32_t* __restrict__ k_per_seq, int n_sink, float qscale,
-    int32_t* __restrict__ sel, int32_t* __restrict__ sel_count,
-    float* __restrict__ scores_out, float* __restrict__ out) {
+    const int32_t* __restrict__ seq_lens, int units, int Hq, int Hkv, int log2P, int MP,
+    int NP, int k_max, const int32_t* __restrict__ k_per_seq, int n_sink, float qscale,
+    int S, int32_t* __restrict__ sel, int32_t* __restrict__ sel_count,
+    float* __restrict__ scores_out, float* __restrict__ partials, float* __restrict__ out) {
   constexpr int NW = NT / kWave;
   constexpr bool MF = step_uses_mfma<DT, D, G>();
   extern __shared__ __align__(16) uint32_t smem[];
@@ -1424,7 +1460,12 @@ __global__ __launch_bounds__(NT, (step_min_blocks<DT, D, G, NT>())) void k_step(
   __shared__ SelectLds<NT> sl;
   __shared__ float s_mw[NW][G];
 
-  const int unit = blockIdx.x, b = unit / Hkv, h = unit - b * Hkv;
+  // workgroup -> (row, split): the S splits of a row share blockIdx mod 8,
+  // i.e. one XCD and its L2, which then serves their repeated box reads
+  const int grp = blockIdx.x / (8 * S), within = blockIdx.x - grp * 8 * S;
+  const int split = within >> 3, unit = grp * 8 + (within & 7);
+  if (unit >= units) return;
+  const int b = unit / Hkv, h = unit - b * Hkv;
   const int tid = threadIdx.x;
   const int P = 1 << log2P;
   if (tid == 0) {
@@ -1436,7 +1477,7 @@ __global__ __launch_bounds__(NT, (step_min_blocks<DT, D, G, NT>())) void k_step(
   const int len = clampi(seq_lens[b], 0, MP * P);
   const int kb = clampi(k_per_seq ? k_per_seq[b] : k_max, 1, k_max);
   const int n = (len + P - 1) >> log2P;
-  if (k_new != nullptr && len >= 1 && tid < D) {
+  if (k_new != nullptr && split == 0 && len >= 1 && tid < D) {
     // the new token is slot (len-1) mod P of page (len-1)/P; its box widens
     // (or opens, on slot 0) before any box of the row is read
     const int pos = len - 1, p = pos >> log2P, slot = pos & (P - 1);
@@ -1459,7 +1500,7 @@ __global__ __launch_bounds__(NT, (step_min_blocks<DT, D, G, NT>())) void k_step(
   __syncthreads();  // block-table row staged; the appended token visible to the workgroup
   score_pages<DT, D, G, NT>(q, meta, s_phys, b, h, Hq, Hkv, n, 0, 1, s_key);
   __syncthreads();
-  if (scores_out) {
+  if (scores_out && split == 0) {
     float* srow_out = scores_out + (size_t)unit * MP;
     for (int p = tid; p < n; p += NT) srow_out[p] = key_to_score(s_key[p]);
   }
@@ -1470,30 +1511,39 @@ __global__ __launch_bounds__(NT, (step_min_blocks<DT, D, G, NT>())) void k_step(
   int32_t* srow = sel + (size_t)unit * k_max;
   float* orow = out + ((size_t)b * Hq + h * G) * D;
   if (cnt == 0) {
-    for (int i = tid; i < G * D; i += NT) orow[i] = 0.f;
-    for (int i = tid; i < k_max; i += NT) srow[i] = -1;
-    if (tid == 0) sel_count[unit] = 0;
+    if (split == 0) {
+      for (int i = tid; i < G * D; i += NT) orow[i] = 0.f;
+      for (int i = tid; i < k_max; i += NT) srow[i] = -1;
+      if (tid == 0) sel_count[unit] = 0;
+    }
     return;
   }
+  // this split's share of the selected-token stream
+  const long t_all = (long)cnt << log2P;
+  const long span = S > 1 ? step_span(t_all, S, kStepMinSpanSteps * 16 * NW) : t_all;
+  const long t0 = (long)split * span, t_end = min(t_all, t0 + span);
+  const int ns = (int)((t_all + span - 1) / span);
+  if (t0 >= t_end) return;  // split 0 always has tokens
   const TokenList tl{reinterpret_cast<const int*>(s_key), s_phys, cnt, 0, len, log2P, Hkv, h, D};
   const float* qg0 = q + ((size_t)b * Hq + h * G) * D;
   const char* kbp = reinterpret_cast<const char*>(k_pool);
   const char* vbp = reinterpret_cast<const char*>(v_pool);
-  const long t_end = (long)cnt << log2P;
   typedef float AccRow[G][D + 1];
   AccRow* s_acc = reinterpret_cast<AccRow*>(dec);
   if constexpr (MF) {
-    mfma_decode_range<DT, D, G, NW, D == 64 ? 4 : 2>(qg0, kbp, vbp, tl, 0, t_end, qscale,
+    mfma_decode_range<DT, D, G, NW, D == 64 ? 4 : 2>(qg0, kbp, vbp, tl, t0, t_end, qscale,
                                                      s_acc, s_mw);
     __syncthreads();
-    finish_split<D, G, NT, NW>(s_acc, s_mw, nullptr, out, b, h, Hq, 1, 0, 1);
+    finish_split<D, G, NT, NW>(s_acc, s_mw, partials, out, b, h, Hq, S, split, ns);
   } else {
-    valu_decode_range<DT, D, G, NT>(qg0, kbp, vbp, tl, 0, t_end, qscale, s_acc, s_mw);
+    valu_decode_range<DT, D, G, NT>(qg0, kbp, vbp, tl, t0, t_end, qscale, s_acc, s_mw);
     __syncthreads();
-    finish_split<D, G, NT, NW>(s_acc, s_mw, nullptr, out, b, h, Hq, 1, 0, 1);
+    finish_split<D, G, NT, NW>(s_acc, s_mw, partials, out, b, h, Hq, S, split, ns);
   }
-  for (int i = tid; i < k_max; i += NT) srow[i] = i < cnt ? (int32_t)s_key[i] : -1;
-  if (tid == 0) sel_count[unit] = cnt;
+  if (split == 0) {
+    for (int i = tid; i < k_max; i += NT) srow[i] = i < cnt ? (int32_t)s_key[i] : -1;
+    if (tid == 0) sel_count[unit] = cnt;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -1577,7 +1627,8 @@ size_t workspace_layout(const Dims& d, int k_max, void* base, Workspace* ws) {
   const size_t o_keys = 0;
   const size_t o_phys = o_keys + round_up(units * d.MP * sizeof(uint32_t));
   const size_t o_part = o_phys + round_up(units * k_max * sizeof(int32_t));
-  const size_t total = o_part + round_up((size_t)d.B * d.Hq * decode_splits(d, k_max) *
+  const size_t splits = std::max(decode_splits(d, k_max), step_splits(d, k_max));
+  const size_t total = o_part + round_up((size_t)d.B * d.Hq * splits *
                                          partial_stride(d) * sizeof(float));
   if (base && ws) {
     char* c = static_cast<char*>(base);
@@ -1683,31 +1734,53 @@ size_t step_lds_bytes(const Dims& d) {
 
 bool step_fits(const Dims& d) { return step_lds_bytes(d) <= kStepMaxLds; }
 
+// Workgroups per row: rows that leave most of the 256 CUs idle are spread
+// over up to 8 workgroups each (every one scores and selects the whole row,
+// then decodes its share of the kept tokens), as far as k_max pages give each
+// split its minimum span; the split partial states are combined by k_merge.
+int step_splits(const Dims& d, int k_max) {
+  const long units = (long)d.B * d.Hkv;
+  const long minspan = kStepMinSpanSteps * 16 * (step_threads(d) / kWave);
+  const long by_tokens = (long)k_max * d.P / minspan;
+  return (int)std::max(1L, std::min({8L, 256 / units, by_tokens}));
+}
+
 hipError_t launch_step(const Dims& d, const float* q, const void* k_new, const void* v_new,
                        void* k_pool, void* v_pool, void* meta, const int32_t* bt,
                        const int32_t* seq_lens, int k_max, const int32_t* k_per_seq,
                        int n_sink, float scale, int32_t* sel, int32_t* sel_count,
-                       float* scores_out, float* out, hipStream_t s) {
+                       float* scores_out, const Workspace& ws, float* out, hipStream_t s) {
   const int nt = step_threads(d);
   const size_t lds = step_lds_bytes(d);
   if (lds > kStepMaxLds) return hipErrorInvalidValue;
   const int log2P = ilog2(d.P);
   const float qscale = scale * 1.44269504088896340736f;  // fold log2(e)
-  const dim3 grid(d.B * d.Hkv);
-  return by_dt_d_g(d, [&](auto DT, auto HD, auto GG) -> hipError_t {
+  const int units = d.B * d.Hkv, S = step_splits(d, k_max);
+  const dim3 grid((units + 7) / 8 * 8 * S);
+  hipError_t e = by_dt_d_g(d, [&](auto DT, auto HD, auto GG) -> hipError_t {
     constexpr int dt = decltype(DT)::value, hd = decltype(HD)::value,
                   g = decltype(GG)::value;
     auto go = [&](auto NTc) -> hipError_t {
       constexpr int nthr = decltype(NTc)::value;
       hipLaunchKernelGGL((k_step<dt, hd, g, nthr>), grid, dim3(nthr), lds, s, q, k_new, v_new,
-                         k_pool, v_pool, meta, bt, seq_lens, d.Hq, d.Hkv, log2P, d.MP, d.NP,
-                         k_max, k_per_seq, n_sink, qscale, sel, sel_count, scores_out, out);
+                         k_pool, v_pool, meta, bt, seq_lens, units, d.Hq, d.Hkv, log2P, d.MP,
+                         d.NP, k_max, k_per_seq, n_sink, qscale, S, sel, sel_count,
+                         scores_out, ws.partials, out);
       return hipGetLastError();
     };
     if constexpr (g == 1)
       if (nt == 1024) return go(IC<1024>{});
     return nt == 256 ? go(IC<256>{}) : go(IC<512>{});
   });
+  if (e != hipSuccess || S == 1) return e;
+  const int waves = d.B * d.Hq, minspan = kStepMinSpanSteps * 16 * (nt / kWave);
+  if (d.D == 64)
+    hipLaunchKernelGGL(k_merge<64>, dim3((waves + 3) / 4), dim3(256), 0, s, ws.partials,
+                       sel_count, d.B, d.Hq, d.Hkv, d.G, log2P, k_max, S, 0, minspan, out);
+  else
+    hipLaunchKernelGGL(k_merge<128>, dim3((waves + 3) / 4), dim3(256), 0, s, ws.partials,
+                       sel_count, d.B, d.Hq, d.Hkv, d.G, log2P, k_max, S, 0, minspan, out);
+  return hipGetLastError();
 }
 
 hipError_t launch_decode(const Dims& d, const float* q, const void* k_pool,
@@ -1745,10 +1818,10 @@ hipError_t launch_decode(const Dims& d, const float* q, const void* k_pool,
   const int tile = decode_tile_tokens(d) * TPW;
   if (d.D == 64)
     hipLaunchKernelGGL(k_merge<64>, dim3((waves + 3) / 4), dim3(256), 0, s, ws.partials,
-                       sel_count, d.B, d.Hq, d.Hkv, d.G, log2P, k_max, S_max, tile, out);
+                       sel_count, d.B, d.Hq, d.Hkv, d.G, log2P, k_max, S_max, tile, 0, out);
   else
     hipLaunchKernelGGL(k_merge<128>, dim3((waves + 3) / 4), dim3(256), 0, s, ws.partials,
-                       sel_count, d.B, d.Hq, d.Hkv, d.G, log2P, k_max, S_max, tile, out);
+                       sel_count, d.B, d.Hq, d.Hkv, d.G, log2P, k_max, S_max, tile, 0, out);
   return hipGetLastError();
 }
 

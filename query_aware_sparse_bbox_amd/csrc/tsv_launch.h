@@ -58,16 +58,20 @@ hipError_t launch_decode(const Dims& d, const float* q, const void* k_pool,
                          int k_max, float scale, const Workspace& ws, float* out,
                          hipStream_t s);
 
-// The whole step of one (sequence, KV head) in one workgroup, one launch for
-// all rows: [append] -> score -> top-K -> decode.  Usable when step_fits(d)
-// (its LDS, which grows with max_pages_per_seq, stays within kStepMaxLds).
+// The whole step of one (sequence, KV head) in one workgroup (or in
+// step_splits(d) workgroups that each score and select the whole row and
+// decode a share of it, merged by a second launch): [append] -> score ->
+// top-K -> decode.  Usable when step_fits(d) (its LDS, which grows with
+// max_pages_per_seq, stays within kStepMaxLds).
 constexpr size_t kStepMaxLds = 64 * 1024;
 size_t step_lds_bytes(const Dims& d);
 bool step_fits(const Dims& d);
+// Workgroups per row of the one-workgroup step (k_merge runs when > 1).
+int step_splits(const Dims& d, int k_max);
 hipError_t launch_step(const Dims& d, const float* q, const void* k_new, const void* v_new,
                        void* k_pool, void* v_pool, void* meta, const int32_t* bt,
                        const int32_t* seq_lens, int k_max, const int32_t* k_per_seq,
                        int n_sink, float scale, int32_t* sel, int32_t* sel_count,
-                       float* scores_out, float* out, hipStream_t s);
+                       float* scores_out, const Workspace& ws, float* out, hipStream_t s);
 
 }  // namespace tsv

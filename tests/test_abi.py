@@ -85,9 +85,13 @@ def test_sizes(tsv):
 
 
 def test_decode_step_launch_plan(tsv):
-    # short block-table rows: the whole step of a row fits one workgroup
+    # short block-table rows: the whole step of a row runs in workgroups of
+    # its own; four rows with 64-page budgets leave the chip idle, so each row
+    # is split (+ a merge); 8-page budgets are too short to split
+    assert tsv.tsv_decode_step_launches(shape(), 64, True) == 2
+    assert tsv.tsv_decode_step_launches(shape(), 64, False) == 2
     assert tsv.tsv_decode_step_launches(shape(), 8, True) == 1
-    assert tsv.tsv_decode_step_launches(shape(), 8, False) == 1
+    assert tsv.tsv_decode_step_launches(shape(batch=128), 64, True) == 1
     # 8 query heads of 128 channels need more staging than one workgroup's
     # 64 KiB; 4096-entry rows with such staging too: the phases run apart
     big = shape(head_dim=128, num_q_heads=16, num_kv_heads=2, max_pages_per_seq=4096)

@@ -106,7 +106,9 @@ def test_one_launch_and_phased_paths_both_covered():
 
     for name in W.CONFIG_ORDER:
         wl = W.make(name)
-        assert T.tsv_decode_step_launches(wl.shape, wl.k_max, bool(wl.steps)) == 1, name
+        # 64 rows of 64 pages: each row over several workgroups, then a merge
+        want = 2 if name == "tinyllama" else 1
+        assert T.tsv_decode_step_launches(wl.shape, wl.k_max, bool(wl.steps)) == want, name
     wl = W.make("ragged", batch=2, lens_range=(65500, 65535), kv_dtype=W.BF16, num_q_heads=64)
     assert wl.shape.max_pages_per_seq >= 4064
     assert T.tsv_decode_step_launches(wl.shape, wl.k_max, True) == 4
