@@ -11,10 +11,12 @@ Cache.  Steps are replayed from a HIP graph (--eager: launched one by one).
 
 Prints one JSON line:
   value        (sequence x query head) / s of the whole step
-  roofline     the step kernel's algorithmic bytes / its mean duration (HIP
-               events around the graph-replayed steps on their stream) against
-               8 TB/s; `traffic` = HBM bytes per launch from rocprofv3 counters
-               when they were taken on the current kernel source, else null
+  roofline     the step's algorithmic bytes / its mean duration (HIP events
+               around the graph-replayed steps on their stream) against 8 TB/s;
+               the step is one kernel (k_step), or k_step + k_merge where rows
+               are spread over several workgroups; `traffic` = HBM bytes per
+               step from rocprofv3 counters when they were taken on the current
+               kernel source, else null
   cpu_baseline the CPU oracle (single thread) on a bounded sample of the step
 
 --copy-calibrate MB only runs a plain device copy of MB megabytes (the
@@ -54,10 +56,11 @@ DESCR = {
 KERNEL_SOURCES = [os.path.join(ROOT, "query_aware_sparse_bbox_amd", "csrc", f)
                   for f in ("tsv_kernels.hip", "tsv_api.hip", "tsv_launch.h")]
 
-# HBM bytes per k_step launch from `rocprofv3 --pmc FETCH_SIZE` and `--pmc
-# WRITE_SIZE` runs of this script, each divided by the same counter's reading
-# per byte of a plain device copy (--copy-calibrate).  Valid only for the
-# kernel source they were taken on (sha256 of KERNEL_SOURCES, first 16 hex).
+# HBM bytes per step (all its kernels) from `rocprofv3 --pmc FETCH_SIZE` and
+# `--pmc WRITE_SIZE` runs of this script, each divided by the same counter's
+# reading per byte of a plain device copy (--copy-calibrate).  Valid only for
+# the kernel source they were taken on (sha256 of KERNEL_SOURCES, first 16
+# hex digits).
 TRAFFIC = {}
 
 
@@ -273,9 +276,10 @@ def main():
     step_gbs = nb["total"] / (ms_step * 1e-3) / 1e9
     src = source_hash()
     tr = TRAFFIC.get(args.config)
-    traffic = tr["bytes_per_launch"] if tr and tr["source"] == src and launches == 1 else None
-    kernel = "k_step (whole step: append, score, select, decode)" if launches == 1 else \
-        f"tsv_decode_step ({launches} kernels)"
+    traffic = tr["bytes_per_step"] if tr and tr["source"] == src else None
+    kernel = {1: "k_step (append, score, select, decode of every row)",
+              2: "k_step + k_merge (rows spread over several workgroups, then merged)"}.get(
+        launches, f"tsv_decode_step phased path ({launches} kernels)")
     line = {
         "metric": METRIC,
         "value": value,
@@ -298,9 +302,11 @@ def main():
         "roofline": {"bound": "hbm", "kernel": kernel,
                      "achieved": step_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": step_gbs / PEAK_HBM_GBS, "traffic": traffic,
-                     "algorithmic_bytes_per_launch": nb["total"],
-                     "mean_launch_us": ms_step * 1e3 / max(launches, 1) if launches == 1
-                     else None,
+                     "algorithmic_bytes_per_step": nb["total"],
+                     "launches_per_step": launches,
+                     "mean_step_us": ms_step * 1e3,
+                     "timed_as": "HIP events on the launch stream around the graph-replayed "
+                                 "steps, divided by the step count",
                      "kernel_source": src},
         "cpu_baseline": cpu,
     }

@@ -312,7 +312,7 @@ __device__ __forceinline__ uint32_t wave_reduce(uint32_t x, Op op) {
 // written before a barrier that precedes the call).
 template <int NT>
 struct SelectLds {
-  int hist[256];
+  int hist[2][256];  // passes alternate, so a pass's scan overlaps the next clear
   int red[8];
   int scan[NT / 64];
 };
@@ -388,12 +388,13 @@ __device__ __forceinline__ int select_block(uint32_t* s_key, uint32_t* s_phys, i
       int top = 31 - __clz(a ^ o);
       tmask = top == 31 ? 0u : ~((2u << top) - 1u);
       tau = a & tmask;
-      for (;;) {
+      if (tid < 256) sl.hist[0][tid] = 0;
+      __syncthreads();
+      for (int pass = 0;; ++pass) {
         const int width = min(8, top + 1), shift = top + 1 - width;
         const uint32_t dmask = (1u << width) - 1u;
         const int nb = 1 << width;
-        if (tid < 256) sl.hist[tid] = 0;
-        __syncthreads();
+        int* hist = sl.hist[pass & 1];
 #pragma unroll
         for (int i = 0; i < MAXM; ++i) {
           if (i >= m) break;
@@ -404,8 +405,8 @@ __device__ __forceinline__ int select_block(uint32_t* s_key, uint32_t* s_phys, i
             const int src = __ffsll(act) - 1;
             const int dl = __builtin_amdgcn_readlane(d, src);
             const unsigned long long same = __ballot(d == dl);
-            if (lane == src) atomicAdd(&sl.hist[dl], (int)__popcll(same));
-            else if (in && d != dl) atomicAdd(&sl.hist[d], 1);
+            if (lane == src) atomicAdd(&hist[dl], (int)__popcll(same));
+            else if (in && d != dl) atomicAdd(&hist[d], 1);
           }
         }
         __syncthreads();
@@ -414,7 +415,7 @@ __device__ __forceinline__ int select_block(uint32_t* s_key, uint32_t* s_phys, i
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             const int bin = nb - 1 - 4 * lane - j;
-            c[j] = bin >= 0 ? sl.hist[bin] : 0;
+            c[j] = bin >= 0 ? hist[bin] : 0;
             sum += c[j];
           }
           int before = wave_incl_scan(sum, lane) - sum;  // keys in higher digits
@@ -427,6 +428,9 @@ __device__ __forceinline__ int select_block(uint32_t* s_key, uint32_t* s_phys, i
             }
             before += c[j];
           }
+        } else {
+          // the other waves clear the next pass's histogram meanwhile
+          for (int i = tid - kWave; i < 256; i += NT - kWave) sl.hist[(pass + 1) & 1][i] = 0;
         }
         __syncthreads();
         const int dg = sl.red[2], cb = sl.red[4];
@@ -698,7 +702,7 @@ __device__ __forceinline__ long step_span(long t_all, int S, int minspan) {
 template <int D>
 __global__ __launch_bounds__(256) void k_merge(
     const float* __restrict__ partials, const int32_t* __restrict__ sel_count, int B,
-    int Hq, int Hkv, int G, int log2P, int k_max, int S_max, int tile, int minspan,
+    int Hq, int Hkv, int G, int log2P, int k_max, int S_max, int tile,
     float* __restrict__ out) {
   constexpr int PER = D / kWave, UNR = 8;
   const int gw = blockIdx.x * 4 + threadIdx.x / kWave;
@@ -706,10 +710,7 @@ __global__ __launch_bounds__(256) void k_merge(
   if (gw >= B * Hq) return;
   const int b = gw / Hq, hq = gw - b * Hq, h = hq / G;
   const int cnt = clampi(sel_count[(size_t)b * Hkv + h], 0, k_max);
-  // splits of `tile` tokens, or (tile == 0) of step_span(t_all, S_max, minspan)
-  const long t_all = (long)cnt << log2P;
-  const long span = tile > 0 ? tile : step_span(t_all, S_max, minspan);
-  const int ns = (int)((t_all + span - 1) / span);
+  const int ns = (int)((((long)cnt << log2P) + tile - 1) / tile);
   if (ns <= 1) return;  // finished by the decode tile itself
   const float* base = partials + (size_t)gw * S_max * (D + 2);
   // global max and denominator, 64 tiles per pass
@@ -761,6 +762,51 @@ __global__ __launch_bounds__(256) void k_merge(
 #pragma unroll
   for (int i = 0; i < PER; ++i)
     out[(size_t)gw * D + lane + kWave * i] = l > 0.f ? acc[i] / l : 0.f;
+}
+
+// Merge of the one-workgroup step's splits: every split of a row left a
+// partial state in its slot (one with max -inf when it had no tokens), so one
+// wave per (sequence, query head) reads all S slots in one round of loads.
+constexpr int kStepMaxSplits = 8;
+
+template <int D>
+__global__ __launch_bounds__(256) void k_merge_step(const float* __restrict__ partials, int BHq,
+                                                    int S, float* __restrict__ out) {
+  constexpr int PER = D / kWave;
+  const int gw = blockIdx.x * 4 + threadIdx.x / kWave;
+  const int lane = threadIdx.x & (kWave - 1);
+  if (gw >= BHq) return;
+  const float* base = partials + (size_t)gw * S * (D + 2);
+  float m[kStepMaxSplits], l[kStepMaxSplits], a[kStepMaxSplits][PER];
+#pragma unroll
+  for (int s = 0; s < kStepMaxSplits; ++s) {
+    if (s >= S) break;
+    const float* ps = base + (size_t)s * (D + 2);
+    m[s] = ps[D];
+    l[s] = ps[D + 1];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) a[s][i] = ps[lane + kWave * i];
+  }
+  float M = -INFINITY;
+#pragma unroll
+  for (int s = 0; s < kStepMaxSplits; ++s) {
+    if (s >= S) break;
+    M = fmaxf(M, m[s]);
+  }
+  float L = 0.f, acc[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) acc[i] = 0.f;
+#pragma unroll
+  for (int s = 0; s < kStepMaxSplits; ++s) {
+    if (s >= S) break;
+    if (m[s] == -INFINITY) continue;  // an empty slot: its sums were never written
+    const float w = __builtin_amdgcn_exp2f(m[s] - M);
+    L = __builtin_fmaf(w, l[s], L);
+#pragma unroll
+    for (int i = 0; i < PER; ++i) acc[i] = __builtin_fmaf(w, a[s][i], acc[i]);
+  }
+#pragma unroll
+  for (int i = 0; i < PER; ++i) out[(size_t)gw * D + lane + kWave * i] = L > 0.f ? acc[i] / L : 0.f;
 }
 
 // End of a split: wave w left its unnormalised sum in s_acc[w][g][0..D),
@@ -1340,7 +1386,7 @@ __device__ __forceinline__ void mfma_decode_range(const float* __restrict__ qg0,
       }
     }
   };
-  if (mine > 0) {
+  if (mine > CH) {
     Chunk ca, cb;
     load(0, ca);
     for (int i = 0; i < mine; i += 2 * CH) {
@@ -1350,6 +1396,10 @@ __device__ __forceinline__ void mfma_decode_range(const float* __restrict__ qg0,
       load(i + 2 * CH, ca);
       compute(i + CH, cb);
     }
+  } else if (mine > 0) {  // one chunk: nothing to prefetch
+    Chunk ca;
+    load(0, ca);
+    compute(0, ca);
   }
   l_run += __shfl_xor(l_run, 16);
   l_run += __shfl_xor(l_run, 32);
@@ -1510,20 +1560,34 @@ __global__ __launch_bounds__(NT, (step_min_blocks<DT, D, G, NT>())) void k_step(
   const int cnt = select_block<NT>(s_key, s_phys, n, keff, f, k_max, nullptr, nullptr, nullptr, sl);
   int32_t* srow = sel + (size_t)unit * k_max;
   float* orow = out + ((size_t)b * Hq + h * G) * D;
+  // with S > 1 every split leaves a partial state for k_merge_step; a split
+  // without tokens leaves an empty one (max -inf)
+  auto empty_partial = [&]() {
+    for (int g = tid; g < G; g += NT) {
+      float* dst = partials + (((size_t)b * Hq + h * G + g) * S + split) * (D + 2);
+      dst[D] = -INFINITY;
+      dst[D + 1] = 0.f;
+    }
+  };
   if (cnt == 0) {
     if (split == 0) {
-      for (int i = tid; i < G * D; i += NT) orow[i] = 0.f;
+      if (S == 1)
+        for (int i = tid; i < G * D; i += NT) orow[i] = 0.f;
       for (int i = tid; i < k_max; i += NT) srow[i] = -1;
       if (tid == 0) sel_count[unit] = 0;
     }
+    if (S > 1) empty_partial();
     return;
   }
   // this split's share of the selected-token stream
   const long t_all = (long)cnt << log2P;
   const long span = S > 1 ? step_span(t_all, S, kStepMinSpanSteps * 16 * NW) : t_all;
   const long t0 = (long)split * span, t_end = min(t_all, t0 + span);
-  const int ns = (int)((t_all + span - 1) / span);
-  if (t0 >= t_end) return;  // split 0 always has tokens
+  const int ns = S > 1 ? S : 1;  // S > 1: always a partial state, merged by k_merge_step
+  if (t0 >= t_end) {  // split 0 always has tokens
+    empty_partial();
+    return;
+  }
   const TokenList tl{reinterpret_cast<const int*>(s_key), s_phys, cnt, 0, len, log2P, Hkv, h, D};
   const float* qg0 = q + ((size_t)b * Hq + h * G) * D;
   const char* kbp = reinterpret_cast<const char*>(k_pool);
@@ -1742,7 +1806,7 @@ int step_splits(const Dims& d, int k_max) {
   const long units = (long)d.B * d.Hkv;
   const long minspan = kStepMinSpanSteps * 16 * (step_threads(d) / kWave);
   const long by_tokens = (long)k_max * d.P / minspan;
-  return (int)std::max(1L, std::min({8L, 256 / units, by_tokens}));
+  return (int)std::max(1L, std::min({(long)kStepMaxSplits, 256 / units, by_tokens}));
 }
 
 hipError_t launch_step(const Dims& d, const float* q, const void* k_new, const void* v_new,
@@ -1773,13 +1837,13 @@ hipError_t launch_step(const Dims& d, const float* q, const void* k_new, const v
     return nt == 256 ? go(IC<256>{}) : go(IC<512>{});
   });
   if (e != hipSuccess || S == 1) return e;
-  const int waves = d.B * d.Hq, minspan = kStepMinSpanSteps * 16 * (nt / kWave);
+  const int waves = d.B * d.Hq;
   if (d.D == 64)
-    hipLaunchKernelGGL(k_merge<64>, dim3((waves + 3) / 4), dim3(256), 0, s, ws.partials,
-                       sel_count, d.B, d.Hq, d.Hkv, d.G, log2P, k_max, S, 0, minspan, out);
+    hipLaunchKernelGGL(k_merge_step<64>, dim3((waves + 3) / 4), dim3(256), 0, s, ws.partials,
+                       waves, S, out);
   else
-    hipLaunchKernelGGL(k_merge<128>, dim3((waves + 3) / 4), dim3(256), 0, s, ws.partials,
-                       sel_count, d.B, d.Hq, d.Hkv, d.G, log2P, k_max, S, 0, minspan, out);
+    hipLaunchKernelGGL(k_merge_step<128>, dim3((waves + 3) / 4), dim3(256), 0, s, ws.partials,
+                       waves, S, out);
   return hipGetLastError();
 }
 
@@ -1818,10 +1882,10 @@ hipError_t launch_decode(const Dims& d, const float* q, const void* k_pool,
   const int tile = decode_tile_tokens(d) * TPW;
   if (d.D == 64)
     hipLaunchKernelGGL(k_merge<64>, dim3((waves + 3) / 4), dim3(256), 0, s, ws.partials,
-                       sel_count, d.B, d.Hq, d.Hkv, d.G, log2P, k_max, S_max, tile, 0, out);
+                       sel_count, d.B, d.Hq, d.Hkv, d.G, log2P, k_max, S_max, tile, out);
   else
     hipLaunchKernelGGL(k_merge<128>, dim3((waves + 3) / 4), dim3(256), 0, s, ws.partials,
-                       sel_count, d.B, d.Hq, d.Hkv, d.G, log2P, k_max, S_max, tile, 0, out);
+                       sel_count, d.B, d.Hq, d.Hkv, d.G, log2P, k_max, S_max, tile, out);
   return hipGetLastError();
 }
 
