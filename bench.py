@@ -61,7 +61,13 @@ KERNEL_SOURCES = [os.path.join(ROOT, "query_aware_sparse_bbox_amd", "csrc", f)
 # reading per byte of a plain device copy (--copy-calibrate).  Valid only for
 # the kernel source they were taken on (sha256 of KERNEL_SOURCES, first 16
 # hex digits).
-TRAFFIC = {}
+TRAFFIC = {
+    "tinyllama": {"source": "566f9ca64130152b", "bytes_per_step": 22328834, "read": 21654834, "written": 674000},
+    "tiny": {"source": "566f9ca64130152b", "bytes_per_step": 532840, "read": 531590, "written": 1250},
+    "gpt2": {"source": "566f9ca64130152b", "bytes_per_step": 41661822, "read": 41485822, "written": 176000},
+    "llama_long": {"source": "566f9ca64130152b", "bytes_per_step": 197409228, "read": 197273228, "written": 136000},
+    "ragged": {"source": "566f9ca64130152b", "bytes_per_step": 393439088, "read": 391978308, "written": 1460779},
+}
 
 
 def source_hash() -> str:
