@@ -62,11 +62,11 @@ KERNEL_SOURCES = [os.path.join(ROOT, "query_aware_sparse_bbox_amd", "csrc", f)
 # the kernel source they were taken on (sha256 of KERNEL_SOURCES, first 16
 # hex digits).
 TRAFFIC = {
-    "tinyllama": {"source": "566f9ca64130152b", "bytes_per_step": 22328834, "read": 21654834, "written": 674000},
-    "tiny": {"source": "566f9ca64130152b", "bytes_per_step": 532840, "read": 531590, "written": 1250},
-    "gpt2": {"source": "566f9ca64130152b", "bytes_per_step": 41661822, "read": 41485822, "written": 176000},
-    "llama_long": {"source": "566f9ca64130152b", "bytes_per_step": 197409228, "read": 197273228, "written": 136000},
-    "ragged": {"source": "566f9ca64130152b", "bytes_per_step": 393439088, "read": 391978308, "written": 1460779},
+    "tinyllama": {"source": "566f9ca64130152b", "bytes_per_step": 22864726, "read": 22174550, "written": 690176},
+    "tiny": {"source": "566f9ca64130152b", "bytes_per_step": 545629, "read": 544349, "written": 1280},
+    "gpt2": {"source": "566f9ca64130152b", "bytes_per_step": 42661705, "read": 42481481, "written": 180224},
+    "llama_long": {"source": "566f9ca64130152b", "bytes_per_step": 202147049, "read": 202007785, "written": 139264},
+    "ragged": {"source": "566f9ca64130152b", "bytes_per_step": 402881626, "read": 401385788, "written": 1495838},
 }
 
 
