@@ -18,6 +18,9 @@ Prints one JSON line:
                step from rocprofv3 counters when they were taken on the current
                kernel source, else null
   cpu_baseline the CPU oracle (single thread) on a bounded sample of the step
+  selection_quality  share of the exact softmax mass (float64, sampled rows)
+               that falls on the kept pages, and the same step with every page
+               kept (dense) timed the same way
 
 --copy-calibrate MB only runs a plain device copy of MB megabytes (the
 reference kernel for scaling the HBM byte counters) and exits.
@@ -114,6 +117,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="CPU-oracle baseline budget (0 disables it)")
     ap.add_argument("--eager", action="store_true", help="launch steps one by one (no graph)")
+    ap.add_argument("--no-quality", action="store_true",
+                    help="skip the selection-quality / dense-speedup report")
     ap.add_argument("--copy-calibrate", type=float, default=0.0, metavar="MB",
                     help="only run a plain device copy of MB megabytes, 5 times, and exit")
     return ap.parse_args()
@@ -259,6 +264,80 @@ def main():
     ms_step = t0.elapsed_time(t1) / K
     print(f"[bench] step {ms_step * 1e3:.2f} us (wall {wall / K * 1e6:.2f} us/step)", flush=True)
 
+    # selection quality: the share of exact softmax mass on the kept pages,
+    # and the same step with every page kept (the dense baseline, same kernels)
+    quality = None
+    if not args.no_quality:
+        MP = sh.max_pages_per_seq
+        dense = []
+        for d in insts:
+            e = type("Dense", (), {})()
+            e.sel = torch.empty((B, Hkv, MP), dtype=torch.int32, device=dev)
+            e.cnt = torch.empty((B, Hkv), dtype=torch.int32, device=dev)
+            e.out = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
+            e.ws = T.new_workspace(sh, MP, dev)
+            e.src = d
+            dense.append(e)
+
+        def dstep(e):
+            d = e.src
+            T.tsv_decode_step(sh, q, k_new, v_new, d.k_pool, d.v_pool, d.meta, bt, lens, MP,
+                              None, n_sink, scale, e.sel, e.cnt, None, e.out, e.ws)
+
+        s2 = torch.cuda.Stream()
+        s2.wait_stream(stream)
+        with torch.cuda.stream(s2):
+            for e in dense:
+                dstep(e)
+        stream.wait_stream(s2)
+        torch.cuda.synchronize()
+        gd = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gd):
+            for e in dense:
+                dstep(e)
+        reps = max(1, min(K, 100) // R)
+        gd.replay()
+        torch.cuda.synchronize()
+        t0.record(stream)
+        for _ in range(reps):
+            gd.replay()
+        t1.record(stream)
+        torch.cuda.synchronize()
+        ms_dense = t0.elapsed_time(t1) / (reps * R)
+        # recall on sampled (sequence, KV head) rows of the first instance,
+        # in float64 from the pool after the step
+        step(first)
+        torch.cuda.synchronize()
+        sel_np, cnt_np = first.sel.cpu().numpy(), first.cnt.cpu().numpy()
+        P = sh.page_size
+        units = B * Hkv
+        rows = list(range(0, units, max(1, units // 32)))[:32]
+        recalls = []
+        for u in rows:
+            b, h = divmod(u, Hkv)
+            L = int(lens_np[b])
+            n_pages = (L + P - 1) // P
+            phys = torch.from_numpy(wl.block_table[b, :n_pages].astype(np.int64)).to(dev)
+            kt = first.k_pool[phys, h].float().reshape(-1, D)[:L].double().cpu().numpy()
+            page_of = np.arange(L) // P
+            keep = np.zeros(n_pages, dtype=bool)
+            keep[sel_np[b, h, :cnt_np[b, h]]] = True
+            for g in range(sh.group):
+                z = (kt @ q_np[b, h * sh.group + g].astype(np.float64)) * float(scale)
+                w = np.exp(z - z.max())
+                recalls.append(float(w[keep[page_of]].sum() / w.sum()))
+        recalls = np.array(recalls)
+        quality = {"attention_mass_recall_mean": float(recalls.mean()),
+                   "attention_mass_recall_min": float(recalls.min()),
+                   "rows_sampled": len(rows), "query_heads_sampled": int(recalls.size),
+                   "dense_step_us": ms_dense * 1e3,
+                   "sparse_speedup_vs_dense": ms_dense / ms_step,
+                   "dense": "the same tsv_decode_step with every page kept (k_max = max pages)"}
+        print(f"[bench] dense step {ms_dense * 1e3:.2f} us, speedup {ms_dense / ms_step:.2f}x, "
+              f"attention-mass recall mean {recalls.mean():.4f} min {recalls.min():.4f}",
+              flush=True)
+        del dense, gd
+
     # CPU oracle baseline (single thread) on a bounded sample of the same step
     cpu = None
     if args.cpu_seconds > 0:
@@ -315,6 +394,7 @@ def main():
                                  "steps, divided by the step count",
                      "kernel_source": src},
         "cpu_baseline": cpu,
+        "selection_quality": quality,
     }
     print(json.dumps(line), flush=True)
 
