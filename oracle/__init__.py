@@ -23,12 +23,17 @@ class Shape(ctypes.Structure):
                  "max_pages_per_seq", "num_phys_pages", "kv_dtype")]
 
 
+# The library to load: the built oracle, or (mutation tests only) a copy with
+# a planted mistake named by TSV_ORACLE_LIB.
+LIB_PATH = os.environ.get("TSV_ORACLE_LIB", _build.LIB)
+
+
 def _load():
     global _lib
     if _lib is None:
-        if not os.path.exists(_build.LIB):
+        if LIB_PATH == _build.LIB and not os.path.exists(LIB_PATH):
             _build.build()
-        lib = ctypes.CDLL(_build.LIB)
+        lib = ctypes.CDLL(LIB_PATH)
         P = ctypes.c_void_p
         I = ctypes.c_int32
         sig = {
