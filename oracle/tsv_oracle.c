@@ -39,7 +39,9 @@
 /* storage formats                                                            */
 /* ------------------------------------------------------------------------- */
 
-static size_t elem_bytes(int dtype) { return dtype == TSVO_F32 ? 4u : 2u; }
+static size_t elem_bytes(int dtype) {
+  return dtype == TSVO_F32 ? 4u : dtype == TSVO_FP8 ? 1u : 2u;
+}
 
 /* IEEE 754 binary16 -> float, from the format's definition. */
 static float half_bits_to_float(uint16_t h) {
@@ -65,6 +67,23 @@ static float bf16_bits_to_float(uint16_t b) {
   return f;
 }
 
+/* OCP FP8 E4M3 -> float, from the format's definition: exponent field e
+ * (bias 7), mantissa m; e = 0 is subnormal (m/8 * 2^-6); e = 15 with m = 7 is
+ * NaN; there are no infinities. */
+static float fp8_bits_to_float(uint8_t b) {
+  int sign = (b >> 7) & 1;
+  int e = (b >> 3) & 0xf;
+  int m = b & 7;
+  double v;
+  if (e == 15 && m == 7)
+    v = NAN;
+  else if (e == 0)
+    v = ldexp((double)m, -9); /* m/8 * 2^-6 */
+  else
+    v = ldexp((double)(8 + m), e - 10); /* (1 + m/8) * 2^(e-7) */
+  return (float)(sign ? -v : v);
+}
+
 /* every binary16 pattern decoded once by half_bits_to_float */
 static float half_table[65536];
 static int half_table_ready = 0;
@@ -83,6 +102,7 @@ static float kv_get(const void* base, int64_t i, int dtype) {
     memcpy(&f, (const char*)base + 4 * i, 4);
     return f;
   }
+  if (dtype == TSVO_FP8) return fp8_bits_to_float(((const uint8_t*)base)[i]);
   uint16_t h;
   memcpy(&h, (const char*)base + 2 * i, 2);
   return dtype == TSVO_F16 ? half_lookup(h) : bf16_bits_to_float(h);
@@ -106,7 +126,7 @@ static int shape_ok(const tsvo_shape* s) {
     return 0;
   if (s->num_q_heads % s->num_kv_heads) return 0;
   if (s->head_dim & (s->head_dim - 1)) return 0; /* tree needs a power of 2 */
-  if (s->kv_dtype < TSVO_F32 || s->kv_dtype > TSVO_BF16) return 0;
+  if (s->kv_dtype < TSVO_F32 || s->kv_dtype > TSVO_FP8) return 0;
   return 1;
 }
 

@@ -36,7 +36,10 @@
 extern "C" {
 #endif
 
-enum { TSVO_F32 = 0, TSVO_F16 = 1, TSVO_BF16 = 2 };
+/* KV storage formats: IEEE binary32, IEEE binary16, bfloat16, and OCP FP8
+ * E4M3 (1 sign, 4 exponent bits with bias 7, 3 mantissa bits; no
+ * infinities, 0x7F / 0xFF are NaN, largest finite 448). */
+enum { TSVO_F32 = 0, TSVO_F16 = 1, TSVO_BF16 = 2, TSVO_FP8 = 3 };
 
 typedef struct {
   int32_t batch, num_q_heads, num_kv_heads, head_dim, page_size,

@@ -47,6 +47,10 @@ MUTATIONS = [
      "for (int64_t t = 0; t < v; ++t) tok[nt++]", "for (int64_t t = 0; t + 1 < v; ++t) tok[nt++]"),
     ("values read from the key pool",
      "acc[d] += w * (double)kv_get(v_pool,", "acc[d] += w * (double)kv_get(k_pool,"),
+    ("fp8 exponent bias 8 (the FNUZ variant)",
+     "v = ldexp((double)(8 + m), e - 10);", "v = ldexp((double)(8 + m), e - 11);"),
+    ("fp8 subnormals scaled like normals",
+     "v = ldexp((double)m, -9);", "v = ldexp((double)m, -10);"),
     ("selection output in score order",
      "for (int64_t p = 0; p < n; ++p)\n        if (chosen[p]) out[c++] = (int32_t)p;",
      "for (int64_t i = 0; i < keff - f; ++i) out[c++] = cand[i].page;\n"

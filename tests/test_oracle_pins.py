@@ -121,6 +121,52 @@ def test_decoder_every_finite_pattern(dtype):
     assert np.array_equal(sc.view(np.uint32), expect.view(np.uint32))
 
 
+def test_fp8_decoder_every_finite_pattern():
+    """Every finite OCP E4M3 code decodes to torch's float8_e4m3fn value (D = 1)."""
+    torch = pytest.importorskip("torch")
+    codes = np.arange(256, dtype=np.uint8)
+    lib = torch.from_numpy(codes.copy()).view(torch.float8_e4m3fn).float().numpy()
+    keep = np.isfinite(lib)
+    assert keep.sum() == 254          # 0x7F and 0xFF are the only NaNs
+    codes, vals = codes[keep], lib[keep]
+    n = len(codes)
+    sh = W.Shape(1, 1, 1, 1, 1, n, n, W.F8)
+    bt = np.arange(n, dtype=np.int32).reshape(1, n)
+    lens = np.array([n], dtype=np.int32)
+    meta = O.meta_build(sh, codes.reshape(n, 1, 1, 1), bt, lens)
+    sc = O.page_scores(sh, np.ones((1, 1, 1), np.float32), meta, bt, lens)[0, 0]
+    expect = vals.copy()
+    expect[expect == 0] = 0.0
+    assert np.array_equal(sc.view(np.uint32), expect.view(np.uint32))
+    # the generator's widening table agrees with the library too
+    back = W.storage_to_f32(np.arange(256, dtype=np.uint8), W.F8)
+    assert np.array_equal(back[keep].view(np.uint32),
+                          lib[keep].view(np.uint32))
+
+
+def test_fp8_rounding_is_nearest_even():
+    """Input rounding to E4M3: torch's conversion inside the finite range
+    (every midpoint included), saturation to +-448 outside it."""
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(8)
+    grid = W.storage_to_f32(np.arange(127, dtype=np.uint8), W.F8).astype(np.float64)
+    mids = (grid[:-1] + grid[1:]) / 2
+    x = np.concatenate([rng.normal(0, 1, 50000), rng.normal(0, 40, 50000),
+                        rng.normal(0, 0.01, 20000), mids, -mids,
+                        np.nextafter(mids, 0), np.nextafter(mids, 1e9)]).astype(np.float32)
+    x = x[np.abs(x) < 464]
+    got = W.to_storage(x, W.F8)
+    lib = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(got, lib)
+    # brute force: the stored value is a nearest grid point
+    v = W.storage_to_f32(got, W.F8).astype(np.float64)
+    sgrid = np.concatenate([-grid[::-1], grid])
+    dist = np.abs(x.astype(np.float64)[:, None] - sgrid[None, :]).min(axis=1)
+    assert np.array_equal(np.abs(x - v), dist)
+    big = np.array([464, 465, 1e4, -1e30], np.float32)
+    assert W.to_storage(big, W.F8).tolist() == [0x7E, 0x7E, 0x7E, 0xFE]
+
+
 # ----------------------------------------------------------------------------
 # page score: closed form and bound
 # ----------------------------------------------------------------------------
@@ -230,7 +276,7 @@ def test_integer_inputs_give_exact_scores():
 # metadata
 # ----------------------------------------------------------------------------
 
-@pytest.mark.parametrize("dtype", [W.F32, W.F16, W.BF16])
+@pytest.mark.parametrize("dtype", [W.F32, W.F16, W.BF16, W.F8])
 def test_box_is_tightest(dtype):
     """Every valid key lies in the box and every face is attained by a valid key."""
     wl = W.make("gpt2", batch=3, context=77, kv_dtype=dtype)
@@ -396,6 +442,7 @@ def dense_attention_f64(wl):
     ("tiny", dict(context=333)),
     ("tinyllama", dict(batch=2, context=517)),
     ("ragged", dict(batch=3, lens_range=(30, 200), append_steps=0)),
+    ("tinyllama", dict(batch=2, context=300, kv_dtype=W.F8)),
 ])
 def test_all_pages_equals_dense_attention(name, kw):
     wl = W.make(name, **kw)

@@ -21,8 +21,11 @@ synthetic with those models' decode shapes:
   rounded buffers.
 
 Storage conventions: fp32 pools are ``float32`` arrays, fp16 pools
-``float16`` arrays and bf16 pools ``uint16`` arrays holding the bf16 bit
-patterns.  Layouts: pools ``[NP][Hkv][P][D]``, ``q`` ``[B][Hq][D]`` fp32,
+``float16`` arrays, bf16 pools ``uint16`` arrays holding the bf16 bit
+patterns and fp8 pools ``uint8`` arrays holding OCP E4M3 ("FN") codes: sign,
+4 exponent bits with bias 7, 3 mantissa bits, no infinities, NaN only at
+magnitude code 0x7F, largest finite 448.  fp8 values are stored unscaled (the
+synthetic keys and values lie well inside its range).  Layouts: pools ``[NP][Hkv][P][D]``, ``q`` ``[B][Hq][D]`` fp32,
 ``block_table`` ``[B][MP]`` int32, ``seq_lens`` ``[B]`` int32 (length counts
 the token being decoded).
 """
@@ -36,10 +39,38 @@ from typing import Optional
 
 import numpy as np
 
-F32, F16, BF16 = 0, 1, 2
-DTYPE_NAMES = {F32: "f32", F16: "f16", BF16: "bf16"}
-DTYPE_BYTES = {F32: 4, F16: 2, BF16: 2}
-STORAGE_NP = {F32: np.float32, F16: np.float16, BF16: np.uint16}
+F32, F16, BF16, F8 = 0, 1, 2, 3
+DTYPE_NAMES = {F32: "f32", F16: "f16", BF16: "bf16", F8: "fp8e4m3"}
+DTYPE_BYTES = {F32: 4, F16: 2, BF16: 2, F8: 1}
+STORAGE_NP = {F32: np.float32, F16: np.float16, BF16: np.uint16, F8: np.uint8}
+
+
+def _e4m3_table() -> np.ndarray:
+    """Value of every E4M3 code 0..255 (float64), from the format's definition."""
+    c = np.arange(256)
+    e = (c >> 3) & 0xF
+    m = (c & 7).astype(np.float64)
+    mag = np.where(e == 0, m * 2.0 ** -9, (8.0 + m) * np.exp2(e - 10.0))
+    mag = np.where((c & 0x7F) == 0x7F, np.nan, mag)
+    return np.where(c >= 128, -mag, mag)
+
+
+_E4M3 = _e4m3_table()
+_E4M3_POS = _E4M3[:127]                                  # codes 0..126, increasing
+_E4M3_MID = (_E4M3_POS[:-1] + _E4M3_POS[1:]) / 2.0       # exact in float64
+
+
+def _to_e4m3(x: np.ndarray) -> np.ndarray:
+    """float32 -> E4M3 code: nearest value, ties to the even code, |x| > 448
+    saturates to 448, NaN -> 0x7F (sign kept)."""
+    a = np.abs(x.astype(np.float64))
+    lo = np.clip(np.searchsorted(_E4M3_MID, a, side="left"), 0, 126)
+    # lo = number of midpoints strictly below a: a lies in (mid[lo-1], mid[lo]]
+    hi = np.minimum(lo + 1, 126)
+    tie = (lo < 126) & (a == _E4M3_MID[np.minimum(lo, 125)])
+    code = np.where(tie & (lo % 2 == 1), hi, lo)
+    code = np.where(np.isnan(a), 0x7F, code).astype(np.uint8)
+    return code | (np.signbit(x).astype(np.uint8) << 7)
 
 
 @dataclass
@@ -105,6 +136,8 @@ def to_storage(x: np.ndarray, dtype: int) -> np.ndarray:
         u = x.view(np.uint32)
         u = (u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)
         return u.astype(np.uint16)
+    if dtype == F8:
+        return _to_e4m3(x)
     raise ValueError(f"unknown kv dtype {dtype}")
 
 
@@ -116,6 +149,8 @@ def storage_to_f32(a: np.ndarray, dtype: int) -> np.ndarray:
         return np.asarray(a, dtype=np.float16).astype(np.float32)
     if dtype == BF16:
         return (np.asarray(a, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+    if dtype == F8:
+        return _E4M3[np.asarray(a, dtype=np.uint8)].astype(np.float32)
     raise ValueError(f"unknown kv dtype {dtype}")
 
 
