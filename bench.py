@@ -113,6 +113,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=300)
     ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--config", default=DEFAULT_CONFIG, choices=W.CONFIG_ORDER)
+    ap.add_argument("--kv-dtype", default=None, choices=sorted(W.DTYPE_NAMES.values()),
+                    help="store the KV cache in this type instead of the configuration's own")
     ap.add_argument("--rotate", type=int, default=0, help="pool copies (0: auto, >=512 MB)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="CPU-oracle baseline budget (0 disables it)")
@@ -162,7 +164,10 @@ def main():
 
     dev = "cuda"
     t_gen = time.time()
-    wl = W.make(args.config)
+    dtype_of = {v: k for k, v in W.DTYPE_NAMES.items()}
+    own_dtype = W.SPECS[args.config].kv_dtype
+    kv_dtype = own_dtype if args.kv_dtype is None else dtype_of[args.kv_dtype]
+    wl = W.make(args.config, kv_dtype=kv_dtype)
     sh = wl.shape
     st = wl.steps[0] if wl.steps else None
     lens_np = st.seq_lens if st else wl.seq_lens
@@ -318,7 +323,8 @@ def main():
             L = int(lens_np[b])
             n_pages = (L + P - 1) // P
             phys = torch.from_numpy(wl.block_table[b, :n_pages].astype(np.int64)).to(dev)
-            kt = first.k_pool[phys, h].float().reshape(-1, D)[:L].double().cpu().numpy()
+            kt = W.storage_to_f32(WD.kv_numpy(first.k_pool[phys, h].reshape(-1, D)[:L],
+                                              sh.kv_dtype), sh.kv_dtype).astype(np.float64)
             page_of = np.arange(L) // P
             keep = np.zeros(n_pages, dtype=bool)
             keep[sel_np[b, h, :cnt_np[b, h]]] = True
@@ -360,7 +366,8 @@ def main():
     value = B * Hq / (ms_step * 1e-3)
     step_gbs = nb["total"] / (ms_step * 1e-3) / 1e9
     src = source_hash()
-    tr = TRAFFIC.get(args.config)
+    tkey = args.config if kv_dtype == own_dtype else f"{args.config}:{W.DTYPE_NAMES[kv_dtype]}"
+    tr = TRAFFIC.get(tkey)
     traffic = tr["bytes_per_step"] if tr and tr["source"] == src else None
     kernel = {1: "k_step (append, score, select, decode of every row)",
               2: "k_step + k_merge (rows spread over several workgroups, then merged)"}.get(
@@ -378,7 +385,9 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": f"{args.config}: {DESCR[args.config]}", "kv_dtype":
+        "config": {"workload": f"{args.config}: {DESCR[args.config]}" + (
+                       "" if kv_dtype == own_dtype
+                       else f" (KV stored as {W.DTYPE_NAMES[kv_dtype]} instead)"), "kv_dtype":
                    W.DTYPE_NAMES[sh.kv_dtype], "batch": B, "q_heads": Hq, "kv_heads": Hkv,
                    "head_dim": D, "page_size": sh.page_size, "k_max": k_max,
                    "rotating_instances": R, "graph": not args.eager},

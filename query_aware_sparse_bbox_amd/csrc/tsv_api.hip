@@ -23,7 +23,8 @@ int check_shape(const tsv_shape* s, Dims* d) {
     return TSV_ERR_INVALID_ARG;
   if (s->num_q_heads % s->num_kv_heads) return TSV_ERR_INVALID_ARG;
   const int G = s->num_q_heads / s->num_kv_heads;
-  if (s->kv_dtype != TSV_F32 && s->kv_dtype != TSV_F16 && s->kv_dtype != TSV_BF16)
+  if (s->kv_dtype != TSV_F32 && s->kv_dtype != TSV_F16 && s->kv_dtype != TSV_BF16 &&
+      s->kv_dtype != TSV_FP8_E4M3)
     return TSV_ERR_UNSUPPORTED;
   if (s->head_dim != 64 && s->head_dim != 128) return TSV_ERR_UNSUPPORTED;
   if (s->page_size != 8 && s->page_size != 16 && s->page_size != 32 &&
@@ -46,7 +47,7 @@ int check_shape(const tsv_shape* s, Dims* d) {
   return TSV_OK;
 }
 
-size_t elem_bytes(const Dims& d) { return d.dt == TSV_F32 ? 4 : 2; }
+size_t elem_bytes(const Dims& d) { return (size_t)tsv::kv_bytes(d.dt); }
 
 int check_workspace(const Dims& d, int32_t k_max, const void* ws, size_t ws_bytes) {
   if (!ws || !aligned(ws, 256)) return TSV_ERR_INVALID_ARG;

@@ -32,18 +32,41 @@ constexpr int kMaxTilesPerSplit = 8;  // decode tiles one workgroup streams
 
 template <int DT>
 struct KV {
-  static constexpr int bytes = DT == DT_F32 ? 4 : 2;
-  static constexpr int per16 = 16 / bytes;  // elements in one 16-byte load
+  static constexpr int bytes = kv_bytes(DT);
+  static constexpr int vec = kv_vec(DT);  // elements of one lane load
 };
 
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ uint4 ld16(const void* p) {
   return *reinterpret_cast<const uint4*>(p);
 }
 
-// Widen one 16-byte load of KV-dtype elements to fp32 (exact).
-template <int DT>
+// One lane load of LB = 8 or 16 bytes (8 bytes land in .x/.y).
+template <int LB>
+__device__ __forceinline__ uint4 ldb(const void* p) {
+  static_assert(LB == 8 || LB == 16, "lane loads are 8 or 16 bytes");
+  if constexpr (LB == 8) {
+    const uint2 x = *reinterpret_cast<const uint2*>(p);
+    return make_uint4(x.x, x.y, 0u, 0u);
+  } else {
+    return ld16(p);
+  }
+}
+
+// Four OCP E4M3 values (bytes 0..3 of w) widened to fp32, exactly.
+__device__ __forceinline__ void fp8x4_to_f32(uint32_t w, float* f) {
+  const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+  const f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
+  f[0] = a.x;
+  f[1] = a.y;
+  f[2] = b.x;
+  f[3] = b.y;
+}
+
+// Widen one lane load of C elements to fp32 (exact).
+template <int DT, int C = KV<DT>::vec>
 __device__ __forceinline__ void unpack(const uint4 r, float* f) {
   const uint32_t w[4] = {r.x, r.y, r.z, r.w};
   if constexpr (DT == DT_F32) {
@@ -55,6 +78,9 @@ __device__ __forceinline__ void unpack(const uint4 r, float* f) {
       f[2 * i] = __uint_as_float(w[i] << 16);
       f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
     }
+  } else if constexpr (DT == DT_F8) {
+#pragma unroll
+    for (int i = 0; i < C / 4; ++i) fp8x4_to_f32(w[i], f + 4 * i);
   } else {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -69,18 +95,21 @@ template <int DT>
 __device__ __forceinline__ float elem_to_f32(uint32_t bits) {
   if constexpr (DT == DT_F32) return __uint_as_float(bits);
   else if constexpr (DT == DT_BF16) return __uint_as_float(bits << 16);
+  else if constexpr (DT == DT_F8) return __builtin_amdgcn_cvt_f32_fp8((int)bits, 0);
   else return (float)__builtin_bit_cast(_Float16, (uint16_t)bits);
 }
 
 template <int DT>
 __device__ __forceinline__ uint32_t load_elem(const void* base, size_t i) {
   if constexpr (DT == DT_F32) return reinterpret_cast<const uint32_t*>(base)[i];
+  else if constexpr (DT == DT_F8) return reinterpret_cast<const uint8_t*>(base)[i];
   else return reinterpret_cast<const uint16_t*>(base)[i];
 }
 
 template <int DT>
 __device__ __forceinline__ void store_elem(void* base, size_t i, uint32_t bits) {
   if constexpr (DT == DT_F32) reinterpret_cast<uint32_t*>(base)[i] = bits;
+  else if constexpr (DT == DT_F8) reinterpret_cast<uint8_t*>(base)[i] = (uint8_t)bits;
   else reinterpret_cast<uint16_t*>(base)[i] = (uint16_t)bits;
 }
 
@@ -282,7 +311,7 @@ constexpr int score_threads() { return G <= 1 ? 1024 : 512; }
 
 template <int DT, int D, int G, int NTH>
 struct ScoreCfg {
-  static constexpr int EB = KV<DT>::bytes, C = KV<DT>::per16, L = D / C;
+  static constexpr int EB = KV<DT>::bytes, C = KV<DT>::vec, L = D / C;
   static constexpr int PPW = kWave / L;  // pages per wave per load
   static constexpr int U = G >= 4 ? 1 : 4;  // rows per lane per batch
   static constexpr int NT = NTH, NW = NT / kWave;
@@ -529,8 +558,8 @@ __device__ __forceinline__ void score_pages(const float* __restrict__ q,
     for (int u = 0; u < U; ++u) {
       const int p = min(bi * PB + u * (NW * PPW) + wave * PPW + slot, n - 1);
       const size_t row = ((size_t)s_phys[p] * Hkv + h) * 2 * D + chunk * C;
-      mn[u] = ld16(mb + row * EB);
-      mx[u] = ld16(mb + (row + D) * EB);
+      mn[u] = ldb<C * EB>(mb + row * EB);
+      mx[u] = ldb<C * EB>(mb + (row + D) * EB);
     }
   };
   auto score_batch = [&](int bi, const uint4 (&rmn)[U], const uint4 (&rmx)[U]) {
@@ -538,8 +567,8 @@ __device__ __forceinline__ void score_pages(const float* __restrict__ q,
     for (int u = 0; u < U; ++u) {
       const int p = bi * PB + u * (NW * PPW) + wave * PPW + slot;
       float mn[C], mx[C];
-      unpack<DT>(rmn[u], mn);
-      unpack<DT>(rmx[u], mx);
+      unpack<DT, C>(rmn[u], mn);
+      unpack<DT, C>(rmx[u], mx);
       float best = 0.f;
 #pragma unroll
       for (int g = 0; g < G; ++g) {
@@ -906,7 +935,7 @@ __device__ __forceinline__ long uniform64(long x) {
 }
 
 // The 16 stream tokens [tw, tw + 16) of one MFMA wave step (tw a multiple of
-// 16, 16-bit KV) lie in one list entry when P >= 16 and in two consecutive
+// 16, EB-byte KV elements) lie in one list entry when P >= 16 and in two consecutive
 // entries when P == 8.  Wave-uniform: token t < split sits at k0/v0 + t*D
 // elements and exists if t < lim0; token t >= split at k1/v1 + (t-split)*D,
 // existing if t - split < lim1.  Slots that do not exist are still inside
@@ -916,6 +945,7 @@ struct StepMap {
   int split, lim0, lim1;
 };
 
+template <int EB>
 __device__ __forceinline__ StepMap step_map(const TokenList& tl, const char* kb, const char* vb,
                                             long tw) {
   const int P = 1 << tl.log2P;
@@ -927,7 +957,7 @@ __device__ __forceinline__ StepMap step_map(const TokenList& tl, const char* kb,
   const int l0 = uniform(tl.lp[ec]);
   const int p0 = uniform((int)tl.ph[ec]);
   m.lim0 = uniform(e < tl.npg && l0 >= 0 ? clampi(tl.len - (l0 * P + st0), 0, m.split) : 0);
-  const size_t b0 = ((((size_t)p0 * tl.Hkv + tl.h) << tl.log2P) + st0) * tl.D * 2;
+  const size_t b0 = ((((size_t)p0 * tl.Hkv + tl.h) << tl.log2P) + st0) * tl.D * EB;
   m.k0 = kb + b0;
   m.v0 = vb + b0;
   m.lim1 = 0;
@@ -938,7 +968,7 @@ __device__ __forceinline__ StepMap step_map(const TokenList& tl, const char* kb,
     const int l1 = uniform(tl.lp[ec1]);
     const int p1 = uniform((int)tl.ph[ec1]);
     m.lim1 = uniform(e + 1 < tl.npg && l1 >= 0 ? clampi(tl.len - l1 * P, 0, 16 - m.split) : 0);
-    const size_t b1 = (((size_t)p1 * tl.Hkv + tl.h) << tl.log2P) * tl.D * 2;
+    const size_t b1 = (((size_t)p1 * tl.Hkv + tl.h) << tl.log2P) * tl.D * EB;
     m.k1 = kb + b1;
     m.v1 = vb + b1;
   }
@@ -952,7 +982,7 @@ __device__ __forceinline__ StepMap step_map(const TokenList& tl, const char* kb,
 // barrier).
 template <int DT, int D, int G, int NT>
 struct ValuDecode {
-  static constexpr int EB = KV<DT>::bytes, C = KV<DT>::per16, L = D / C;
+  static constexpr int EB = KV<DT>::bytes, C = KV<DT>::vec, L = D / C;
   // loads in flight per lane and buffer: 16-wave workgroups hold half as many
   static constexpr int SPW = kWave / L, NW = NT / kWave, TPI = NW * SPW, J = NT >= 1024 ? 2 : 4;
   static constexpr int TILE = J * TPI;
@@ -992,8 +1022,8 @@ __device__ __forceinline__ void valu_decode_range(const float* __restrict__ qg0,
       const long o = tl.off(ts);
       ok[j] = o >= 0 && ts < t_end;  // the list may go on past this range
       const long off = ok[j] ? o + chunk * C : safe_off;
-      kr[j] = ld16(kb + off * EB);
-      vr[j] = ld16(vb + off * EB);
+      kr[j] = ldb<C * EB>(kb + off * EB);
+      vr[j] = ldb<C * EB>(vb + off * EB);
     }
   };
   float m_run[G], l_run[G], acc[G][C];
@@ -1009,7 +1039,7 @@ __device__ __forceinline__ void valu_decode_range(const float* __restrict__ qg0,
 #pragma unroll
     for (int j = 0; j < J; ++j) {
       float kf[C];
-      unpack<DT>(kr[j], kf);
+      unpack<DT, C>(kr[j], kf);
 #pragma unroll
       for (int g = 0; g < G; ++g) {
         float a = 0.f;
@@ -1036,7 +1066,7 @@ __device__ __forceinline__ void valu_decode_range(const float* __restrict__ qg0,
 #pragma unroll
     for (int j = 0; j < J; ++j) {
       float vf[C];
-      unpack<DT>(ok[j] ? vr[j] : make_uint4(0, 0, 0, 0), vf);
+      unpack<DT, C>(ok[j] ? vr[j] : make_uint4(0, 0, 0, 0), vf);
 #pragma unroll
       for (int g = 0; g < G; ++g) {
         const float pz = __builtin_amdgcn_exp2f(z[g][j] - ms[g]);
@@ -1206,6 +1236,14 @@ struct Mma<DT_F16> {
   static __device__ __forceinline__ short bits(elem x) { return __builtin_bit_cast(short, x); }
 };
 
+// Two OCP E4M3 values (bytes 0, 1 of w, or 2, 3 with HI) as a bf16 pair,
+// low half first, in one conversion (scale 1).  Exact: every E4M3 value is
+// a bf16 value.
+template <bool HI>
+__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w, 1.0f, HI));
+}
+
 template <int DT>
 __device__ __forceinline__ void split_hi_lo(float x, typename Mma<DT>::elem& hi,
                                             typename Mma<DT>::elem& lo) {
@@ -1227,7 +1265,8 @@ struct MfmaDecode {
 // one chunk ahead of the arithmetic, and the running softmax state is
 // rescaled once per chunk.  Page lookups are wave-uniform (scalar), each
 // lane keeps one K and one V address per step.  Ends with each wave's state
-// in s_acc[wave] / s_mw[wave] (no barrier).
+// in s_acc[wave] / s_mw[wave] (no barrier).  fp8 KV is widened to bf16 in
+// registers (exactly) and takes the bf16 instructions.
 template <int DT, int D, int G, int NW, int CH>
 __device__ __forceinline__ void mfma_decode_range(const float* __restrict__ qg0,
                                                   const char* __restrict__ kb,
@@ -1235,13 +1274,17 @@ __device__ __forceinline__ void mfma_decode_range(const float* __restrict__ qg0,
                                                   const TokenList& tl, long t0, long t_end,
                                                   float qscale, float (*s_acc)[G][D + 1],
                                                   float (*s_mw)[G]) {
-  using M = Mma<DT>;
+  constexpr int MDT = DT == DT_F8 ? DT_BF16 : DT;  // MFMA operand type
+  constexpr int EB = KV<DT>::bytes;
+  using M = Mma<MDT>;
   using MD = MfmaDecode<DT, D>;
   using vec8 = typename M::vec8;
   using vec4 = typename M::vec4;
   using E = typename M::elem;
   constexpr int WS = MD::WS, NCH = MD::NCH, NDT = MD::NDT;
-  constexpr int VW = D / 32;  // dwords of V per token and lane (W = 2*VW channels)
+  constexpr int VW = D / 32;  // bf16/f16 dwords of V per token and lane (W = 2*VW channels)
+  constexpr int VR = VW * EB / 2;  // dwords of V as loaded
+  using KRaw = std::conditional_t<EB == 1, uint2, uint4>;  // 8 channels of K as loaded
   static_assert(G <= 8, "hi and lo parts of the group share one 16-row fragment");
   const int lane = threadIdx.x & (kWave - 1), wave = uniform(threadIdx.x / kWave);
   const int n16 = lane & 15, c4 = lane >> 4;
@@ -1261,7 +1304,7 @@ __device__ __forceinline__ void mfma_decode_range(const float* __restrict__ qg0,
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         E hi, lo;
-        split_hi_lo<DT>(has ? xs[j] : 0.f, hi, lo);
+        split_hi_lo<MDT>(has ? xs[j] : 0.f, hi, lo);
         qf[ch][j] = lo_part ? lo : hi;
       }
     }
@@ -1270,11 +1313,11 @@ __device__ __forceinline__ void mfma_decode_range(const float* __restrict__ qg0,
   const int mine = nsteps > wave ? (nsteps - wave + NW - 1) / NW : 0;
   // per-lane byte offsets: K row n16 (8 channels at 8*c4), V rows 4*c4 .. +3
   // (W channels at W*n16)
-  const int k_lane = (n16 * D + 8 * c4) * 2;
-  const int v_lane = 2 * VW * n16 * 2;
+  const int k_lane = (n16 * D + 8 * c4) * EB;
+  const int v_lane = 2 * VW * n16 * EB;
   struct Chunk {
-    uint4 k[CH][NCH];          // token n16, channels 32*ch + 8*c4 .. + 7
-    uint32_t v[CH][4][VW];     // token 4*c4 + j, channels W*n16 .. W*n16 + W-1
+    KRaw k[CH][NCH];           // token n16, channels 32*ch + 8*c4 .. + 7
+    uint32_t v[CH][4][VR];     // token 4*c4 + j, channels W*n16 .. W*n16 + W-1
     int vlim[CH];              // tokens 4*c4 + j with j < vlim exist
   };
   // the chunk of the wave's steps i0 .. i0+CH-1 (clamped to its last step,
@@ -1283,22 +1326,26 @@ __device__ __forceinline__ void mfma_decode_range(const float* __restrict__ qg0,
 #pragma unroll
     for (int cc = 0; cc < CH; ++cc) {
       const int i = min(i0 + cc, mine - 1);
-      const StepMap sm = step_map(tl, kb, vb, t0 + (long)(wave + i * NW) * WS);
-      const char* kp = n16 < sm.split ? sm.k0 + k_lane : sm.k1 + (k_lane - sm.split * D * 2);
+      const StepMap sm = step_map<EB>(tl, kb, vb, t0 + (long)(wave + i * NW) * WS);
+      const char* kp = n16 < sm.split ? sm.k0 + k_lane : sm.k1 + (k_lane - sm.split * D * EB);
 #pragma unroll
-      for (int ch = 0; ch < NCH; ++ch) c.k[cc][ch] = ld16(kp + 64 * ch);
+      for (int ch = 0; ch < NCH; ++ch)
+        c.k[cc][ch] = *reinterpret_cast<const KRaw*>(kp + 32 * EB * ch);
       const bool first = 4 * c4 < sm.split;
-      const char* vp = (first ? sm.v0 : sm.v1 - sm.split * D * 2) + 4 * c4 * D * 2 + v_lane;
+      const char* vp = (first ? sm.v0 : sm.v1 - sm.split * D * EB) + 4 * c4 * D * EB + v_lane;
       c.vlim[cc] = i0 + cc < mine ? (first ? sm.lim0 - 4 * c4 : sm.lim1 - (4 * c4 - sm.split))
                                   : 0;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        if constexpr (VW == 2) {
-          const uint2 x = *reinterpret_cast<const uint2*>(vp + j * D * 2);
+        const char* vj = vp + j * D * EB;
+        if constexpr (VR == 1) {
+          c.v[cc][j][0] = *reinterpret_cast<const uint32_t*>(vj);
+        } else if constexpr (VR == 2) {
+          const uint2 x = *reinterpret_cast<const uint2*>(vj);
           c.v[cc][j][0] = x.x;
           c.v[cc][j][1] = x.y;
         } else {
-          const uint4 x = ld16(vp + j * D * 2);
+          const uint4 x = ld16(vj);
           c.v[cc][j][0] = x.x;
           c.v[cc][j][1] = x.y;
           c.v[cc][j][2] = x.z;
@@ -1322,8 +1369,16 @@ __device__ __forceinline__ void mfma_decode_range(const float* __restrict__ qg0,
       if (i0 + cc >= mine) continue;  // padding of the wave's last chunk
       f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ch = 0; ch < NCH; ++ch)
-        acc = M::mma32(__builtin_bit_cast(vec8, c.k[cc][ch]), qf[ch], acc);
+      for (int ch = 0; ch < NCH; ++ch) {
+        if constexpr (EB == 1) {
+          const KRaw r = c.k[cc][ch];
+          const uint4 kw = {fp8x2_to_bf16x2<false>(r.x), fp8x2_to_bf16x2<true>(r.x),
+                            fp8x2_to_bf16x2<false>(r.y), fp8x2_to_bf16x2<true>(r.y)};
+          acc = M::mma32(__builtin_bit_cast(vec8, kw), qf[ch], acc);
+        } else {
+          acc = M::mma32(__builtin_bit_cast(vec8, c.k[cc][ch]), qf[ch], acc);
+        }
+      }
       const int lim = has ? c.vlim[cc] : 0;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -1364,8 +1419,8 @@ __device__ __forceinline__ void mfma_decode_range(const float* __restrict__ qg0,
         const float pz = __builtin_amdgcn_exp2f(z[cc][r] - ms);
         l_run += pz;
         E hi, lo;
-        split_hi_lo<DT>(pz * M::kPScale, hi, lo);
-        if constexpr (DT == DT_BF16) pa[r] = M::bits(lo_part ? lo : hi);
+        split_hi_lo<MDT>(pz * M::kPScale, hi, lo);
+        if constexpr (MDT == DT_BF16) pa[r] = M::bits(lo_part ? lo : hi);
         else pa[r] = lo_part ? lo : hi;
       }
       // V of tokens that do not exist is zeroed (their slots may hold
@@ -1374,7 +1429,15 @@ __device__ __forceinline__ void mfma_decode_range(const float* __restrict__ qg0,
 #pragma unroll
       for (int j = 0; j < 4; ++j)
 #pragma unroll
-        for (int x = 0; x < VW; ++x) w[j][x] = j < c.vlim[cc] ? c.v[cc][j][x] : 0u;
+        for (int x = 0; x < VR; ++x) {
+          const uint32_t raw = j < c.vlim[cc] ? c.v[cc][j][x] : 0u;
+          if constexpr (EB == 1) {
+            w[j][2 * x] = fp8x2_to_bf16x2<false>(raw);
+            w[j][2 * x + 1] = fp8x2_to_bf16x2<true>(raw);
+          } else {
+            w[j][x] = raw;
+          }
+        }
 #pragma unroll
       for (int e = 0; e < NDT; ++e) {
         // channel W*n16 + e of tokens 4*c4 + 0..3: the low (e even) or high
@@ -1623,6 +1686,7 @@ hipError_t by_dtype(int dt, Fn&& fn) {
     case DT_F32: return fn(IC<DT_F32>{});
     case DT_F16: return fn(IC<DT_F16>{});
     case DT_BF16: return fn(IC<DT_BF16>{});
+    case DT_F8: return fn(IC<DT_F8>{});
   }
   return hipErrorInvalidValue;
 }
@@ -1667,8 +1731,7 @@ bool use_mfma_decode(const Dims& d) {
 
 int decode_tile_tokens(const Dims& d) {
   if (use_mfma_decode(d)) return 64;
-  const int bytes = d.dt == DT_F32 ? 4 : 2;
-  const int C = 16 / bytes, L = d.D / C, SPW = kWave / L;
+  const int C = kv_vec(d.dt), L = d.D / C, SPW = kWave / L;
   return 4 * (kDecodeThreads / kWave) * SPW;
 }
 

@@ -7,7 +7,13 @@
 
 namespace tsv {
 
-enum : int { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2 };
+enum : int { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2, DT_F8 = 3 };
+
+// Bytes of one KV element.
+constexpr int kv_bytes(int dt) { return dt == DT_F32 ? 4 : dt == DT_F8 ? 1 : 2; }
+// Consecutive channels of one row a lane loads at once: one 16-byte load, or
+// 8 bytes for fp8 (so a lane holds as many channels as for 16-bit data).
+constexpr int kv_vec(int dt) { return dt == DT_F8 ? 8 : 16 / kv_bytes(dt); }
 
 // Validated sizes of one call.
 struct Dims {

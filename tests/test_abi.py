@@ -76,6 +76,8 @@ def test_sizes(tsv):
     s = shape()
     assert tsv.tsv_meta_bytes(s) == 20 * 2 * 2 * 64 * 2
     assert tsv.tsv_meta_bytes(shape(kv_dtype=0)) == 20 * 2 * 2 * 64 * 4
+    assert tsv.tsv_meta_bytes(shape(kv_dtype=3)) == 20 * 2 * 2 * 64 * 1  # fp8 E4M3
+    assert tsv.tsv_meta_bytes(shape(kv_dtype=4)) == 0
     ws = tsv.tsv_workspace_bytes(s, 8)
     assert ws > 0 and ws % 256 == 0
     assert tsv.tsv_workspace_bytes(s, 16) >= ws
@@ -103,7 +105,7 @@ def test_decode_step_launch_plan(tsv):
 
 @pytest.mark.parametrize("kw,status", [
     (dict(head_dim=96), -2), (dict(head_dim=32), -2), (dict(page_size=12), -2),
-    (dict(kv_dtype=7), -2), (dict(num_q_heads=24, num_kv_heads=8), -2),  # G = 3
+    (dict(kv_dtype=7), -2), (dict(kv_dtype=-1), -2), (dict(num_q_heads=24, num_kv_heads=8), -2),  # G = 3
     (dict(num_q_heads=7), -1), (dict(batch=0), -1), (dict(num_phys_pages=0), -1),
     (dict(max_pages_per_seq=5000), -2),
 ])

@@ -2,7 +2,8 @@
 
 Bars: page boxes equal by value, page scores bit-equal (-0 stored as +0),
 selections and counts bit-exact, outputs within max-abs 1e-5 (fp32 KV) or
-2e-3 (fp16 / bf16 KV).  The five decode configurations run at their full
+2e-3 (fp16 / bf16 / fp8 KV: the stored values are exact in every path, the
+tolerance covers the attention arithmetic).  The five decode configurations run at their full
 sizes in the launch configuration the benchmark times; smaller variants add
 ragged tails, several tiles per row and the method's degenerate cases.
 """
@@ -32,6 +33,13 @@ def test_full_config(name):
     _case(wl)
 
 
+@pytest.mark.parametrize("name", ["tinyllama", "llama_long", "ragged"])
+def test_full_config_fp8(name):
+    """The same full-size steps with the KV cache stored as fp8 E4M3."""
+    wl = W.make(name, kv_dtype=W.F8)
+    _case(wl)
+
+
 @pytest.mark.parametrize("name,kw", [
     ("tiny", dict(context=1000)),
     ("tiny", dict(context=17, kv_dtype=W.BF16)),
@@ -44,13 +52,21 @@ def test_full_config(name):
     ("llama_long", dict(batch=2, context=3000, page_size=8)),
     ("ragged", dict(batch=8, lens_range=(1, 3000))),
     ("ragged", dict(batch=6, lens_range=(100, 2000), kv_dtype=W.BF16, num_q_heads=64)),
+    # fp8 E4M3 KV: MFMA decode (G = 8, 4), VALU decode (G = 1, 2), 8-token pages
+    ("tinyllama", dict(batch=3, context=1001, kv_dtype=W.F8)),
+    ("tinyllama", dict(batch=2, context=333, num_q_heads=8, num_kv_heads=4, kv_dtype=W.F8)),
+    ("tinyllama", dict(batch=2, context=777, page_size=8, kv_dtype=W.F8)),
+    ("gpt2", dict(batch=3, context=500, kv_dtype=W.F8)),
+    ("gpt2", dict(batch=2, context=700, head_dim=128, kv_dtype=W.F8)),
+    ("ragged", dict(batch=6, lens_range=(100, 2000), kv_dtype=W.F8)),
+    ("ragged", dict(batch=4, lens_range=(1, 1500), kv_dtype=W.F8, num_q_heads=64)),
 ])
 def test_small_variants(name, kw):
     wl = W.make(name, **kw)
     _case(wl)
 
 
-@pytest.mark.parametrize("dtype", [W.F32, W.F16, W.BF16])
+@pytest.mark.parametrize("dtype", [W.F32, W.F16, W.BF16, W.F8])
 @pytest.mark.parametrize("G", [1, 4])
 def test_tie_heavy(dtype, G):
     wl = W.tie_heavy(31 + G, kv_dtype=dtype, num_q_heads=2 * G, num_kv_heads=2, context=777,
@@ -63,7 +79,9 @@ def test_tie_heavy(dtype, G):
 
 def test_poisoned_unused_slots():
     for name, kw in [("gpt2", dict(batch=4, context=301)),
-                     ("ragged", dict(batch=8, lens_range=(5, 900)))]:
+                     ("ragged", dict(batch=8, lens_range=(5, 900))),
+                     ("tinyllama", dict(batch=3, context=333, kv_dtype=W.F8)),
+                     ("gpt2", dict(batch=3, context=250, kv_dtype=W.F8))]:
         wl = W.make(name, **kw)
         W.poison_unused(wl)
         g, _ = _case(wl)
@@ -85,7 +103,9 @@ def test_three_calls_equal_fused_step():
 
     for name, kw in [("ragged", dict(batch=8, lens_range=(100, 4000))),
                      ("tinyllama", dict(batch=4, context=2000)),
-                     ("llama_long", dict(batch=2, context=6000))]:
+                     ("llama_long", dict(batch=2, context=6000)),
+                     ("ragged", dict(batch=4, lens_range=(100, 3000), kv_dtype=W.F8)),
+                     ("gpt2", dict(batch=4, context=600, kv_dtype=W.F8))]:
         wl = W.make(name, **kw)
         say(f"[case] three calls vs one step: {name} {kw} launches="
             f"{T.tsv_decode_step_launches(wl.shape, wl.k_max, bool(wl.steps))}")
@@ -215,7 +235,8 @@ def test_permuted_pool_same_selection():
     assert np.array_equal(ga["out"].view(np.uint32), gb["out"].view(np.uint32))
 
 
-def test_ragged_appends_seventeen_steps():
+@pytest.mark.parametrize("kw", [dict(batch=16), dict(batch=8, kv_dtype=W.F8)])
+def test_ragged_appends_seventeen_steps(kw):
     """17 consecutive appends cover every slot residue mod 16 and page opens."""
     import torch
 
@@ -223,7 +244,7 @@ def test_ragged_appends_seventeen_steps():
     import query_aware_sparse_bbox_amd as T
     from workloads import device as WD
 
-    wl = W.make("ragged", batch=16, append_steps=17)
+    wl = W.make("ragged", append_steps=17, **kw)
     sh = wl.shape
     say(f"[case] ragged appends shape={sh}")
     d = WD.upload(wl)
