@@ -39,12 +39,12 @@ def _load():
         sig = {
             "tsvo_meta_build": [P, P, P, P, P],
             "tsvo_meta_append": [P, P, P, P, P, P, P, P],
-            "tsvo_page_scores": [P, P, P, P, P, P],
-            "tsvo_select_from_scores": [P, P, P, I, P, I, P, P],
-            "tsvo_select_pages": [P, P, P, P, P, I, P, I, P, P, P],
+            "tsvo_page_scores": [P, P, P, P, P, I, P],
+            "tsvo_select_from_scores": [P, P, P, I, P, I, I, P, P],
+            "tsvo_select_pages": [P, P, P, P, P, I, P, I, I, I, P, P, P],
             "tsvo_sparse_decode": [P, P, P, P, P, P, P, P, I, ctypes.c_float, P],
-            "tsvo_decode_step": [P, P, P, P, P, P, P, P, P, I, P, I, ctypes.c_float,
-                                 P, P, P, P],
+            "tsvo_decode_step": [P, P, P, P, P, P, P, P, P, I, P, I, I, I,
+                                 ctypes.c_float, P, P, P, P],
         }
         for name, args in sig.items():
             f = getattr(lib, name)
@@ -52,6 +52,10 @@ def _load():
             f.restype = ctypes.c_int
         _lib = lib
     return _lib
+
+
+# how the G query heads of a KV head combine into the page score
+AGG_MAX, AGG_SUM = 0, 1
 
 
 def shape_of(sh) -> Shape:
@@ -97,28 +101,31 @@ def meta_append(sh, k_new, v_new, k_pool, v_pool, meta, block_table, seq_lens):
            "tsvo_meta_append")
 
 
-def page_scores(sh, q, meta, block_table, seq_lens):
-    """Score of every page (upper bound of q.k over its box), [B][Hkv][MP]; NaN past n_b."""
+def page_scores(sh, q, meta, block_table, seq_lens, group_agg=AGG_MAX):
+    """Score of every page (upper bound of q.k over its box, combined over the
+    group's query heads by max or sum), [B][Hkv][MP]; NaN past n_b."""
     sc = np.full((sh.batch, sh.num_kv_heads, sh.max_pages_per_seq), np.nan, dtype=np.float32)
     q = np.ascontiguousarray(q, dtype=np.float32)
     bt, sl = _i32(block_table), _i32(seq_lens)
     _check(_load().tsvo_page_scores(ctypes.byref(shape_of(sh)), _p(q), _p(meta), _p(bt),
-                                    _p(sl), _p(sc)), "tsvo_page_scores")
+                                    _p(sl), group_agg, _p(sc)), "tsvo_page_scores")
     return sc
 
 
-def select_from_scores(sh, scores, seq_lens, k_max, k_per_seq=None, n_sink=0):
+def select_from_scores(sh, scores, seq_lens, k_max, k_per_seq=None, n_sink=0, n_recent=0):
     sel = np.empty((sh.batch, sh.num_kv_heads, k_max), dtype=np.int32)
     cnt = np.empty((sh.batch, sh.num_kv_heads), dtype=np.int32)
     scores = np.ascontiguousarray(scores, dtype=np.float32)
     sl, kp = _i32(seq_lens), _i32(k_per_seq)
     _check(_load().tsvo_select_from_scores(ctypes.byref(shape_of(sh)), _p(scores), _p(sl),
-                                           k_max, _p(kp), n_sink, _p(sel), _p(cnt)),
+                                           k_max, _p(kp), n_sink, n_recent, _p(sel),
+                                           _p(cnt)),
            "tsvo_select_from_scores")
     return sel, cnt
 
 
-def select_pages(sh, q, meta, block_table, seq_lens, k_max, k_per_seq=None, n_sink=0):
+def select_pages(sh, q, meta, block_table, seq_lens, k_max, k_per_seq=None, n_sink=0,
+                 n_recent=0, group_agg=AGG_MAX):
     """(sel, sel_count, scores) exactly as the selection rule defines them."""
     sel = np.empty((sh.batch, sh.num_kv_heads, k_max), dtype=np.int32)
     cnt = np.empty((sh.batch, sh.num_kv_heads), dtype=np.int32)
@@ -126,7 +133,8 @@ def select_pages(sh, q, meta, block_table, seq_lens, k_max, k_per_seq=None, n_si
     q = np.ascontiguousarray(q, dtype=np.float32)
     bt, sl, kp = _i32(block_table), _i32(seq_lens), _i32(k_per_seq)
     _check(_load().tsvo_select_pages(ctypes.byref(shape_of(sh)), _p(q), _p(meta), _p(bt),
-                                     _p(sl), k_max, _p(kp), n_sink, _p(sel), _p(cnt), _p(sc)),
+                                     _p(sl), k_max, _p(kp), n_sink, n_recent, group_agg,
+                                     _p(sel), _p(cnt), _p(sc)),
            "tsvo_select_pages")
     return sel, cnt, sc
 
@@ -145,7 +153,8 @@ def sparse_decode(sh, q, k_pool, v_pool, block_table, seq_lens, sel, sel_count, 
 
 
 def decode_step(sh, q, k_pool, v_pool, meta, block_table, seq_lens, k_max, scale,
-                k_per_seq=None, n_sink=0, k_new=None, v_new=None):
+                k_per_seq=None, n_sink=0, k_new=None, v_new=None, n_recent=0,
+                group_agg=AGG_MAX):
     """Append (if k_new is given), score, select and attend; pools/meta updated in place."""
     sel = np.empty((sh.batch, sh.num_kv_heads, k_max), dtype=np.int32)
     cnt = np.empty((sh.batch, sh.num_kv_heads), dtype=np.int32)
@@ -155,7 +164,8 @@ def decode_step(sh, q, k_pool, v_pool, meta, block_table, seq_lens, k_max, scale
     bt, sl, kp = _i32(block_table), _i32(seq_lens), _i32(k_per_seq)
     _check(_load().tsvo_decode_step(ctypes.byref(shape_of(sh)), _p(q), _p(k_new), _p(v_new),
                                     _p(k_pool), _p(v_pool), _p(meta), _p(bt), _p(sl), k_max,
-                                    _p(kp), n_sink, ctypes.c_float(scale), _p(sel), _p(cnt),
+                                    _p(kp), n_sink, n_recent, group_agg,
+                                    ctypes.c_float(scale), _p(sel), _p(cnt),
                                     _p(sc), _p(out)),
            "tsvo_decode_step")
     return sel, cnt, sc, out

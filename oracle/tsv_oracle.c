@@ -253,8 +253,9 @@ static float tree_sum(const float* t, int n) {
 
 int tsvo_page_scores(const tsvo_shape* s, const float* q, const void* meta,
                      const int32_t* bt, const int32_t* seq_lens,
-                     float* scores) {
+                     int32_t group_agg, float* scores) {
   if (!shape_ok(s) || !q || !meta || !bt || !seq_lens || !scores) return -1;
+  if (group_agg != TSVO_AGG_MAX && group_agg != TSVO_AGG_SUM) return -1;
   const int D = s->head_dim, G = s->num_q_heads / s->num_kv_heads;
   float* t = (float*)malloc(sizeof(float) * (size_t)D);
   if (!t) return -1;
@@ -265,7 +266,8 @@ int tsvo_page_scores(const tsvo_shape* s, const float* q, const void* meta,
         int64_t phys;
         if (!phys_of(s, bt, b, p, &phys)) { free(t); return -1; }
         float best = 0.0f;
-        for (int g = 0; g < G; ++g) {
+        for (int gi = 0; gi < G; ++gi) {
+          const int g = gi; /* query heads in increasing order */
           const float* qv = q + ((int64_t)b * s->num_q_heads + h * G + g) * D;
           for (int d = 0; d < D; ++d) {
             float mn = kv_get(meta, meta_idx(s, phys, h, 0, d), s->kv_dtype);
@@ -275,7 +277,10 @@ int tsvo_page_scores(const tsvo_shape* s, const float* q, const void* meta,
             t[d] = a > c ? a : c;
           }
           float sg = tree_sum(t, D);
-          if (g == 0 || sg > best) best = sg;
+          if (group_agg == TSVO_AGG_SUM)
+            best = gi == 0 ? sg : best + sg; /* fp32, one rounding per head */
+          else if (gi == 0 || sg > best)
+            best = sg;
         }
         if (best == 0.0f) best = 0.0f; /* -0 -> +0 */
         scores[((int64_t)b * s->num_kv_heads + h) * s->max_pages_per_seq + p] =
@@ -307,9 +312,11 @@ static int cand_cmp(const void* pa, const void* pb) {
 int tsvo_select_from_scores(const tsvo_shape* s, const float* scores,
                             const int32_t* seq_lens, int32_t k_max,
                             const int32_t* k_per_seq, int32_t n_sink,
-                            int32_t* sel, int32_t* sel_count) {
+                            int32_t n_recent, int32_t* sel, int32_t* sel_count) {
   if (!shape_ok(s) || !scores || !seq_lens || !sel || !sel_count) return -1;
-  if (k_max < 1 || n_sink < 0 || n_sink > k_max) return -1;
+  if (k_max < 1 || n_sink < 0 || n_recent < 0 || n_sink > k_max ||
+      n_recent > k_max - n_sink)
+    return -1;
   const int64_t MP = s->max_pages_per_seq;
   cand_t* cand = (cand_t*)malloc(sizeof(cand_t) * (size_t)MP);
   char* chosen = (char*)malloc((size_t)MP);
@@ -321,18 +328,20 @@ int tsvo_select_from_scores(const tsvo_shape* s, const float* scores,
     if (kb > k_max) kb = k_max;
     int64_t keff = kb < n ? kb : n;
     int64_t f = n_sink < keff ? n_sink : keff;
+    int64_t r = n_recent < keff - f ? n_recent : keff - f;
     for (int h = 0; h < s->num_kv_heads; ++h) {
       const float* row = scores + ((int64_t)b * s->num_kv_heads + h) * MP;
       memset(chosen, 0, (size_t)MP);
       for (int64_t p = 0; p < f; ++p) chosen[p] = 1; /* forced sink pages */
+      for (int64_t p = n - r; p < n; ++p) chosen[p] = 1; /* forced recent pages */
       int64_t nc = 0;
-      for (int64_t p = f; p < n; ++p) {
+      for (int64_t p = f; p < n - r; ++p) {
         cand[nc].score = row[p];
         cand[nc].page = (int32_t)p;
         ++nc;
       }
       qsort(cand, (size_t)nc, sizeof(cand_t), cand_cmp);
-      for (int64_t i = 0; i < keff - f; ++i) chosen[cand[i].page] = 1;
+      for (int64_t i = 0; i < keff - f - r; ++i) chosen[cand[i].page] = 1;
       int32_t* out = sel + ((int64_t)b * s->num_kv_heads + h) * k_max;
       int32_t c = 0;
       for (int64_t p = 0; p < n; ++p)
@@ -348,16 +357,17 @@ int tsvo_select_from_scores(const tsvo_shape* s, const float* scores,
 
 int tsvo_select_pages(const tsvo_shape* s, const float* q, const void* meta,
                       const int32_t* bt, const int32_t* seq_lens, int32_t k_max,
-                      const int32_t* k_per_seq, int32_t n_sink, int32_t* sel,
-                      int32_t* sel_count, float* scores_out) {
+                      const int32_t* k_per_seq, int32_t n_sink, int32_t n_recent,
+                      int32_t group_agg, int32_t* sel, int32_t* sel_count,
+                      float* scores_out) {
   if (!shape_ok(s)) return -1;
   size_t ns = (size_t)s->batch * s->num_kv_heads * s->max_pages_per_seq;
   float* sc = scores_out ? scores_out : (float*)malloc(sizeof(float) * ns);
   if (!sc) return -1;
-  int rc = tsvo_page_scores(s, q, meta, bt, seq_lens, sc);
+  int rc = tsvo_page_scores(s, q, meta, bt, seq_lens, group_agg, sc);
   if (rc == 0)
     rc = tsvo_select_from_scores(s, sc, seq_lens, k_max, k_per_seq, n_sink,
-                                 sel, sel_count);
+                                 n_recent, sel, sel_count);
   if (!scores_out) free(sc);
   return rc;
 }
@@ -437,16 +447,16 @@ int tsvo_sparse_decode(const tsvo_shape* s, const float* q, const void* k_pool,
 int tsvo_decode_step(const tsvo_shape* s, const float* q, const void* k_new,
                      const void* v_new, void* k_pool, void* v_pool, void* meta,
                      const int32_t* bt, const int32_t* seq_lens, int32_t k_max,
-                     const int32_t* k_per_seq, int32_t n_sink, float scale,
-                     int32_t* sel, int32_t* sel_count, float* scores_out,
-                     float* out) {
+                     const int32_t* k_per_seq, int32_t n_sink, int32_t n_recent,
+                     int32_t group_agg, float scale, int32_t* sel,
+                     int32_t* sel_count, float* scores_out, float* out) {
   int rc = 0;
   if (k_new || v_new) {
     rc = tsvo_meta_append(s, k_new, v_new, k_pool, v_pool, meta, bt, seq_lens);
     if (rc) return rc;
   }
   rc = tsvo_select_pages(s, q, meta, bt, seq_lens, k_max, k_per_seq, n_sink,
-                         sel, sel_count, scores_out);
+                         n_recent, group_agg, sel, sel_count, scores_out);
   if (rc) return rc;
   return tsvo_sparse_decode(s, q, k_pool, v_pool, bt, seq_lens, sel, sel_count,
                             k_max, scale, out);

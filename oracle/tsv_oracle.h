@@ -47,6 +47,17 @@ typedef struct {
   int32_t kv_dtype;
 } tsvo_shape;
 
+/* How the G query heads of a KV head combine their box bounds into the page
+ * score: the largest (TSVO_AGG_MAX) or their fp32 sum in increasing head
+ * order (TSVO_AGG_SUM). */
+enum { TSVO_AGG_MAX = 0, TSVO_AGG_SUM = 1 };
+
+/* Selection: with keff = min(K_b, n_b), the first f = min(n_sink, keff)
+ * pages (attention sinks) and the last r = min(n_recent, keff - f) pages
+ * (local window) are always kept; the remaining keff - f - r slots go to the
+ * highest-scoring pages in between (ties: lower logical page).
+ * n_sink + n_recent must not exceed k_max. */
+
 int tsvo_meta_build(const tsvo_shape* s, const void* k_pool, void* meta,
                     const int32_t* block_table, const int32_t* seq_lens);
 
@@ -56,17 +67,18 @@ int tsvo_meta_append(const tsvo_shape* s, const void* k_new, const void* v_new,
 
 int tsvo_page_scores(const tsvo_shape* s, const float* q, const void* meta,
                      const int32_t* block_table, const int32_t* seq_lens,
-                     float* scores);
+                     int32_t group_agg, float* scores);
 
 int tsvo_select_from_scores(const tsvo_shape* s, const float* scores,
                             const int32_t* seq_lens, int32_t k_max,
                             const int32_t* k_per_seq, int32_t n_sink,
-                            int32_t* sel, int32_t* sel_count);
+                            int32_t n_recent, int32_t* sel, int32_t* sel_count);
 
 int tsvo_select_pages(const tsvo_shape* s, const float* q, const void* meta,
                       const int32_t* block_table, const int32_t* seq_lens,
                       int32_t k_max, const int32_t* k_per_seq, int32_t n_sink,
-                      int32_t* sel, int32_t* sel_count, float* scores_out);
+                      int32_t n_recent, int32_t group_agg, int32_t* sel,
+                      int32_t* sel_count, float* scores_out);
 
 int tsvo_sparse_decode(const tsvo_shape* s, const float* q, const void* k_pool,
                        const void* v_pool, const int32_t* block_table,
@@ -78,8 +90,9 @@ int tsvo_decode_step(const tsvo_shape* s, const float* q, const void* k_new,
                      const void* v_new, void* k_pool, void* v_pool, void* meta,
                      const int32_t* block_table, const int32_t* seq_lens,
                      int32_t k_max, const int32_t* k_per_seq, int32_t n_sink,
-                     float scale, int32_t* sel, int32_t* sel_count,
-                     float* scores_out, float* out);
+                     int32_t n_recent, int32_t group_agg, float scale,
+                     int32_t* sel, int32_t* sel_count, float* scores_out,
+                     float* out);
 
 #ifdef __cplusplus
 }

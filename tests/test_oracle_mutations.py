@@ -24,7 +24,11 @@ MUTATIONS = [
      "float sg = tree_sum(t, D);",
      "float sg = 0.0f; for (int d = 0; d < D; ++d) sg += t[d];"),
     ("first query head of the group only",
-     "if (g == 0 || sg > best) best = sg;", "if (g == 0) best = sg;"),
+     "else if (gi == 0 || sg > best)", "else if (gi == 0)"),
+    ("group sum taken as the max",
+     "best = gi == 0 ? sg : best + sg;", "best = gi == 0 || sg > best ? sg : best;"),
+    ("group heads visited in decreasing order",
+     "const int g = gi;", "const int g = G - 1 - gi;"),
     ("score uses the box max for every channel",
      "float a = qv[d] * mn;", "float a = qv[d] * mx;"),
     ("ties go to the higher page",
@@ -34,8 +38,13 @@ MUTATIONS = [
      "for (int64_t p = 0; p < f; ++p) chosen[p] = 1; /* forced sink pages */",
      "f = 0;"),
     ("one page short of the budget",
-     "for (int64_t i = 0; i < keff - f; ++i) chosen[cand[i].page] = 1;",
-     "for (int64_t i = 0; i + 1 < keff - f; ++i) chosen[cand[i].page] = 1;"),
+     "for (int64_t i = 0; i < keff - f - r; ++i) chosen[cand[i].page] = 1;",
+     "for (int64_t i = 0; i + 1 < keff - f - r; ++i) chosen[cand[i].page] = 1;"),
+    ("recent window shifted one page back",
+     "for (int64_t p = n - r; p < n; ++p) chosen[p] = 1;",
+     "for (int64_t p = n - r - 1; p < n - 1; ++p) if (p >= 0) chosen[p] = 1;"),
+    ("recent pages not forced",
+     "for (int64_t p = n - r; p < n; ++p) chosen[p] = 1; /* forced recent pages */", ""),
     ("box ignores the last valid token",
      "for (int64_t t = 1; t < v; ++t) {", "for (int64_t t = 1; t < v - 1; ++t) {"),
     ("append never opens a new box",

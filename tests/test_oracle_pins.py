@@ -272,6 +272,64 @@ def test_integer_inputs_give_exact_scores():
                 assert sc[b, h, p] == exact
 
 
+def one_token_pages(qs, key):
+    """Score of a D = 1, one-token page whose key is `key` for G = len(qs)
+    query heads (q_g = qs[g]), under both group aggregations."""
+    G = len(qs)
+    sh = W.Shape(1, G, 1, 1, 1, 1, 1, W.F32)
+    kp = np.array([key], np.float32).reshape(1, 1, 1, 1)
+    bt = np.zeros((1, 1), np.int32)
+    lens = np.ones(1, np.int32)
+    meta = O.meta_build(sh, kp, bt, lens)
+    q = np.array(qs, np.float32).reshape(1, G, 1)
+    return [float(O.page_scores(sh, q, meta, bt, lens, agg)[0, 0, 0])
+            for agg in (O.AGG_MAX, O.AGG_SUM)]
+
+
+def test_group_sum_fixed_order():
+    """Sum over the group: fp32, heads in increasing order.  With per-head
+    scores (1, 1e8, -1e8) that order gives (1 + 1e8) - 1e8 = 0 (1e8 + 1 rounds
+    to 1e8), the reverse order 1, and the max 1e8."""
+    assert one_token_pages([1.0, 1e8, -1e8], 1.0) == [1e8, 0.0]
+    assert one_token_pages([-1e8, 1e8, 1.0], 1.0) == [1e8, 1.0]
+    assert one_token_pages([3.0, -5.0], 2.0) == [6.0, -4.0]
+
+
+def test_group_sum_is_sum_of_corner_maxima():
+    """Small-integer inputs: the sum-aggregated score is exactly the sum over
+    the group's heads of each head's box-corner maximum (brute force)."""
+    rng = np.random.default_rng(17)
+    D, G, P = 8, 4, 5
+    keys = rng.integers(-3, 4, size=(1, 1, 3 * P, D)).astype(np.float32)
+    q = rng.integers(-3, 4, size=(1, G, D)).astype(np.float32)
+    wl = make_wl(keys, keys, q, [3 * P], P)
+    sh = wl.shape
+    meta = O.meta_build(sh, wl.k_pool, wl.block_table, wl.seq_lens)
+    sc = O.page_scores(sh, wl.q, meta, wl.block_table, wl.seq_lens, O.AGG_SUM)
+    for p in range(3):
+        mn = meta[wl.block_table[0, p], 0, 0].astype(np.float64)
+        mx = meta[wl.block_table[0, p], 0, 1].astype(np.float64)
+        want = sum(corner_max(q[0, g], mn, mx) for g in range(G))
+        assert sc[0, 0, p] == want
+
+
+def test_group_sum_bounds_the_group_logit_sum():
+    """Sum aggregation bounds sum_g q_g.k for every key of the page."""
+    wl = W.make("tinyllama", batch=2, context=300)
+    sh = wl.shape
+    meta = O.meta_build(sh, wl.k_pool, wl.block_table, wl.seq_lens)
+    sc = O.page_scores(sh, wl.q, meta, wl.block_table, wl.seq_lens, O.AGG_SUM)
+    G, P = sh.group, sh.page_size
+    for b in range(sh.batch):
+        for h in range(sh.num_kv_heads):
+            qs = wl.q[b, h * G:(h + 1) * G].astype(np.float64).sum(axis=0)
+            for p in range(-(-300 // P)):
+                k = page_pool_rows(wl, b, h, p)
+                tight = (k @ qs).max()
+                slack = 1e-5 * np.abs(wl.q[b, h * G:(h + 1) * G]).sum() * np.abs(k).max() * 2
+                assert sc[b, h, p] >= tight - slack
+
+
 # ----------------------------------------------------------------------------
 # metadata
 # ----------------------------------------------------------------------------
@@ -324,12 +382,14 @@ def test_append_matches_rebuild():
 # selection
 # ----------------------------------------------------------------------------
 
-def brute_force_selection(scores, n, K, n_sink):
-    """All subsets: the one whose members all beat all other candidates."""
+def brute_force_selection(scores, n, K, n_sink, n_recent=0):
+    """All subsets: the one whose members all beat all other candidates
+    (sink pages first, then the most recent pages, are kept outright)."""
     keff = min(K, n)
     f = min(n_sink, keff)
-    cands = list(range(f, n))
-    r = keff - f
+    rec = min(n_recent, keff - f)
+    cands = list(range(f, n - rec))
+    r = keff - f - rec
 
     def beats(a, b):
         return scores[a] > scores[b] or (scores[a] == scores[b] and a < b)
@@ -338,23 +398,24 @@ def brute_force_selection(scores, n, K, n_sink):
     for sub in itertools.combinations(cands, r):
         s = set(sub)
         if all(beats(a, b) for a in s for b in cands if b not in s):
-            winners.append(sorted(list(range(f)) + list(sub)))
+            winners.append(sorted(list(range(f)) + list(sub) + list(range(n - rec, n))))
     return winners
 
 
 def test_selection_is_unique_dominant_subset():
     rng = np.random.default_rng(5)
-    for trial in range(300):
+    for trial in range(600):
         n = int(rng.integers(1, 10))
         K = int(rng.integers(1, 6))
         n_sink = int(rng.integers(0, min(K, 3) + 1))
+        n_recent = int(rng.integers(0, K - n_sink + 1)) if trial % 2 else 0
         P = 2
         sh = W.Shape(1, 1, 1, 4, P, 10, 10, W.F32)
         scores = np.full((1, 1, 10), np.nan, dtype=np.float32)
         scores[0, 0, :n] = rng.integers(-2, 3, size=n).astype(np.float32)  # many ties
         lens = np.array([n * P - int(rng.integers(0, P))], dtype=np.int32)
-        sel, cnt = O.select_from_scores(sh, scores, lens, K, None, n_sink)
-        winners = brute_force_selection(scores[0, 0], n, K, n_sink)
+        sel, cnt = O.select_from_scores(sh, scores, lens, K, None, n_sink, n_recent)
+        winners = brute_force_selection(scores[0, 0], n, K, n_sink, n_recent)
         assert len(winners) == 1
         got = sel[0, 0, :cnt[0, 0]].tolist()
         assert got == winners[0]
@@ -404,6 +465,27 @@ def test_sink_page_always_kept():
     sel, cnt = O.select_from_scores(sh, sc, wl.seq_lens, wl.k_max, None, 1)
     assert np.all(sel[:, :, 0] == 0)
     assert np.all(cnt == min(wl.k_max, -(-2000 // 32)))
+
+
+def test_recent_window_always_kept():
+    """Sinks first, then the local window, then the best pages in between;
+    K below sinks + window keeps the sinks and as much of the window as fits."""
+    sh = W.Shape(1, 1, 1, 4, 1, 12, 12, W.F32)
+    scores = np.array([[[5, 9, 1, 8, 2, 7, 3, 6, 0, 4, -1, -2]]], dtype=np.float32)
+    lens = np.array([12], dtype=np.int32)
+
+    def pick(K, n_sink, n_recent):   # row width 6, this row's budget K
+        sel, cnt = O.select_from_scores(sh, scores, lens, 6, np.array([K], np.int32),
+                                        n_sink, n_recent)
+        return sel[0, 0, :cnt[0, 0]].tolist()
+
+    assert pick(6, 1, 2) == [0, 1, 3, 5, 10, 11]   # sink 0, window 10-11, top-3 of 1..9
+    assert pick(3, 1, 2) == [0, 10, 11]
+    assert pick(2, 1, 2) == [0, 11]                # the budget cuts the window
+    assert pick(4, 0, 4) == [8, 9, 10, 11]
+    assert pick(5, 2, 3) == [0, 1, 9, 10, 11]
+    with pytest.raises(RuntimeError):               # sinks + window beyond the row width
+        O.select_from_scores(sh, scores, lens, 4, None, 2, 3)
 
 
 def test_budget_clamped_and_zero_length():
