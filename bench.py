@@ -115,6 +115,10 @@ def parse():
     ap.add_argument("--config", default=DEFAULT_CONFIG, choices=W.CONFIG_ORDER)
     ap.add_argument("--kv-dtype", default=None, choices=sorted(W.DTYPE_NAMES.values()),
                     help="store the KV cache in this type instead of the configuration's own")
+    ap.add_argument("--group-agg", default="max", choices=["max", "sum"],
+                    help="combine the G query heads' box bounds by max (default) or sum")
+    ap.add_argument("--recent", type=int, default=0,
+                    help="always keep the last N pages of every sequence (local window)")
     ap.add_argument("--rotate", type=int, default=0, help="pool copies (0: auto, >=512 MB)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="CPU-oracle baseline budget (0 disables it)")
@@ -195,9 +199,17 @@ def main():
         d.ws = T.new_workspace(sh, k_max, dev)
         return d
 
+    agg = {"max": T.TSV_AGG_MAX, "sum": T.TSV_AGG_SUM}[args.group_agg]
+    variant = args.recent != 0 or agg != T.TSV_AGG_MAX
+
     def step(d):
-        T.tsv_decode_step(sh, q, k_new, v_new, d.k_pool, d.v_pool, d.meta, bt, lens, k_max,
-                          kps, n_sink, scale, d.sel, d.cnt, None, d.out, d.ws)
+        if variant:
+            T.tsv_decode_step_ex(sh, q, k_new, v_new, d.k_pool, d.v_pool, d.meta, bt, lens,
+                                 k_max, kps, n_sink, args.recent, agg, scale, d.sel, d.cnt,
+                                 None, d.out, d.ws)
+        else:
+            T.tsv_decode_step(sh, q, k_new, v_new, d.k_pool, d.v_pool, d.meta, bt, lens, k_max,
+                              kps, n_sink, scale, d.sel, d.cnt, None, d.out, d.ws)
 
     first = instance()
     step(first)
@@ -354,7 +366,8 @@ def main():
         while t_cpu < args.cpu_seconds:
             c0 = time.perf_counter()
             O.decode_step(sh, q_np, kp, vp, meta, wl.block_table, lens_np, k_max, scale,
-                          kps_np, n_sink, st.k_new if st else None, st.v_new if st else None)
+                          kps_np, n_sink, st.k_new if st else None, st.v_new if st else None,
+                          args.recent, agg)
             t_cpu += time.perf_counter() - c0
             reps += 1
         cpu = {"value": B * Hq * reps / t_cpu, "unit": "(seq·head)/s", "cores": 1,
@@ -367,7 +380,7 @@ def main():
     step_gbs = nb["total"] / (ms_step * 1e-3) / 1e9
     src = source_hash()
     tkey = args.config if kv_dtype == own_dtype else f"{args.config}:{W.DTYPE_NAMES[kv_dtype]}"
-    tr = TRAFFIC.get(tkey)
+    tr = None if variant else TRAFFIC.get(tkey)
     traffic = tr["bytes_per_step"] if tr and tr["source"] == src else None
     kernel = {1: "k_step (append, score, select, decode of every row)",
               2: "k_step + k_merge (rows spread over several workgroups, then merged)"}.get(
@@ -390,7 +403,9 @@ def main():
                        else f" (KV stored as {W.DTYPE_NAMES[kv_dtype]} instead)"), "kv_dtype":
                    W.DTYPE_NAMES[sh.kv_dtype], "batch": B, "q_heads": Hq, "kv_heads": Hkv,
                    "head_dim": D, "page_size": sh.page_size, "k_max": k_max,
-                   "rotating_instances": R, "graph": not args.eager},
+                   "rotating_instances": R, "graph": not args.eager,
+                   "selection": {"n_sink": n_sink, "n_recent": args.recent,
+                                 "group_agg": args.group_agg}},
         "step_algorithmic_bytes": nb["total"],
         "step_bytes_breakdown": {k: v for k, v in nb.items() if k != "total"},
         "roofline": {"bound": "hbm", "kernel": kernel,

@@ -195,6 +195,49 @@ int tsv_decode_step(const tsv_shape* shape, const float* q, const void* k_new,
                     float* scores_out, float* out, void* workspace,
                     size_t workspace_bytes, void* stream);
 
+/* Selection variants (the pages fix neither how the G query heads of a KV
+   head are combined nor which pages besides the highest-scoring ones are
+   kept; attention-sink pages are cited under "Builds on").
+     group_agg  TSV_AGG_MAX: page score = the largest of the G heads' box
+                bounds (the default); TSV_AGG_SUM: their fp32 sum, heads in
+                increasing order, each addition rounded once (the bound of the
+                group's summed logit).
+     n_recent   >= 0: the last min(n_recent, K_b') pages of every sequence are
+                always kept as a local window, where K_b' = min(K_b, n_b) minus
+                the sink pages kept; counted inside the budget.  Sinks are
+                served first, then the window, then the highest scores among
+                the pages in between.  n_sink + n_recent must not exceed
+                k_max.
+   Per-layer budgets need no option: each call is one layer's step and takes
+   its own k_max / k_per_seq. */
+typedef enum { TSV_AGG_MAX = 0, TSV_AGG_SUM = 1 } tsv_group_agg;
+
+typedef struct {
+  int32_t n_recent;
+  int32_t group_agg; /* tsv_group_agg */
+} tsv_select_opts;
+
+/* tsv_select_pages with selection variants; opts = NULL is
+   {n_recent = 0, group_agg = TSV_AGG_MAX}, i.e. tsv_select_pages.
+   TSV_ERR_INVALID_ARG also for n_recent < 0, n_sink + n_recent > k_max or an
+   unknown group_agg. */
+int tsv_select_pages_ex(const tsv_shape* shape, const float* q, const void* meta,
+                        const int32_t* block_table, const int32_t* seq_lens,
+                        int32_t k_max, const int32_t* k_per_seq, int32_t n_sink,
+                        const tsv_select_opts* opts, int32_t* sel,
+                        int32_t* sel_count, float* scores_out, void* workspace,
+                        size_t workspace_bytes, void* stream);
+
+/* tsv_decode_step with selection variants (opts as for
+   tsv_select_pages_ex; NULL gives tsv_decode_step). */
+int tsv_decode_step_ex(const tsv_shape* shape, const float* q, const void* k_new,
+                       const void* v_new, void* k_pool, void* v_pool, void* meta,
+                       const int32_t* block_table, const int32_t* seq_lens,
+                       int32_t k_max, const int32_t* k_per_seq, int32_t n_sink,
+                       const tsv_select_opts* opts, float scale, int32_t* sel,
+                       int32_t* sel_count, float* scores_out, float* out,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

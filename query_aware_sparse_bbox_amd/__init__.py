@@ -23,10 +23,12 @@ _lib = ctypes.CDLL(LIB_PATH)
 
 TSV_F32, TSV_F16, TSV_BF16, TSV_FP8_E4M3 = 0, 1, 2, 3
 TSV_OK, TSV_ERR_INVALID_ARG, TSV_ERR_UNSUPPORTED, TSV_ERR_HIP = 0, -1, -2, -3
+TSV_AGG_MAX, TSV_AGG_SUM = 0, 1
 
 EXPORTS = ("tsv_version", "tsv_status_string", "tsv_meta_bytes", "tsv_workspace_bytes",
            "tsv_decode_step_launches", "tsv_meta_build", "tsv_meta_append",
-           "tsv_select_pages", "tsv_sparse_decode", "tsv_decode_step")
+           "tsv_select_pages", "tsv_sparse_decode", "tsv_decode_step",
+           "tsv_select_pages_ex", "tsv_decode_step_ex")
 
 
 class TsvError(RuntimeError):
@@ -47,8 +49,14 @@ class Shape(ctypes.Structure):
         return cls(*(int(getattr(s, n)) for n, _ in cls._fields_))
 
 
+class SelectOpts(ctypes.Structure):
+    """tsv_select_opts."""
+    _fields_ = [("n_recent", ctypes.c_int32), ("group_agg", ctypes.c_int32)]
+
+
 _P, _I, _F, _Z = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
 _SP = ctypes.POINTER(Shape)
+_OP = ctypes.POINTER(SelectOpts)
 _SIGS = {
     "tsv_version": ([], ctypes.c_int),
     "tsv_status_string": ([ctypes.c_int], ctypes.c_char_p),
@@ -63,6 +71,10 @@ _SIGS = {
                           ctypes.c_int),
     "tsv_decode_step": ([_SP, _P, _P, _P, _P, _P, _P, _P, _P, _I, _P, _I, _F, _P, _P, _P,
                          _P, _P, _Z, _P], ctypes.c_int),
+    "tsv_select_pages_ex": ([_SP, _P, _P, _P, _P, _I, _P, _I, _OP, _P, _P, _P, _P, _Z, _P],
+                            ctypes.c_int),
+    "tsv_decode_step_ex": ([_SP, _P, _P, _P, _P, _P, _P, _P, _P, _I, _P, _I, _OP, _F, _P, _P,
+                            _P, _P, _P, _Z, _P], ctypes.c_int),
 }
 for _name, (_args, _res) in _SIGS.items():
     _f = getattr(_lib, _name)
@@ -161,4 +173,28 @@ def tsv_decode_step(shape, q, k_new, v_new, k_pool, v_pool, meta, block_table, s
           _ptr(v_new), _ptr(k_pool), _ptr(v_pool), _ptr(meta), _ptr(block_table),
           _ptr(seq_lens), int(k_max), _ptr(k_per_seq), int(n_sink), float(scale),
           _ptr(sel), _ptr(sel_count), _ptr(scores_out), _ptr(out), _ptr(workspace),
+          workspace.numel() * workspace.element_size(), _stream(stream))
+
+
+def _opts(n_recent, group_agg):
+    return ctypes.byref(SelectOpts(int(n_recent), int(group_agg)))
+
+
+def tsv_select_pages_ex(shape, q, meta, block_table, seq_lens, k_max, k_per_seq, n_sink,
+                        n_recent, group_agg, sel, sel_count, scores_out, workspace,
+                        stream=None):
+    _call("tsv_select_pages_ex", ctypes.byref(Shape.of(shape)), _ptr(q), _ptr(meta),
+          _ptr(block_table), _ptr(seq_lens), int(k_max), _ptr(k_per_seq), int(n_sink),
+          _opts(n_recent, group_agg), _ptr(sel), _ptr(sel_count), _ptr(scores_out),
+          _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
+
+
+def tsv_decode_step_ex(shape, q, k_new, v_new, k_pool, v_pool, meta, block_table, seq_lens,
+                       k_max, k_per_seq, n_sink, n_recent, group_agg, scale, sel, sel_count,
+                       scores_out, out, workspace, stream=None):
+    _call("tsv_decode_step_ex", ctypes.byref(Shape.of(shape)), _ptr(q), _ptr(k_new),
+          _ptr(v_new), _ptr(k_pool), _ptr(v_pool), _ptr(meta), _ptr(block_table),
+          _ptr(seq_lens), int(k_max), _ptr(k_per_seq), int(n_sink),
+          _opts(n_recent, group_agg), float(scale), _ptr(sel), _ptr(sel_count),
+          _ptr(scores_out), _ptr(out), _ptr(workspace),
           workspace.numel() * workspace.element_size(), _stream(stream))

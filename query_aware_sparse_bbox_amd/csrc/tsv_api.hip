@@ -55,13 +55,27 @@ int check_workspace(const Dims& d, int32_t k_max, const void* ws, size_t ws_byte
   return TSV_OK;
 }
 
+// Selection policy of a call; opts may be NULL (no window, max over heads).
+int make_policy(int32_t k_max, int32_t n_sink, const tsv_select_opts* opts,
+                tsv::SelectPolicy* pol) {
+  const int32_t n_recent = opts ? opts->n_recent : 0;
+  const int32_t agg = opts ? opts->group_agg : TSV_AGG_MAX;
+  if (n_sink < 0 || n_recent < 0 || n_sink > k_max || n_recent > k_max - n_sink)
+    return TSV_ERR_INVALID_ARG;
+  if (agg != TSV_AGG_MAX && agg != TSV_AGG_SUM) return TSV_ERR_INVALID_ARG;
+  pol->n_sink = n_sink;
+  pol->n_recent = n_recent;
+  pol->group_sum = agg == TSV_AGG_SUM;
+  return TSV_OK;
+}
+
 int check_select_args(const Dims& d, const float* q, const void* meta,
                       const int32_t* bt, const int32_t* seq_lens, int32_t k_max,
-                      int32_t n_sink, const int32_t* sel, const int32_t* sel_count,
+                      const int32_t* sel, const int32_t* sel_count,
                       const void* ws, size_t ws_bytes) {
   if (!q || !meta || !bt || !seq_lens || !sel || !sel_count)
     return TSV_ERR_INVALID_ARG;
-  if (k_max < 1 || n_sink < 0 || n_sink > k_max) return TSV_ERR_INVALID_ARG;
+  if (k_max < 1) return TSV_ERR_INVALID_ARG;
   if (!aligned(q, 16) || !aligned(meta, 16)) return TSV_ERR_INVALID_ARG;
   return check_workspace(d, k_max, ws, ws_bytes);
 }
@@ -142,22 +156,36 @@ int tsv_meta_append(const tsv_shape* shape, const void* k_new, const void* v_new
                                             (hipStream_t)stream));
 }
 
+int tsv_select_pages_ex(const tsv_shape* shape, const float* q, const void* meta,
+                        const int32_t* block_table, const int32_t* seq_lens,
+                        int32_t k_max, const int32_t* k_per_seq, int32_t n_sink,
+                        const tsv_select_opts* opts, int32_t* sel, int32_t* sel_count,
+                        float* scores_out, void* workspace, size_t workspace_bytes,
+                        void* stream) {
+  Dims d;
+  int rc = check_shape(shape, &d);
+  if (rc) return rc;
+  rc = check_select_args(d, q, meta, block_table, seq_lens, k_max, sel, sel_count,
+                         workspace, workspace_bytes);
+  if (rc) return rc;
+  tsv::SelectPolicy pol;
+  rc = make_policy(k_max, n_sink, opts, &pol);
+  if (rc) return rc;
+  tsv::Workspace ws;
+  tsv::workspace_layout(d, k_max, workspace, &ws);
+  return hip_status(tsv::launch_score_select(d, q, meta, block_table, seq_lens, k_max,
+                                             k_per_seq, pol, sel, sel_count, scores_out,
+                                             ws, (hipStream_t)stream));
+}
+
 int tsv_select_pages(const tsv_shape* shape, const float* q, const void* meta,
                      const int32_t* block_table, const int32_t* seq_lens,
                      int32_t k_max, const int32_t* k_per_seq, int32_t n_sink,
                      int32_t* sel, int32_t* sel_count, float* scores_out,
                      void* workspace, size_t workspace_bytes, void* stream) {
-  Dims d;
-  int rc = check_shape(shape, &d);
-  if (rc) return rc;
-  rc = check_select_args(d, q, meta, block_table, seq_lens, k_max, n_sink, sel,
-                         sel_count, workspace, workspace_bytes);
-  if (rc) return rc;
-  tsv::Workspace ws;
-  tsv::workspace_layout(d, k_max, workspace, &ws);
-  return hip_status(tsv::launch_score_select(d, q, meta, block_table, seq_lens, k_max,
-                                             k_per_seq, n_sink, sel, sel_count,
-                                             scores_out, ws, (hipStream_t)stream));
+  return tsv_select_pages_ex(shape, q, meta, block_table, seq_lens, k_max, k_per_seq,
+                             n_sink, nullptr, sel, sel_count, scores_out, workspace,
+                             workspace_bytes, stream);
 }
 
 int tsv_sparse_decode(const tsv_shape* shape, const float* q, const void* k_pool,
@@ -179,29 +207,32 @@ int tsv_sparse_decode(const tsv_shape* shape, const float* q, const void* k_pool
                                        (hipStream_t)stream));
 }
 
-int tsv_decode_step(const tsv_shape* shape, const float* q, const void* k_new,
-                    const void* v_new, void* k_pool, void* v_pool, void* meta,
-                    const int32_t* block_table, const int32_t* seq_lens,
-                    int32_t k_max, const int32_t* k_per_seq, int32_t n_sink,
-                    float scale, int32_t* sel, int32_t* sel_count,
-                    float* scores_out, float* out, void* workspace,
-                    size_t workspace_bytes, void* stream) {
+int tsv_decode_step_ex(const tsv_shape* shape, const float* q, const void* k_new,
+                       const void* v_new, void* k_pool, void* v_pool, void* meta,
+                       const int32_t* block_table, const int32_t* seq_lens,
+                       int32_t k_max, const int32_t* k_per_seq, int32_t n_sink,
+                       const tsv_select_opts* opts, float scale, int32_t* sel,
+                       int32_t* sel_count, float* scores_out, float* out,
+                       void* workspace, size_t workspace_bytes, void* stream) {
   Dims d;
   int rc = check_shape(shape, &d);
   if (rc) return rc;
   if ((k_new == nullptr) != (v_new == nullptr)) return TSV_ERR_INVALID_ARG;
-  rc = check_select_args(d, q, meta, block_table, seq_lens, k_max, n_sink, sel,
-                         sel_count, workspace, workspace_bytes);
+  rc = check_select_args(d, q, meta, block_table, seq_lens, k_max, sel, sel_count,
+                         workspace, workspace_bytes);
   if (rc) return rc;
   rc = check_decode_args(d, q, k_pool, v_pool, block_table, seq_lens, sel,
                          sel_count, k_max, out, workspace, workspace_bytes);
+  if (rc) return rc;
+  tsv::SelectPolicy pol;
+  rc = make_policy(k_max, n_sink, opts, &pol);
   if (rc) return rc;
   hipStream_t s = (hipStream_t)stream;
   tsv::Workspace ws;
   tsv::workspace_layout(d, k_max, workspace, &ws);
   if (tsv::step_fits(d))  // every row's whole step in its own workgroup(s)
     return hip_status(tsv::launch_step(d, q, k_new, v_new, k_pool, v_pool, meta,
-                                       block_table, seq_lens, k_max, k_per_seq, n_sink,
+                                       block_table, seq_lens, k_max, k_per_seq, pol,
                                        scale, sel, sel_count, scores_out, ws, out, s));
   if (k_new) {
     rc = hip_status(tsv::launch_meta_append(d, k_new, v_new, k_pool, v_pool, meta,
@@ -209,12 +240,24 @@ int tsv_decode_step(const tsv_shape* shape, const float* q, const void* k_new,
     if (rc) return rc;
   }
   rc = hip_status(tsv::launch_score_select(d, q, meta, block_table, seq_lens, k_max,
-                                           k_per_seq, n_sink, sel, sel_count,
-                                           scores_out, ws, s));
+                                           k_per_seq, pol, sel, sel_count, scores_out,
+                                           ws, s));
   if (rc) return rc;
   return hip_status(tsv::launch_decode(d, q, k_pool, v_pool, block_table, seq_lens,
                                        sel, ws.sel_phys, sel_count, k_max, scale, ws,
                                        out, s));
+}
+
+int tsv_decode_step(const tsv_shape* shape, const float* q, const void* k_new,
+                    const void* v_new, void* k_pool, void* v_pool, void* meta,
+                    const int32_t* block_table, const int32_t* seq_lens,
+                    int32_t k_max, const int32_t* k_per_seq, int32_t n_sink,
+                    float scale, int32_t* sel, int32_t* sel_count,
+                    float* scores_out, float* out, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  return tsv_decode_step_ex(shape, q, k_new, v_new, k_pool, v_pool, meta, block_table,
+                            seq_lens, k_max, k_per_seq, n_sink, nullptr, scale, sel,
+                            sel_count, scores_out, out, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

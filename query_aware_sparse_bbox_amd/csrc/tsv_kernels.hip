@@ -365,7 +365,7 @@ struct SelectLds {
 // to prow (if non-null) and the count to *count.  Ends with a barrier.
 template <int NT>
 __device__ __forceinline__ int select_block(uint32_t* s_key, uint32_t* s_phys, int n,
-                                            int keff, int f, int k_max,
+                                            int keff, int f, int r, int k_max,
                                             int32_t* __restrict__ srow,
                                             int32_t* __restrict__ prow,
                                             int32_t* __restrict__ count, SelectLds<NT>& sl) {
@@ -374,7 +374,7 @@ __device__ __forceinline__ int select_block(uint32_t* s_key, uint32_t* s_phys, i
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
   const int m = (n + NT - 1) / NT;
   const int p0 = tid * m, nl = max(n - 1, 0);
-  const int R = keff - f, ncand = n - f;
+  const int R = keff - f - r, ncand = n - f - r, pr = n - r;  // candidates [f, pr)
   const bool take_all = R >= ncand, radix = R > 0 && R < ncand;
   uint32_t kk[MAXM], ph[MAXM];
 #pragma unroll
@@ -386,7 +386,7 @@ __device__ __forceinline__ int select_block(uint32_t* s_key, uint32_t* s_phys, i
   }
   auto is_cand = [&](int i) {
     const int p = p0 + i;
-    return i < m && p < n && p >= f;
+    return i < m && p < pr && p >= f;
   };
   uint32_t tmask = 0, tau = 0;  // (key & tmask) > tau: kept; == tau: the first `need`
   int need = 0;
@@ -475,10 +475,10 @@ __device__ __forceinline__ int select_block(uint32_t* s_key, uint32_t* s_phys, i
   auto flags = [&](int i, bool& keep, bool& eq) {
     const int p = p0 + i;
     const bool valid = i < m && p < n;
-    const bool cand = valid && p >= f;
+    const bool cand = valid && p >= f && p < pr;
     const uint32_t km = kk[i] & tmask;
     eq = radix && cand && km == tau;
-    keep = (valid && p < f) || (cand && (take_all || (radix && km > tau)));
+    keep = (valid && (p < f || p >= pr)) || (cand && (take_all || (radix && km > tau)));
   };
   int nkeep = 0, neq = 0;
 #pragma unroll
@@ -522,8 +522,10 @@ __device__ __forceinline__ int select_block(uint32_t* s_key, uint32_t* s_phys, i
 }
 
 // Scores batches bstart, bstart + bstride, ... of one unit's n pages into
-// s_key (order keys).  s_phys holds the unit's block-table row.  No barrier.
-template <int DT, int D, int G, int NT>
+// s_key (order keys).  s_phys holds the unit's block-table row.  GSUM: the
+// group's heads are summed (fp32, increasing head order), else maxed.  No
+// barrier.
+template <int DT, int D, int G, int NT, bool GSUM>
 __device__ __forceinline__ void score_pages(const float* __restrict__ q,
                                             const void* __restrict__ meta,
                                             const uint32_t* s_phys, int b, int h, int Hq,
@@ -577,7 +579,8 @@ __device__ __forceinline__ void score_pages(const float* __restrict__ q,
         for (int cc = 0; cc < C; ++cc)
           t[cc] = __builtin_fmaf(qn[g][cc], mn[cc], qp[g][cc] * mx[cc]);
         const float sc = group_sum<L>(tree_sum<C>(t));
-        best = g == 0 ? sc : fmaxf(best, sc);
+        if constexpr (GSUM) best = g == 0 ? sc : best + sc;
+        else best = g == 0 ? sc : fmaxf(best, sc);
       }
       best = best == 0.f ? 0.f : best;  // -0 -> +0
       if (p < n && chunk == 0) s_key[p] = order_key(best);
@@ -614,7 +617,7 @@ __global__ __launch_bounds__(NTH, score_min_waves<G>()) void k_score_select(
     const float* __restrict__ q, const void* __restrict__ meta,
     const int32_t* __restrict__ bt, const int32_t* __restrict__ seq_lens,
     int Hq, int Hkv, int P, int MP, int NP, int NS, int k_max,
-    const int32_t* __restrict__ k_per_seq, int n_sink,
+    const int32_t* __restrict__ k_per_seq, SelectPolicy pol,
     int32_t* __restrict__ sel, int32_t* __restrict__ sel_count,
     float* __restrict__ scores_out, uint32_t* __restrict__ keys,
     int32_t* __restrict__ sel_phys) {
@@ -642,7 +645,11 @@ __global__ __launch_bounds__(NTH, score_min_waves<G>()) void k_score_select(
   const int nbatch = (n + PB - 1) / PB;
   if (split > 0 && split >= nbatch) return;  // whole workgroup: no pages
   __syncthreads();
-  score_pages<DT, D, G, NT>(q, meta, s_phys, b, h, Hq, Hkv, n, split, NS, s_key);
+  // one copy of the scoring loop per aggregation; the branch is uniform
+  if (pol.group_sum)
+    score_pages<DT, D, G, NT, true>(q, meta, s_phys, b, h, Hq, Hkv, n, split, NS, s_key);
+  else
+    score_pages<DT, D, G, NT, false>(q, meta, s_phys, b, h, Hq, Hkv, n, split, NS, s_key);
   __syncthreads();
   // this workgroup's pages: keys for k_select (split rows), optional scores
   if (NS > 1 || scores_out) {
@@ -659,8 +666,8 @@ __global__ __launch_bounds__(NTH, score_min_waves<G>()) void k_score_select(
       }
   }
   if (NS > 1) return;
-  const int keff = min(kb, n), f = min(n_sink, keff);
-  select_block<NT>(s_key, s_phys, n, keff, f, k_max, sel + (size_t)unit * k_max,
+  const int keff = min(kb, n), f = min(pol.n_sink, keff), r = min(pol.n_recent, keff - f);
+  select_block<NT>(s_key, s_phys, n, keff, f, r, k_max, sel + (size_t)unit * k_max,
                    sel_phys + (size_t)unit * k_max, sel_count + unit, sl);
 }
 
@@ -670,7 +677,7 @@ constexpr int kSelectThreads = 256;
 
 __global__ __launch_bounds__(kSelectThreads) void k_select(
     const int32_t* __restrict__ bt, const int32_t* __restrict__ seq_lens, int Hkv, int P,
-    int MP, int NP, int k_max, const int32_t* __restrict__ k_per_seq, int n_sink,
+    int MP, int NP, int k_max, const int32_t* __restrict__ k_per_seq, SelectPolicy pol,
     const uint32_t* __restrict__ keys, int32_t* __restrict__ sel,
     int32_t* __restrict__ sel_count, int32_t* __restrict__ sel_phys) {
   constexpr int NT = kSelectThreads;
@@ -691,8 +698,8 @@ __global__ __launch_bounds__(kSelectThreads) void k_select(
   const int kb = clampi(k_per_seq ? k_per_seq[b] : k_max, 1, k_max);
   const int n = (len + P - 1) / P;
   __syncthreads();
-  const int keff = min(kb, n), f = min(n_sink, keff);
-  select_block<NT>(s_key, s_phys, n, keff, f, k_max, sel + (size_t)unit * k_max,
+  const int keff = min(kb, n), f = min(pol.n_sink, keff), r = min(pol.n_recent, keff - f);
+  select_block<NT>(s_key, s_phys, n, keff, f, r, k_max, sel + (size_t)unit * k_max,
                    sel_phys + (size_t)unit * k_max, sel_count + unit, sl);
 }
 
@@ -1560,7 +1567,7 @@ __global__ __launch_bounds__(NT, (step_min_blocks<DT, D, G, NT>())) void k_step(
     const void* __restrict__ v_new, void* __restrict__ k_pool, void* __restrict__ v_pool,
     void* __restrict__ meta, const int32_t* __restrict__ bt,
     const int32_t* __restrict__ seq_lens, int units, int Hq, int Hkv, int log2P, int MP,
-    int NP, int k_max, const int32_t* __restrict__ k_per_seq, int n_sink, float qscale,
+    int NP, int k_max, const int32_t* __restrict__ k_per_seq, SelectPolicy pol, float qscale,
     int S, int32_t* __restrict__ sel, int32_t* __restrict__ sel_count,
     float* __restrict__ scores_out, float* __restrict__ partials, float* __restrict__ out) {
   constexpr int NW = NT / kWave;
@@ -1611,16 +1618,20 @@ __global__ __launch_bounds__(NT, (step_min_blocks<DT, D, G, NT>())) void k_step(
     }
   }
   __syncthreads();  // block-table row staged; the appended token visible to the workgroup
-  score_pages<DT, D, G, NT>(q, meta, s_phys, b, h, Hq, Hkv, n, 0, 1, s_key);
+  if (pol.group_sum)  // uniform branch: one copy of the scoring loop per aggregation
+    score_pages<DT, D, G, NT, true>(q, meta, s_phys, b, h, Hq, Hkv, n, 0, 1, s_key);
+  else
+    score_pages<DT, D, G, NT, false>(q, meta, s_phys, b, h, Hq, Hkv, n, 0, 1, s_key);
   __syncthreads();
   if (scores_out && split == 0) {
     float* srow_out = scores_out + (size_t)unit * MP;
     for (int p = tid; p < n; p += NT) srow_out[p] = key_to_score(s_key[p]);
   }
-  const int keff = min(kb, n), f = min(n_sink, keff);
+  const int keff = min(kb, n), f = min(pol.n_sink, keff), r = min(pol.n_recent, keff - f);
   // the selection stays in LDS; it is written out at the end, so that no
   // barrier before the decode waits for those stores
-  const int cnt = select_block<NT>(s_key, s_phys, n, keff, f, k_max, nullptr, nullptr, nullptr, sl);
+  const int cnt =
+      select_block<NT>(s_key, s_phys, n, keff, f, r, k_max, nullptr, nullptr, nullptr, sl);
   int32_t* srow = sel + (size_t)unit * k_max;
   float* orow = out + ((size_t)b * Hq + h * G) * D;
   // with S > 1 every split leaves a partial state for k_merge_step; a split
@@ -1794,9 +1805,9 @@ hipError_t launch_meta_append(const Dims& d, const void* k_new,
 
 hipError_t launch_score_select(const Dims& d, const float* q, const void* meta,
                                const int32_t* bt, const int32_t* seq_lens,
-                               int k_max, const int32_t* k_per_seq, int n_sink,
-                               int32_t* sel, int32_t* sel_count, float* scores_out,
-                               const Workspace& ws, hipStream_t s) {
+                               int k_max, const int32_t* k_per_seq,
+                               const SelectPolicy& pol, int32_t* sel, int32_t* sel_count,
+                               float* scores_out, const Workspace& ws, hipStream_t s) {
   return by_dt_d_g(d, [&](auto DT, auto HD, auto GG) -> hipError_t {
     constexpr int dt = decltype(DT)::value, hd = decltype(HD)::value,
                   g = decltype(GG)::value;
@@ -1818,17 +1829,17 @@ hipError_t launch_score_select(const Dims& d, const float* q, const void* meta,
     if (small)
       hipLaunchKernelGGL((k_score_select<dt, hd, g, 256>), dim3(units * NS), dim3(256), shmem,
                          s, q, meta, bt, seq_lens, d.Hq, d.Hkv, d.P, d.MP, d.NP, NS, k_max,
-                         k_per_seq, n_sink, sel, sel_count, scores_out, ws.keys, ws.sel_phys);
+                         k_per_seq, pol, sel, sel_count, scores_out, ws.keys, ws.sel_phys);
     else
       hipLaunchKernelGGL((k_score_select<dt, hd, g, Big::NT>), dim3(units * NS), dim3(Big::NT),
                          shmem, s, q, meta, bt, seq_lens, d.Hq, d.Hkv, d.P, d.MP, d.NP, NS,
-                         k_max, k_per_seq, n_sink, sel, sel_count, scores_out, ws.keys,
+                         k_max, k_per_seq, pol, sel, sel_count, scores_out, ws.keys,
                          ws.sel_phys);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || NS == 1) return e;
     hipLaunchKernelGGL(k_select, dim3(units), dim3(kSelectThreads),
                        2 * sizeof(uint32_t) * (size_t)d.MP,
-                       s, bt, seq_lens, d.Hkv, d.P, d.MP, d.NP, k_max, k_per_seq, n_sink,
+                       s, bt, seq_lens, d.Hkv, d.P, d.MP, d.NP, k_max, k_per_seq, pol,
                        ws.keys, sel, sel_count, ws.sel_phys);
     return hipGetLastError();
   });
@@ -1875,8 +1886,9 @@ int step_splits(const Dims& d, int k_max) {
 hipError_t launch_step(const Dims& d, const float* q, const void* k_new, const void* v_new,
                        void* k_pool, void* v_pool, void* meta, const int32_t* bt,
                        const int32_t* seq_lens, int k_max, const int32_t* k_per_seq,
-                       int n_sink, float scale, int32_t* sel, int32_t* sel_count,
-                       float* scores_out, const Workspace& ws, float* out, hipStream_t s) {
+                       const SelectPolicy& pol, float scale, int32_t* sel,
+                       int32_t* sel_count, float* scores_out, const Workspace& ws,
+                       float* out, hipStream_t s) {
   const int nt = step_threads(d);
   const size_t lds = step_lds_bytes(d);
   if (lds > kStepMaxLds) return hipErrorInvalidValue;
@@ -1891,7 +1903,7 @@ hipError_t launch_step(const Dims& d, const float* q, const void* k_new, const v
       constexpr int nthr = decltype(NTc)::value;
       hipLaunchKernelGGL((k_step<dt, hd, g, nthr>), grid, dim3(nthr), lds, s, q, k_new, v_new,
                          k_pool, v_pool, meta, bt, seq_lens, units, d.Hq, d.Hkv, log2P, d.MP,
-                         d.NP, k_max, k_per_seq, n_sink, qscale, S, sel, sel_count,
+                         d.NP, k_max, k_per_seq, pol, qscale, S, sel, sel_count,
                          scores_out, ws.partials, out);
       return hipGetLastError();
     };

@@ -15,6 +15,12 @@ constexpr int kv_bytes(int dt) { return dt == DT_F32 ? 4 : dt == DT_F8 ? 1 : 2; 
 // 8 bytes for fp8 (so a lane holds as many channels as for 16-bit data).
 constexpr int kv_vec(int dt) { return dt == DT_F8 ? 8 : 16 / kv_bytes(dt); }
 
+// Selection policy of one call: forced sink pages, forced most recent pages,
+// and whether the G query heads' box bounds are summed (else maxed).
+struct SelectPolicy {
+  int n_sink, n_recent, group_sum;
+};
+
 // Validated sizes of one call.
 struct Dims {
   int B, Hq, Hkv, D, P, MP, NP, dt, G;
@@ -50,8 +56,9 @@ hipError_t launch_meta_append(const Dims& d, const void* k_new,
 // Scores every page, keeps the top pages; also fills ws.sel_phys.
 hipError_t launch_score_select(const Dims& d, const float* q, const void* meta,
                                const int32_t* bt, const int32_t* seq_lens,
-                               int k_max, const int32_t* k_per_seq, int n_sink,
-                               int32_t* sel, int32_t* sel_count, float* scores_out,
+                               int k_max, const int32_t* k_per_seq,
+                               const SelectPolicy& pol, int32_t* sel, int32_t* sel_count,
+                               float* scores_out,
                                const Workspace& ws, hipStream_t s);
 
 // Split decode; units with several tiles are merged by a second kernel.
@@ -77,7 +84,8 @@ int step_splits(const Dims& d, int k_max);
 hipError_t launch_step(const Dims& d, const float* q, const void* k_new, const void* v_new,
                        void* k_pool, void* v_pool, void* meta, const int32_t* bt,
                        const int32_t* seq_lens, int k_max, const int32_t* k_per_seq,
-                       int n_sink, float scale, int32_t* sel, int32_t* sel_count,
-                       float* scores_out, const Workspace& ws, float* out, hipStream_t s);
+                       const SelectPolicy& pol, float scale, int32_t* sel,
+                       int32_t* sel_count, float* scores_out, const Workspace& ws,
+                       float* out, hipStream_t s);
 
 }  // namespace tsv

@@ -21,7 +21,7 @@ def say(*a):
     sys.stdout.flush()
 
 
-def oracle_run(wl, k_max=None, k_per_seq="wl", n_sink=None, step=0):
+def oracle_run(wl, k_max=None, k_per_seq="wl", n_sink=None, step=0, n_recent=0, group_agg=0):
     """Oracle results of one decode step (append first if the workload has steps)."""
     sh = wl.shape
     k_max = wl.k_max if k_max is None else k_max
@@ -33,17 +33,21 @@ def oracle_run(wl, k_max=None, k_per_seq="wl", n_sink=None, step=0):
         meta = O.meta_build(sh, kp, wl.block_table, lens_pre)
         kps = st.k_per_seq if isinstance(k_per_seq, str) else k_per_seq
         sel, cnt, sc, out = O.decode_step(sh, st.q, kp, vp, meta, wl.block_table, st.seq_lens,
-                                          k_max, wl.scale, kps, n_sink, st.k_new, st.v_new)
+                                          k_max, wl.scale, kps, n_sink, st.k_new, st.v_new,
+                                          n_recent, group_agg)
     else:
         meta = O.meta_build(sh, kp, wl.block_table, wl.seq_lens)
         kps = wl.k_per_seq if isinstance(k_per_seq, str) else k_per_seq
         sel, cnt, sc, out = O.decode_step(sh, wl.q, kp, vp, meta, wl.block_table, wl.seq_lens,
-                                          k_max, wl.scale, kps, n_sink)
+                                          k_max, wl.scale, kps, n_sink, None, None,
+                                          n_recent, group_agg)
     return dict(meta=meta, sel=sel, cnt=cnt, scores=sc, out=out, k_pool=kp, v_pool=vp)
 
 
-def gpu_run(wl, k_max=None, k_per_seq="wl", n_sink=None, step=0, separate=False):
-    """HIP results of the same step; `separate` uses the three-call path."""
+def gpu_run(wl, k_max=None, k_per_seq="wl", n_sink=None, step=0, separate=False, n_recent=0,
+            group_agg=0):
+    """HIP results of the same step; `separate` uses the three-call path.  With
+    selection options the _ex entry points are called, else the plain ones."""
     import torch
 
     import query_aware_sparse_bbox_amd as T
@@ -78,10 +82,18 @@ def gpu_run(wl, k_max=None, k_per_seq="wl", n_sink=None, step=0, separate=False)
         if k_new is not None:
             T.tsv_meta_append(sh, k_new, v_new, d.k_pool, d.v_pool, d.meta, d.block_table,
                               seq_lens)
-        T.tsv_select_pages(sh, q, d.meta, d.block_table, seq_lens, k_max, kps, n_sink, sel,
-                           cnt, sc, ws)
+        if n_recent or group_agg:
+            T.tsv_select_pages_ex(sh, q, d.meta, d.block_table, seq_lens, k_max, kps, n_sink,
+                                  n_recent, group_agg, sel, cnt, sc, ws)
+        else:
+            T.tsv_select_pages(sh, q, d.meta, d.block_table, seq_lens, k_max, kps, n_sink,
+                               sel, cnt, sc, ws)
         T.tsv_sparse_decode(sh, q, d.k_pool, d.v_pool, d.block_table, seq_lens, sel, cnt,
                             k_max, wl.scale, out, ws)
+    elif n_recent or group_agg:
+        T.tsv_decode_step_ex(sh, q, k_new, v_new, d.k_pool, d.v_pool, d.meta, d.block_table,
+                             seq_lens, k_max, kps, n_sink, n_recent, group_agg, wl.scale, sel,
+                             cnt, sc, out, ws)
     else:
         T.tsv_decode_step(sh, q, k_new, v_new, d.k_pool, d.v_pool, d.meta, d.block_table,
                           seq_lens, k_max, kps, n_sink, wl.scale, sel, cnt, sc, out, ws)

@@ -36,7 +36,7 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ("tsv_meta_append", "tsv_select_pages", "tsv_sparse_decode", "tsv_decode_step",
               "tsv_meta_build", "tsv_workspace_bytes", "tsv_meta_bytes", "tsv_status_string",
-              "tsv_version"):
+              "tsv_version", "tsv_select_pages_ex", "tsv_decode_step_ex"):
         assert n in names
 
 
@@ -148,3 +148,21 @@ def test_bad_arguments_rejected_before_any_hip_call(tsv):
                              ctypes.c_float(0.1), f, f, None, f, f, need, None) == -1
     # null shape
     assert L.tsv_meta_build(None, f, f, f, f, None) == -1
+
+
+@pytest.mark.parametrize("n_sink,n_recent,agg,status", [
+    (0, -1, 0, -1),      # negative window
+    (2, 3, 0, -1),       # sinks + window beyond k_max = 4
+    (0, 0, 2, -1),       # unknown group aggregation
+    (0, 0, -1, -1),
+])
+def test_bad_selection_options_rejected_before_any_hip_call(tsv, n_sink, n_recent, agg, status):
+    s = shape()
+    f = ctypes.c_void_p(1 << 20)
+    L = tsv._lib
+    need = L.tsv_workspace_bytes(ctypes.byref(s), 4)
+    o = ctypes.byref(tsv.SelectOpts(n_recent, agg))
+    assert L.tsv_select_pages_ex(ctypes.byref(s), f, f, f, f, 4, None, n_sink, o, f, f, None, f,
+                                 need, None) == status
+    assert L.tsv_decode_step_ex(ctypes.byref(s), f, None, None, f, f, f, f, f, 4, None, n_sink,
+                                o, ctypes.c_float(0.1), f, f, None, f, f, need, None) == status

@@ -77,6 +77,48 @@ def test_tie_heavy(dtype, G):
     assert max(len(v) - len(set(v.tolist())) for v in sc.reshape(-1, 49)) > 5
 
 
+# selection variants: group sum aggregation (MFMA and VALU decode, both
+# paths), a forced recent window with and without sinks, budgets that cut the
+# window, tie-heavy rows
+@pytest.mark.parametrize("name,kw,opts", [
+    ("tinyllama", dict(batch=3, context=1001), dict(group_agg=1)),
+    ("tinyllama", dict(batch=2, context=333, num_q_heads=8, num_kv_heads=4), dict(group_agg=1)),
+    ("ragged", dict(batch=6, lens_range=(100, 2000)), dict(group_agg=1, n_recent=3)),
+    ("llama_long", dict(batch=2, context=5000), dict(n_recent=4)),
+    ("llama_long", dict(batch=2, context=3000, kv_dtype=W.F8), dict(n_recent=2, group_agg=1)),
+    ("gpt2", dict(batch=5, context=999), dict(n_recent=1, n_sink=1)),
+    ("ragged", dict(batch=8, lens_range=(1, 600)), dict(n_recent=2, n_sink=1, k_max=4)),
+])
+def test_selection_variants(name, kw, opts):
+    wl = W.make(name, **kw)
+    o = dict(opts)
+    if "k_max" in o:
+        o["k_per_seq"] = None
+    _case(wl, **o)
+
+
+def test_selection_variants_phased_and_full_size():
+    import query_aware_sparse_bbox_amd as T
+
+    wl = W.make("tinyllama")
+    _case(wl, group_agg=1, n_recent=2)
+    # the phased path (three calls) and a 4095-page row (phased one-call step)
+    wl = W.make("ragged", batch=4, lens_range=(100, 3000))
+    o = oracle_run(wl, group_agg=1, n_recent=2)
+    g = gpu_run(wl, group_agg=1, n_recent=2, separate=True)
+    compare(wl, g, o)
+    wl = W.make("ragged", batch=2, lens_range=(65500, 65535), kv_dtype=W.BF16, num_q_heads=64)
+    assert T.tsv_decode_step_launches(wl.shape, wl.k_max, True) == 4
+    _case(wl, group_agg=1, n_recent=5)
+
+
+@pytest.mark.parametrize("G", [1, 4])
+def test_selection_variants_tie_heavy(G):
+    wl = W.tie_heavy(41 + G, kv_dtype=W.BF16, num_q_heads=2 * G, num_kv_heads=2, context=777,
+                     k_max=9, n_sink=1, value_range=2)
+    _case(wl, group_agg=1, n_recent=2)
+
+
 def test_poisoned_unused_slots():
     for name, kw in [("gpt2", dict(batch=4, context=301)),
                      ("ragged", dict(batch=8, lens_range=(5, 900))),
