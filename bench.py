@@ -63,13 +63,17 @@ KERNEL_SOURCES = [os.path.join(ROOT, "query_aware_sparse_bbox_amd", "csrc", f)
 # `--pmc WRITE_SIZE` runs of this script, each divided by the same counter's
 # reading per byte of a plain device copy (--copy-calibrate).  Valid only for
 # the kernel source they were taken on (sha256 of KERNEL_SOURCES, first 16
-# hex digits).
+# hex digits).  Keys: configuration, or configuration:KV type when the
+# configuration's KV type is overridden.
 TRAFFIC = {
-    "tinyllama": {"source": "566f9ca64130152b", "bytes_per_step": 22864726, "read": 22174550, "written": 690176},
-    "tiny": {"source": "566f9ca64130152b", "bytes_per_step": 545629, "read": 544349, "written": 1280},
-    "gpt2": {"source": "566f9ca64130152b", "bytes_per_step": 42661705, "read": 42481481, "written": 180224},
-    "llama_long": {"source": "566f9ca64130152b", "bytes_per_step": 202147049, "read": 202007785, "written": 139264},
-    "ragged": {"source": "566f9ca64130152b", "bytes_per_step": 402881626, "read": 401385788, "written": 1495838},
+    "tinyllama": {"source": "f13d5c42e4084c34", "bytes_per_step": 22883188, "read": 22193012, "written": 690176},
+    "tiny": {"source": "f13d5c42e4084c34", "bytes_per_step": 566019, "read": 564739, "written": 1280},
+    "gpt2": {"source": "f13d5c42e4084c34", "bytes_per_step": 42663431, "read": 42483207, "written": 180224},
+    "llama_long": {"source": "f13d5c42e4084c34", "bytes_per_step": 202179980, "read": 202040716, "written": 139264},
+    "ragged": {"source": "f13d5c42e4084c34", "bytes_per_step": 402990046, "read": 401494294, "written": 1495752},
+    "tinyllama:fp8e4m3": {"source": "f13d5c42e4084c34", "bytes_per_step": 12415531, "read": 11725355, "written": 690176},
+    "llama_long:fp8e4m3": {"source": "f13d5c42e4084c34", "bytes_per_step": 101446688, "read": 101307424, "written": 139264},
+    "ragged:fp8e4m3": {"source": "f13d5c42e4084c34", "bytes_per_step": 204170223, "read": 202816704, "written": 1353519},
 }
 
 

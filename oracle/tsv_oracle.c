@@ -96,13 +96,28 @@ static float half_lookup(uint16_t h) {
   return half_table[h];
 }
 
-static float kv_get(const void* base, int64_t i, int dtype) {
+/* every E4M3 code decoded once by fp8_bits_to_float */
+static float fp8_table[256];
+static int fp8_table_ready = 0;
+
+static float fp8_lookup(uint8_t b) {
+  if (!fp8_table_ready) {
+    for (uint32_t i = 0; i < 256; ++i) fp8_table[i] = fp8_bits_to_float((uint8_t)i);
+    fp8_table_ready = 1;
+  }
+  return fp8_table[b];
+}
+
+/* Element i of a KV-dtype array as float.  Inlined into every loop that
+ * reads the pools (a call per element would double the oracle's run time). */
+static inline __attribute__((always_inline)) float kv_get(const void* base, int64_t i,
+                                                          int dtype) {
   if (dtype == TSVO_F32) {
     float f;
     memcpy(&f, (const char*)base + 4 * i, 4);
     return f;
   }
-  if (dtype == TSVO_FP8) return fp8_bits_to_float(((const uint8_t*)base)[i]);
+  if (dtype == TSVO_FP8) return fp8_lookup(((const uint8_t*)base)[i]);
   uint16_t h;
   memcpy(&h, (const char*)base + 2 * i, 2);
   return dtype == TSVO_F16 ? half_lookup(h) : bf16_bits_to_float(h);
