@@ -3,7 +3,8 @@
 Each case plants one mistake in a copy of the oracle's C source (a flipped
 comparison, a different summation order, a dropped term or token, a wrong
 tie rule, ...), builds it with gcc in a temporary directory and runs the pin
-suite against that library in a child process: at least one pin must fail.
+suite and the hand-derived golden cases against that library in a child
+process: at least one of them must fail.
 The oracle itself is never modified.
 """
 import os
@@ -68,7 +69,8 @@ MUTATIONS = [
 
 
 def _pins_against(source_text, tmp_path):
-    """Build `source_text` as the oracle library and run the pins against it."""
+    """Build `source_text` as the oracle library and run the pins and the
+    golden cases (CPU) against it."""
     mutated = tmp_path / "tsv_oracle_mut.c"
     mutated.write_text(source_text)
     lib = tmp_path / "libtsv_oracle_mut.so"
@@ -77,7 +79,9 @@ def _pins_against(source_text, tmp_path):
                     "-lm"], check=True)
     env = dict(os.environ, TSV_ORACLE_LIB=str(lib))
     return subprocess.run([sys.executable, "-m", "pytest", "-q", "-x", "-p", "no:cacheprovider",
-                           os.path.join(ROOT, "tests", "test_oracle_pins.py")],
+                           "-m", "not gpu",
+                           os.path.join(ROOT, "tests", "test_oracle_pins.py"),
+                           os.path.join(ROOT, "tests", "test_golden.py")],
                           cwd=ROOT, env=env, capture_output=True, text=True, timeout=300)
 
 
