@@ -3,9 +3,10 @@
 Bars: page boxes equal by value, page scores bit-equal (-0 stored as +0),
 selections and counts bit-exact, outputs within max-abs 1e-5 (fp32 KV) or
 2e-3 (fp16 / bf16 / fp8 KV: the stored values are exact in every path, the
-tolerance covers the attention arithmetic).  The five decode configurations run at their full
-sizes in the launch configuration the benchmark times; smaller variants add
-ragged tails, several tiles per row and the method's degenerate cases.
+tolerance covers the attention arithmetic).  The five decode configurations
+run at their full sizes in the launch configuration the benchmark times;
+smaller variants add ragged tails, several tiles per row and the method's
+degenerate cases.
 """
 import numpy as np
 import pytest
@@ -236,6 +237,84 @@ def test_graph_replay_matches_eager():
         say(f"  replay {i}")
         assert torch.equal(sel, ref[0]) and torch.equal(cnt, ref[1])
         assert torch.equal(out.view(torch.int32), ref[2].view(torch.int32))
+
+
+def test_multi_layer_graph_with_per_layer_budgets():
+    """Four layers of a decode step, each with its own pools, KV type, budget
+    and selection options, captured in one HIP graph: every eager layer
+    matches the oracle, every replay (eager work and synchronisations
+    between replays) reproduces the eager results bit for bit."""
+    import torch
+
+    import query_aware_sparse_bbox_amd as T
+    from workloads import device as WD
+
+    specs = [  # (KV type, k_max, per-sequence budgets?, n_sink, n_recent, group_agg)
+        (W.BF16, 24, True, 0, 0, 0),
+        (W.BF16, 16, False, 0, 0, 1),
+        (W.F8, 32, True, 1, 2, 0),
+        (W.F16, 8, False, 1, 1, 1),
+    ]
+    layers = []
+    for i, (dt, k_max, per_seq, n_sink, n_recent, agg) in enumerate(specs):
+        wl = W.make("tinyllama", seed=500 + i, batch=4, context=1500, kv_dtype=dt)
+        sh = wl.shape
+        kps = wl.k_per_seq if per_seq else None
+        if kps is not None:
+            kps = np.minimum(kps, k_max).astype(np.int32)
+        o = oracle_run(wl, k_max=k_max, k_per_seq=kps, n_sink=n_sink, n_recent=n_recent,
+                       group_agg=agg)
+        d = WD.upload(wl)
+        T.tsv_meta_build(sh, d.k_pool, d.meta, d.block_table, d.seq_lens)
+        B, Hq, Hkv, D = sh.batch, sh.num_q_heads, sh.num_kv_heads, sh.head_dim
+        L = dict(wl=wl, sh=sh, d=d, o=o, k_max=k_max, kps=WD.i32(kps), n_sink=n_sink,
+                 n_recent=n_recent, agg=agg,
+                 sel=torch.empty((B, Hkv, k_max), dtype=torch.int32, device="cuda"),
+                 cnt=torch.empty((B, Hkv), dtype=torch.int32, device="cuda"),
+                 sc=torch.empty((B, Hkv, sh.max_pages_per_seq), device="cuda"),
+                 out=torch.empty((B, Hq, D), device="cuda"), ws=T.new_workspace(sh, k_max))
+        layers.append(L)
+
+    def step():
+        for L in layers:
+            d = L["d"]
+            T.tsv_decode_step_ex(L["sh"], d.q, None, None, d.k_pool, d.v_pool, d.meta,
+                                 d.block_table, d.seq_lens, L["k_max"], L["kps"], L["n_sink"],
+                                 L["n_recent"], L["agg"], L["wl"].scale, L["sel"], L["cnt"],
+                                 L["sc"], L["out"], L["ws"])
+
+    def results():
+        return [(L["sel"].cpu().numpy(), L["cnt"].cpu().numpy(), L["sc"].cpu().numpy(),
+                 L["out"].cpu().numpy()) for L in layers]
+
+    step()
+    torch.cuda.synchronize()
+    eager = results()
+    for i, (L, (sel, cnt, sc, out)) in enumerate(zip(layers, eager)):
+        g = dict(meta=WD.kv_numpy(L["d"].meta, L["sh"].kv_dtype), sel=sel, cnt=cnt, scores=sc,
+                 out=out)
+        err = compare(L["wl"], g, L["o"])
+        say(f"  layer {i}: k_max {L['k_max']}, max-abs err {err:.2e}")
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for r in range(3):
+        for L in layers:
+            L["sel"].fill_(-5)
+            L["out"].fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for (a_sel, a_cnt, a_sc, a_out), (b_sel, b_cnt, b_sc, b_out) in zip(eager, results()):
+            assert np.array_equal(a_sel, b_sel) and np.array_equal(a_cnt, b_cnt)
+            assert np.array_equal(a_out.view(np.uint32), b_out.view(np.uint32))
+        say(f"  replay {r} equals eager")
 
 
 def test_bitwise_deterministic():
