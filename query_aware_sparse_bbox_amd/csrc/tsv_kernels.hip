@@ -346,9 +346,9 @@ struct SelectLds {
   int scan[NT / 64];
 };
 
-// Top-K of one row by a whole workgroup.  Pages [0, f) are always kept; the
-// other R = keff - f slots take the largest order keys among pages [f, n),
-// equal keys lowest page first.
+// Top-K of one row by a whole workgroup.  Pages [0, f) and [n - r, n) are
+// always kept; the other R = keff - f - r slots take the largest order keys
+// among pages [f, n - r), equal keys lowest page first.
 //
 // Thread t owns the m = ceil(n/NT) consecutive pages [t*m, t*m + m) and keeps
 // their keys in registers.  The threshold is found most-significant digit
@@ -588,8 +588,11 @@ __device__ __forceinline__ void score_pages(const float* __restrict__ q,
   };
   // a ring of DEPTH batches in flight: batch bi's slot is refilled with
   // batch bi + DEPTH*bstride right after bi is scored (indices past the
-  // last batch reload the last one, so the loads need no branch)
-  constexpr int DEPTH = U == 1 ? 4 : 2;
+  // last batch reload the last one, so the loads need no branch).  fp8 lanes
+  // load 8 bytes, so their ring is twice as deep for the same bytes in flight
+  // (single-row batches only: four-row batches would not fit 1024-thread
+  // workgroups' registers).
+  constexpr int DEPTH = U == 1 ? 4 * (16 / (C * EB)) : 2;
   if (bstart >= nbatch) return;
   uint4 rmn[DEPTH][U], rmx[DEPTH][U];
 #pragma unroll
@@ -1723,6 +1726,8 @@ hipError_t by_dt_d_g(const Dims& d, Fn&& fn) {
 }
 
 constexpr int kDecodeThreads = 256;
+// Rows at least this many: every row of the phased score is one workgroup.
+constexpr int kScoreRowsOneWorkgroup = 256;
 
 int ilog2(int x) {
   int r = 0;
@@ -1819,10 +1824,7 @@ hipError_t launch_score_select(const Dims& d, const float* q, const void* meta,
     // enough rows to fill the chip: one streaming workgroup per row, top-K in
     // place; otherwise split every row over several workgroups
     const int batches = (d.MP + PB - 1) / PB;
-#ifndef TSV_SCORE_ROWS_ONE_WG
-#define TSV_SCORE_ROWS_ONE_WG 256
-#endif
-    const int NS = units >= TSV_SCORE_ROWS_ONE_WG
+    const int NS = units >= kScoreRowsOneWorkgroup
                        ? 1
                        : std::max(1, std::min(batches, (512 + units - 1) / units));
     const size_t shmem = 2 * sizeof(uint32_t) * (size_t)d.MP;
