@@ -66,14 +66,14 @@ KERNEL_SOURCES = [os.path.join(ROOT, "query_aware_sparse_bbox_amd", "csrc", f)
 # hex digits).  Keys: configuration, or configuration:KV type when the
 # configuration's KV type is overridden.
 TRAFFIC = {
-    "tinyllama": {"source": "f13d5c42e4084c34", "bytes_per_step": 22883188, "read": 22193012, "written": 690176},
-    "tiny": {"source": "f13d5c42e4084c34", "bytes_per_step": 566019, "read": 564739, "written": 1280},
-    "gpt2": {"source": "f13d5c42e4084c34", "bytes_per_step": 42663431, "read": 42483207, "written": 180224},
-    "llama_long": {"source": "f13d5c42e4084c34", "bytes_per_step": 202179980, "read": 202040716, "written": 139264},
-    "ragged": {"source": "f13d5c42e4084c34", "bytes_per_step": 402990046, "read": 401494294, "written": 1495752},
-    "tinyllama:fp8e4m3": {"source": "f13d5c42e4084c34", "bytes_per_step": 12415531, "read": 11725355, "written": 690176},
-    "llama_long:fp8e4m3": {"source": "f13d5c42e4084c34", "bytes_per_step": 101446688, "read": 101307424, "written": 139264},
-    "ragged:fp8e4m3": {"source": "f13d5c42e4084c34", "bytes_per_step": 204170223, "read": 202816704, "written": 1353519},
+    "tinyllama": {"source": "d7928a1ee7236120", "bytes_per_step": 22874839, "read": 22184663, "written": 690176},
+    "tiny": {"source": "d7928a1ee7236120", "bytes_per_step": 563459, "read": 562179, "written": 1280},
+    "gpt2": {"source": "d7928a1ee7236120", "bytes_per_step": 42650226, "read": 42470002, "written": 180224},
+    "llama_long": {"source": "d7928a1ee7236120", "bytes_per_step": 202173638, "read": 202034374, "written": 139264},
+    "ragged": {"source": "d7928a1ee7236120", "bytes_per_step": 402929022, "read": 401433400, "written": 1495621},
+    "tinyllama:fp8e4m3": {"source": "d7928a1ee7236120", "bytes_per_step": 12498696, "read": 11808520, "written": 690176},
+    "llama_long:fp8e4m3": {"source": "d7928a1ee7236120", "bytes_per_step": 101440454, "read": 101301190, "written": 139264},
+    "ragged:fp8e4m3": {"source": "d7928a1ee7236120", "bytes_per_step": 204259017, "read": 202904924, "written": 1354093},
 }
 
 
