@@ -556,6 +556,43 @@ def test_scale_zero_gives_mean_of_selected_values():
             assert np.allclose(out[b, h], mean, rtol=1e-6, atol=1e-7)
 
 
+def test_constant_values_give_that_constant():
+    """Every selected token carrying the same V row: out is that row, for any
+    query and any selection (softmax weights sum to one)."""
+    wl = W.make("ragged", batch=3, lens_range=(40, 400), append_steps=0)
+    sh = wl.shape
+    row = np.linspace(-2, 2, sh.head_dim).astype(np.float32)   # exact in fp16
+    wl.v_pool[...] = W.to_storage(np.broadcast_to(row, wl.v_pool.shape), sh.kv_dtype)
+    meta = O.meta_build(sh, wl.k_pool, wl.block_table, wl.seq_lens)
+    _, cnt, _, out = O.decode_step(sh, wl.q, wl.k_pool, wl.v_pool, meta, wl.block_table,
+                                   wl.seq_lens, wl.k_max, wl.scale, wl.k_per_seq)
+    want = W.storage_to_f32(W.to_storage(row, sh.kv_dtype), sh.kv_dtype)
+    assert np.all(cnt > 0)
+    assert np.allclose(out, want[None, None, :], rtol=0, atol=1e-6)
+
+
+def test_fma_form_of_the_term_is_bit_identical():
+    """The per-channel term max(fl(q*mn), fl(q*mx)) equals the one-product
+    form fl(q * (mx if q >= 0 else mn)) (the form a GPU evaluates as
+    fma(min(q, 0), mn, max(q, 0) * mx)) on random triples with mn <= mx,
+    signed zeros and wide exponents included; -0 compared as +0."""
+    rng = np.random.default_rng(11)
+    n = 200000
+    a = (rng.standard_normal(n) * np.exp2(rng.integers(-30, 30, n))).astype(np.float32)
+    c = (rng.standard_normal(n) * np.exp2(rng.integers(-30, 30, n))).astype(np.float32)
+    q = (rng.standard_normal(n) * np.exp2(rng.integers(-30, 30, n))).astype(np.float32)
+    q[:100] = 0.0
+    q[100:200] = -0.0
+    a[200:300] = 0.0
+    mn, mx = np.minimum(a, c), np.maximum(a, c)
+    with np.errstate(over="ignore"):
+        lhs = np.maximum(q * mn, q * mx)
+        rhs = np.where(q >= 0, q * mx, q * mn)
+    lhs[lhs == 0] = 0.0
+    rhs[rhs == 0] = 0.0
+    assert np.array_equal(lhs.view(np.uint32), rhs.view(np.uint32))
+
+
 def test_single_token_returns_its_value():
     rng = np.random.default_rng(1)
     keys = rng.normal(size=(1, 1, 1, 64))
