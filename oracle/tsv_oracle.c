@@ -40,7 +40,7 @@
 /* ------------------------------------------------------------------------- */
 
 static size_t elem_bytes(int dtype) {
-  return dtype == TSVO_F32 ? 4u : dtype == TSVO_FP8 ? 1u : 2u;
+  return dtype == TSVO_F32 ? 4u : (dtype == TSVO_FP8 || dtype == TSVO_FP8_E5M2) ? 1u : 2u;
 }
 
 /* IEEE 754 binary16 -> float, from the format's definition. */
@@ -96,16 +96,36 @@ static float half_lookup(uint16_t h) {
   return half_table[h];
 }
 
-/* every E4M3 code decoded once by fp8_bits_to_float */
-static float fp8_table[256];
-static int fp8_table_ready = 0;
+/* OCP FP8 E5M2 -> float, from the format's definition: exponent field e
+ * (bias 15), mantissa m; e = 0 is subnormal (m/4 * 2^-14); e = 31 is infinity
+ * (m = 0) or NaN. */
+static float e5m2_bits_to_float(uint8_t b) {
+  int sign = (b >> 7) & 1;
+  int e = (b >> 2) & 0x1f;
+  int m = b & 3;
+  double v;
+  if (e == 31)
+    v = m ? NAN : INFINITY;
+  else if (e == 0)
+    v = ldexp((double)m, -16); /* m/4 * 2^-14 */
+  else
+    v = ldexp((double)(4 + m), e - 17); /* (1 + m/4) * 2^(e-15) */
+  return (float)(sign ? -v : v);
+}
 
-static float fp8_lookup(uint8_t b) {
-  if (!fp8_table_ready) {
-    for (uint32_t i = 0; i < 256; ++i) fp8_table[i] = fp8_bits_to_float((uint8_t)i);
-    fp8_table_ready = 1;
+/* every E4M3 / E5M2 code decoded once */
+static float fp8_table[256], e5m2_table[256];
+static int fp8_tables_ready = 0;
+
+static float fp8_lookup(uint8_t b, int dtype) {
+  if (!fp8_tables_ready) {
+    for (uint32_t i = 0; i < 256; ++i) {
+      fp8_table[i] = fp8_bits_to_float((uint8_t)i);
+      e5m2_table[i] = e5m2_bits_to_float((uint8_t)i);
+    }
+    fp8_tables_ready = 1;
   }
-  return fp8_table[b];
+  return dtype == TSVO_FP8 ? fp8_table[b] : e5m2_table[b];
 }
 
 /* Element i of a KV-dtype array as float.  Inlined into every loop that
@@ -117,7 +137,8 @@ static inline __attribute__((always_inline)) float kv_get(const void* base, int6
     memcpy(&f, (const char*)base + 4 * i, 4);
     return f;
   }
-  if (dtype == TSVO_FP8) return fp8_lookup(((const uint8_t*)base)[i]);
+  if (dtype == TSVO_FP8 || dtype == TSVO_FP8_E5M2)
+    return fp8_lookup(((const uint8_t*)base)[i], dtype);
   uint16_t h;
   memcpy(&h, (const char*)base + 2 * i, 2);
   return dtype == TSVO_F16 ? half_lookup(h) : bf16_bits_to_float(h);
@@ -141,7 +162,7 @@ static int shape_ok(const tsvo_shape* s) {
     return 0;
   if (s->num_q_heads % s->num_kv_heads) return 0;
   if (s->head_dim & (s->head_dim - 1)) return 0; /* tree needs a power of 2 */
-  if (s->kv_dtype < TSVO_F32 || s->kv_dtype > TSVO_FP8) return 0;
+  if (s->kv_dtype < TSVO_F32 || s->kv_dtype > TSVO_FP8_E5M2) return 0;
   return 1;
 }
 

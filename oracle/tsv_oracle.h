@@ -36,10 +36,12 @@
 extern "C" {
 #endif
 
-/* KV storage formats: IEEE binary32, IEEE binary16, bfloat16, and OCP FP8
+/* KV storage formats: IEEE binary32, IEEE binary16, bfloat16, OCP FP8
  * E4M3 (1 sign, 4 exponent bits with bias 7, 3 mantissa bits; no
- * infinities, 0x7F / 0xFF are NaN, largest finite 448). */
-enum { TSVO_F32 = 0, TSVO_F16 = 1, TSVO_BF16 = 2, TSVO_FP8 = 3 };
+ * infinities, 0x7F / 0xFF are NaN, largest finite 448) and OCP FP8 E5M2
+ * (1 sign, 5 exponent bits with bias 15, 2 mantissa bits; exponent field 31
+ * holds infinities and NaNs as in IEEE, largest finite 57344). */
+enum { TSVO_F32 = 0, TSVO_F16 = 1, TSVO_BF16 = 2, TSVO_FP8 = 3, TSVO_FP8_E5M2 = 4 };
 
 typedef struct {
   int32_t batch, num_q_heads, num_kv_heads, head_dim, page_size,

@@ -61,6 +61,10 @@ MUTATIONS = [
      "v = ldexp((double)(8 + m), e - 10);", "v = ldexp((double)(8 + m), e - 11);"),
     ("fp8 subnormals scaled like normals",
      "v = ldexp((double)m, -9);", "v = ldexp((double)m, -10);"),
+    ("E5M2 exponent bias 16 (the FNUZ variant)",
+     "v = ldexp((double)(4 + m), e - 17);", "v = ldexp((double)(4 + m), e - 18);"),
+    ("E5M2 decoded with the E4M3 table",
+     "return dtype == TSVO_FP8 ? fp8_table[b] : e5m2_table[b];", "return fp8_table[b];"),
     ("selection output in score order",
      "for (int64_t p = 0; p < n; ++p)\n        if (chosen[p]) out[c++] = (int32_t)p;",
      "for (int64_t i = 0; i < keff - f; ++i) out[c++] = cand[i].page;\n"

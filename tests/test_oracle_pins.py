@@ -121,16 +121,23 @@ def test_decoder_every_finite_pattern(dtype):
     assert np.array_equal(sc.view(np.uint32), expect.view(np.uint32))
 
 
-def test_fp8_decoder_every_finite_pattern():
-    """Every finite OCP E4M3 code decodes to torch's float8_e4m3fn value (D = 1)."""
+FP8 = [  # (KV type, torch type name, finite codes, rounding range, saturating code)
+    (W.F8, "float8_e4m3fn", 254, 464, 0x7E),
+    (W.F8E5, "float8_e5m2", 248, 61440, 0x7B),
+]
+
+
+@pytest.mark.parametrize("dt,tname,nfinite,lim,top", FP8, ids=["e4m3", "e5m2"])
+def test_fp8_decoder_every_finite_pattern(dt, tname, nfinite, lim, top):
+    """Every finite OCP fp8 code decodes to torch's value of it (D = 1)."""
     torch = pytest.importorskip("torch")
     codes = np.arange(256, dtype=np.uint8)
-    lib = torch.from_numpy(codes.copy()).view(torch.float8_e4m3fn).float().numpy()
+    lib = torch.from_numpy(codes.copy()).view(getattr(torch, tname)).float().numpy()
     keep = np.isfinite(lib)
-    assert keep.sum() == 254          # 0x7F and 0xFF are the only NaNs
+    assert keep.sum() == nfinite
     codes, vals = codes[keep], lib[keep]
     n = len(codes)
-    sh = W.Shape(1, 1, 1, 1, 1, n, n, W.F8)
+    sh = W.Shape(1, 1, 1, 1, 1, n, n, dt)
     bt = np.arange(n, dtype=np.int32).reshape(1, n)
     lens = np.array([n], dtype=np.int32)
     meta = O.meta_build(sh, codes.reshape(n, 1, 1, 1), bt, lens)
@@ -139,32 +146,33 @@ def test_fp8_decoder_every_finite_pattern():
     expect[expect == 0] = 0.0
     assert np.array_equal(sc.view(np.uint32), expect.view(np.uint32))
     # the generator's widening table agrees with the library too
-    back = W.storage_to_f32(np.arange(256, dtype=np.uint8), W.F8)
-    assert np.array_equal(back[keep].view(np.uint32),
-                          lib[keep].view(np.uint32))
+    back = W.storage_to_f32(np.arange(256, dtype=np.uint8), dt)
+    assert np.array_equal(back[keep].view(np.uint32), lib[keep].view(np.uint32))
 
 
-def test_fp8_rounding_is_nearest_even():
-    """Input rounding to E4M3: torch's conversion inside the finite range
-    (every midpoint included), saturation to +-448 outside it."""
+@pytest.mark.parametrize("dt,tname,nfinite,lim,top", FP8, ids=["e4m3", "e5m2"])
+def test_fp8_rounding_is_nearest_even(dt, tname, nfinite, lim, top):
+    """Input rounding to fp8: torch's conversion inside the finite range
+    (every midpoint included), saturation to the largest finite value outside
+    it."""
     torch = pytest.importorskip("torch")
     rng = np.random.default_rng(8)
-    grid = W.storage_to_f32(np.arange(127, dtype=np.uint8), W.F8).astype(np.float64)
+    grid = W.storage_to_f32(np.arange(top + 1, dtype=np.uint8), dt).astype(np.float64)
     mids = (grid[:-1] + grid[1:]) / 2
-    x = np.concatenate([rng.normal(0, 1, 50000), rng.normal(0, 40, 50000),
+    x = np.concatenate([rng.normal(0, 1, 50000), rng.normal(0, lim / 12, 50000),
                         rng.normal(0, 0.01, 20000), mids, -mids,
                         np.nextafter(mids, 0), np.nextafter(mids, 1e9)]).astype(np.float32)
-    x = x[np.abs(x) < 464]
-    got = W.to_storage(x, W.F8)
-    lib = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    x = x[np.abs(x) < lim]
+    got = W.to_storage(x, dt)
+    lib = torch.from_numpy(x).to(getattr(torch, tname)).view(torch.uint8).numpy()
     assert np.array_equal(got, lib)
     # brute force: the stored value is a nearest grid point
-    v = W.storage_to_f32(got, W.F8).astype(np.float64)
+    v = W.storage_to_f32(got, dt).astype(np.float64)
     sgrid = np.concatenate([-grid[::-1], grid])
     dist = np.abs(x.astype(np.float64)[:, None] - sgrid[None, :]).min(axis=1)
     assert np.array_equal(np.abs(x - v), dist)
-    big = np.array([464, 465, 1e4, -1e30], np.float32)
-    assert W.to_storage(big, W.F8).tolist() == [0x7E, 0x7E, 0x7E, 0xFE]
+    big = np.array([lim, lim + 1, 1e30, -1e30], np.float32)
+    assert W.to_storage(big, dt).tolist() == [top, top, top, top | 0x80]
 
 
 # ----------------------------------------------------------------------------
@@ -334,7 +342,7 @@ def test_group_sum_bounds_the_group_logit_sum():
 # metadata
 # ----------------------------------------------------------------------------
 
-@pytest.mark.parametrize("dtype", [W.F32, W.F16, W.BF16, W.F8])
+@pytest.mark.parametrize("dtype", [W.F32, W.F16, W.BF16, W.F8, W.F8E5])
 def test_box_is_tightest(dtype):
     """Every valid key lies in the box and every face is attained by a valid key."""
     wl = W.make("gpt2", batch=3, context=77, kv_dtype=dtype)
@@ -525,6 +533,7 @@ def dense_attention_f64(wl):
     ("tinyllama", dict(batch=2, context=517)),
     ("ragged", dict(batch=3, lens_range=(30, 200), append_steps=0)),
     ("tinyllama", dict(batch=2, context=300, kv_dtype=W.F8)),
+    ("gpt2", dict(batch=2, context=200, kv_dtype=W.F8E5)),
 ])
 def test_all_pages_equals_dense_attention(name, kw):
     wl = W.make(name, **kw)

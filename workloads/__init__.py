@@ -22,10 +22,12 @@ synthetic with those models' decode shapes:
 
 Storage conventions: fp32 pools are ``float32`` arrays, fp16 pools
 ``float16`` arrays, bf16 pools ``uint16`` arrays holding the bf16 bit
-patterns and fp8 pools ``uint8`` arrays holding OCP E4M3 ("FN") codes: sign,
+patterns and fp8 pools ``uint8`` arrays holding OCP E4M3 ("FN") codes (sign,
 4 exponent bits with bias 7, 3 mantissa bits, no infinities, NaN only at
-magnitude code 0x7F, largest finite 448.  fp8 values are stored unscaled (the
-synthetic keys and values lie well inside its range).  Layouts: pools ``[NP][Hkv][P][D]``, ``q`` ``[B][Hq][D]`` fp32,
+magnitude code 0x7F, largest finite 448) or OCP E5M2 codes (sign, 5 exponent
+bits with bias 15, 2 mantissa bits, infinities and NaNs at exponent field 31,
+largest finite 57344).  fp8 values are stored unscaled (the synthetic keys
+and values lie well inside both ranges).  Layouts: pools ``[NP][Hkv][P][D]``, ``q`` ``[B][Hq][D]`` fp32,
 ``block_table`` ``[B][MP]`` int32, ``seq_lens`` ``[B]`` int32 (length counts
 the token being decoded).
 """
@@ -39,10 +41,10 @@ from typing import Optional
 
 import numpy as np
 
-F32, F16, BF16, F8 = 0, 1, 2, 3
-DTYPE_NAMES = {F32: "f32", F16: "f16", BF16: "bf16", F8: "fp8e4m3"}
-DTYPE_BYTES = {F32: 4, F16: 2, BF16: 2, F8: 1}
-STORAGE_NP = {F32: np.float32, F16: np.float16, BF16: np.uint16, F8: np.uint8}
+F32, F16, BF16, F8, F8E5 = 0, 1, 2, 3, 4
+DTYPE_NAMES = {F32: "f32", F16: "f16", BF16: "bf16", F8: "fp8e4m3", F8E5: "fp8e5m2"}
+DTYPE_BYTES = {F32: 4, F16: 2, BF16: 2, F8: 1, F8E5: 1}
+STORAGE_NP = {F32: np.float32, F16: np.float16, BF16: np.uint16, F8: np.uint8, F8E5: np.uint8}
 
 
 def _e4m3_table() -> np.ndarray:
@@ -55,21 +57,34 @@ def _e4m3_table() -> np.ndarray:
     return np.where(c >= 128, -mag, mag)
 
 
+def _e5m2_table() -> np.ndarray:
+    """Value of every E5M2 code 0..255 (float64), from the format's definition:
+    bias 15, 2 mantissa bits, exponent field 31 = infinity (m = 0) or NaN."""
+    c = np.arange(256)
+    e = (c >> 2) & 0x1F
+    m = (c & 3).astype(np.float64)
+    mag = np.where(e == 0, m * 2.0 ** -16, (4.0 + m) * np.exp2(e - 17.0))
+    mag = np.where(e == 31, np.where(m == 0, np.inf, np.nan), mag)
+    return np.where(c >= 128, -mag, mag)
+
+
 _E4M3 = _e4m3_table()
-_E4M3_POS = _E4M3[:127]                                  # codes 0..126, increasing
-_E4M3_MID = (_E4M3_POS[:-1] + _E4M3_POS[1:]) / 2.0       # exact in float64
+_E5M2 = _e5m2_table()
 
 
-def _to_e4m3(x: np.ndarray) -> np.ndarray:
-    """float32 -> E4M3 code: nearest value, ties to the even code, |x| > 448
-    saturates to 448, NaN -> 0x7F (sign kept)."""
+def _round_to_fp8(x: np.ndarray, table: np.ndarray, top: int, nan_code: int) -> np.ndarray:
+    """float32 -> fp8 code: nearest finite value (codes 0..top increase with
+    the value), ties to the even code, magnitudes beyond the largest finite
+    value saturate to it, NaN -> nan_code (sign kept)."""
+    pos = table[:top + 1]
+    mid = (pos[:-1] + pos[1:]) / 2.0                      # exact in float64
     a = np.abs(x.astype(np.float64))
-    lo = np.clip(np.searchsorted(_E4M3_MID, a, side="left"), 0, 126)
+    lo = np.clip(np.searchsorted(mid, a, side="left"), 0, top)
     # lo = number of midpoints strictly below a: a lies in (mid[lo-1], mid[lo]]
-    hi = np.minimum(lo + 1, 126)
-    tie = (lo < 126) & (a == _E4M3_MID[np.minimum(lo, 125)])
+    hi = np.minimum(lo + 1, top)
+    tie = (lo < top) & (a == mid[np.minimum(lo, top - 1)])
     code = np.where(tie & (lo % 2 == 1), hi, lo)
-    code = np.where(np.isnan(a), 0x7F, code).astype(np.uint8)
+    code = np.where(np.isnan(a), nan_code, code).astype(np.uint8)
     return code | (np.signbit(x).astype(np.uint8) << 7)
 
 
@@ -137,7 +152,9 @@ def to_storage(x: np.ndarray, dtype: int) -> np.ndarray:
         u = (u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)
         return u.astype(np.uint16)
     if dtype == F8:
-        return _to_e4m3(x)
+        return _round_to_fp8(x, _E4M3, 0x7E, 0x7F)
+    if dtype == F8E5:
+        return _round_to_fp8(x, _E5M2, 0x7B, 0x7F)
     raise ValueError(f"unknown kv dtype {dtype}")
 
 
@@ -149,8 +166,9 @@ def storage_to_f32(a: np.ndarray, dtype: int) -> np.ndarray:
         return np.asarray(a, dtype=np.float16).astype(np.float32)
     if dtype == BF16:
         return (np.asarray(a, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
-    if dtype == F8:
-        return _E4M3[np.asarray(a, dtype=np.uint8)].astype(np.float32)
+    if dtype in (F8, F8E5):
+        t = _E4M3 if dtype == F8 else _E5M2
+        return t[np.asarray(a, dtype=np.uint8)].astype(np.float32)
     raise ValueError(f"unknown kv dtype {dtype}")
 
 

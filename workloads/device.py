@@ -1,7 +1,7 @@
 """Upload a seeded workload to the GPU as torch tensors (plumbing only).
 
 KV pools keep their storage bytes: fp32 -> float32, fp16 -> float16, bf16
-bit patterns -> bfloat16 (same 16 bits), fp8 E4M3 codes -> uint8.  Nothing of the method is computed.
+bit patterns -> bfloat16 (same 16 bits), fp8 codes (E4M3, E5M2) -> uint8.  Nothing of the method is computed.
 """
 from __future__ import annotations
 
@@ -10,9 +10,10 @@ from types import SimpleNamespace
 import numpy as np
 import torch
 
-from . import BF16, F8, F16, F32, Workload
+from . import BF16, F8, F8E5, F16, F32, Workload
 
-TORCH_KV = {F32: torch.float32, F16: torch.float16, BF16: torch.bfloat16, F8: torch.uint8}
+TORCH_KV = {F32: torch.float32, F16: torch.float16, BF16: torch.bfloat16, F8: torch.uint8,
+            F8E5: torch.uint8}
 
 
 def kv_tensor(a: np.ndarray, dtype: int, device="cuda") -> torch.Tensor:
