@@ -65,11 +65,19 @@ extern "C" {
 
 /* KV storage types.  TSV_FP8_E4M3 is the OCP 8-bit float E4M3 ("FN"): sign,
    4 exponent bits (bias 7), 3 mantissa bits, no infinities, NaN only at
-   magnitude 0x7F, largest finite value 448.  Values are used as stored (no
-   scale factor); every one of them is exact in fp32 and bf16, so the page
-   boxes and scores are exact functions of the stored codes as for the other
-   types.  Box metadata is kept in the KV type. */
-typedef enum { TSV_F32 = 0, TSV_F16 = 1, TSV_BF16 = 2, TSV_FP8_E4M3 = 3 } tsv_dtype;
+   magnitude 0x7F, largest finite value 448.  TSV_FP8_E5M2 is the OCP E5M2:
+   sign, 5 exponent bits (bias 15), 2 mantissa bits, infinities and NaNs at
+   exponent field 31 as in IEEE, largest finite value 57344.  Values are used
+   as stored (no scale factor); every one of them is exact in fp32 and bf16,
+   so the page boxes and scores are exact functions of the stored codes as
+   for the other types.  Box metadata is kept in the KV type. */
+typedef enum {
+  TSV_F32 = 0,
+  TSV_F16 = 1,
+  TSV_BF16 = 2,
+  TSV_FP8_E4M3 = 3,
+  TSV_FP8_E5M2 = 4
+} tsv_dtype;
 
 typedef struct {
   int32_t batch;

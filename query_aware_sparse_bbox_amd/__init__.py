@@ -21,7 +21,7 @@ if not os.path.exists(LIB_PATH):
 
 _lib = ctypes.CDLL(LIB_PATH)
 
-TSV_F32, TSV_F16, TSV_BF16, TSV_FP8_E4M3 = 0, 1, 2, 3
+TSV_F32, TSV_F16, TSV_BF16, TSV_FP8_E4M3, TSV_FP8_E5M2 = 0, 1, 2, 3, 4
 TSV_OK, TSV_ERR_INVALID_ARG, TSV_ERR_UNSUPPORTED, TSV_ERR_HIP = 0, -1, -2, -3
 TSV_AGG_MAX, TSV_AGG_SUM = 0, 1
 

@@ -24,7 +24,7 @@ int check_shape(const tsv_shape* s, Dims* d) {
   if (s->num_q_heads % s->num_kv_heads) return TSV_ERR_INVALID_ARG;
   const int G = s->num_q_heads / s->num_kv_heads;
   if (s->kv_dtype != TSV_F32 && s->kv_dtype != TSV_F16 && s->kv_dtype != TSV_BF16 &&
-      s->kv_dtype != TSV_FP8_E4M3)
+      s->kv_dtype != TSV_FP8_E4M3 && s->kv_dtype != TSV_FP8_E5M2)
     return TSV_ERR_UNSUPPORTED;
   if (s->head_dim != 64 && s->head_dim != 128) return TSV_ERR_UNSUPPORTED;
   if (s->page_size != 8 && s->page_size != 16 && s->page_size != 32 &&

@@ -55,10 +55,18 @@ __device__ __forceinline__ uint4 ldb(const void* p) {
   }
 }
 
-// Four OCP E4M3 values (bytes 0..3 of w) widened to fp32, exactly.
+// Four OCP fp8 values (bytes 0..3 of w; E4M3 for DT_F8, E5M2 for DT_F8E5)
+// widened to fp32, exactly.
+template <int DT>
 __device__ __forceinline__ void fp8x4_to_f32(uint32_t w, float* f) {
-  const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
-  const f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
+  f32x2 a, b;
+  if constexpr (DT == DT_F8) {
+    a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+    b = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
+  } else {
+    a = __builtin_amdgcn_cvt_pk_f32_bf8((int)w, false);
+    b = __builtin_amdgcn_cvt_pk_f32_bf8((int)w, true);
+  }
   f[0] = a.x;
   f[1] = a.y;
   f[2] = b.x;
@@ -78,9 +86,9 @@ __device__ __forceinline__ void unpack(const uint4 r, float* f) {
       f[2 * i] = __uint_as_float(w[i] << 16);
       f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
     }
-  } else if constexpr (DT == DT_F8) {
+  } else if constexpr (is_fp8(DT)) {
 #pragma unroll
-    for (int i = 0; i < C / 4; ++i) fp8x4_to_f32(w[i], f + 4 * i);
+    for (int i = 0; i < C / 4; ++i) fp8x4_to_f32<DT>(w[i], f + 4 * i);
   } else {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -96,20 +104,21 @@ __device__ __forceinline__ float elem_to_f32(uint32_t bits) {
   if constexpr (DT == DT_F32) return __uint_as_float(bits);
   else if constexpr (DT == DT_BF16) return __uint_as_float(bits << 16);
   else if constexpr (DT == DT_F8) return __builtin_amdgcn_cvt_f32_fp8((int)bits, 0);
+  else if constexpr (DT == DT_F8E5) return __builtin_amdgcn_cvt_f32_bf8((int)bits, 0);
   else return (float)__builtin_bit_cast(_Float16, (uint16_t)bits);
 }
 
 template <int DT>
 __device__ __forceinline__ uint32_t load_elem(const void* base, size_t i) {
   if constexpr (DT == DT_F32) return reinterpret_cast<const uint32_t*>(base)[i];
-  else if constexpr (DT == DT_F8) return reinterpret_cast<const uint8_t*>(base)[i];
+  else if constexpr (is_fp8(DT)) return reinterpret_cast<const uint8_t*>(base)[i];
   else return reinterpret_cast<const uint16_t*>(base)[i];
 }
 
 template <int DT>
 __device__ __forceinline__ void store_elem(void* base, size_t i, uint32_t bits) {
   if constexpr (DT == DT_F32) reinterpret_cast<uint32_t*>(base)[i] = bits;
-  else if constexpr (DT == DT_F8) reinterpret_cast<uint8_t*>(base)[i] = (uint8_t)bits;
+  else if constexpr (is_fp8(DT)) reinterpret_cast<uint8_t*>(base)[i] = (uint8_t)bits;
   else reinterpret_cast<uint16_t*>(base)[i] = (uint16_t)bits;
 }
 
@@ -1179,8 +1188,8 @@ __global__ __launch_bounds__(NT) void k_decode_split(
 }
 
 // ---------------------------------------------------------------------------
-// K2 for grouped-query heads (G = 4, 8) on 16-bit KV: both contractions on
-// MFMA, 16 tokens per wave step
+// K2 for grouped-query heads (G = 4, 8) on 16-bit or fp8 KV: both
+// contractions on MFMA, 16 tokens per wave step (fp8 widened to bf16)
 // ---------------------------------------------------------------------------
 //
 // Both fp32 operands that meet a 16-bit KV operand (q, and the
@@ -1246,12 +1255,15 @@ struct Mma<DT_F16> {
   static __device__ __forceinline__ short bits(elem x) { return __builtin_bit_cast(short, x); }
 };
 
-// Two OCP E4M3 values (bytes 0, 1 of w, or 2, 3 with HI) as a bf16 pair,
-// low half first, in one conversion (scale 1).  Exact: every E4M3 value is
-// a bf16 value.
-template <bool HI>
+// Two OCP fp8 values (bytes 0, 1 of w, or 2, 3 with HI; E4M3 for DT_F8,
+// E5M2 for DT_F8E5) as a bf16 pair, low half first, in one conversion
+// (scale 1).  Exact: every E4M3 and every E5M2 value is a bf16 value.
+template <int DT, bool HI>
 __device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
-  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w, 1.0f, HI));
+  if constexpr (DT == DT_F8)
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w, 1.0f, HI));
+  else
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8((int)w, 1.0f, HI));
 }
 
 template <int DT>
@@ -1284,7 +1296,7 @@ __device__ __forceinline__ void mfma_decode_range(const float* __restrict__ qg0,
                                                   const TokenList& tl, long t0, long t_end,
                                                   float qscale, float (*s_acc)[G][D + 1],
                                                   float (*s_mw)[G]) {
-  constexpr int MDT = DT == DT_F8 ? DT_BF16 : DT;  // MFMA operand type
+  constexpr int MDT = is_fp8(DT) ? DT_BF16 : DT;  // MFMA operand type
   constexpr int EB = KV<DT>::bytes;
   using M = Mma<MDT>;
   using MD = MfmaDecode<DT, D>;
@@ -1382,8 +1394,8 @@ __device__ __forceinline__ void mfma_decode_range(const float* __restrict__ qg0,
       for (int ch = 0; ch < NCH; ++ch) {
         if constexpr (EB == 1) {
           const KRaw r = c.k[cc][ch];
-          const uint4 kw = {fp8x2_to_bf16x2<false>(r.x), fp8x2_to_bf16x2<true>(r.x),
-                            fp8x2_to_bf16x2<false>(r.y), fp8x2_to_bf16x2<true>(r.y)};
+          const uint4 kw = {fp8x2_to_bf16x2<DT, false>(r.x), fp8x2_to_bf16x2<DT, true>(r.x),
+                            fp8x2_to_bf16x2<DT, false>(r.y), fp8x2_to_bf16x2<DT, true>(r.y)};
           acc = M::mma32(__builtin_bit_cast(vec8, kw), qf[ch], acc);
         } else {
           acc = M::mma32(__builtin_bit_cast(vec8, c.k[cc][ch]), qf[ch], acc);
@@ -1442,8 +1454,8 @@ __device__ __forceinline__ void mfma_decode_range(const float* __restrict__ qg0,
         for (int x = 0; x < VR; ++x) {
           const uint32_t raw = j < c.vlim[cc] ? c.v[cc][j][x] : 0u;
           if constexpr (EB == 1) {
-            w[j][2 * x] = fp8x2_to_bf16x2<false>(raw);
-            w[j][2 * x + 1] = fp8x2_to_bf16x2<true>(raw);
+            w[j][2 * x] = fp8x2_to_bf16x2<DT, false>(raw);
+            w[j][2 * x + 1] = fp8x2_to_bf16x2<DT, true>(raw);
           } else {
             w[j][x] = raw;
           }
@@ -1492,8 +1504,8 @@ __device__ __forceinline__ void mfma_decode_range(const float* __restrict__ qg0,
   }
 }
 
-// Split decode workgroup for grouped-query heads on 16-bit KV: four waves,
-// splits of TPW steps of 64 tokens.
+// Split decode workgroup for grouped-query heads on 16-bit or fp8 KV: four
+// waves, splits of TPW steps of 64 tokens.
 template <int DT, int D, int G>
 __global__ __launch_bounds__(256, D == 128 ? 2 : 3) void k_decode_mfma(
     const float* __restrict__ q, const void* __restrict__ k_pool,
@@ -1701,6 +1713,7 @@ hipError_t by_dtype(int dt, Fn&& fn) {
     case DT_F16: return fn(IC<DT_F16>{});
     case DT_BF16: return fn(IC<DT_BF16>{});
     case DT_F8: return fn(IC<DT_F8>{});
+    case DT_F8E5: return fn(IC<DT_F8E5>{});
   }
   return hipErrorInvalidValue;
 }
@@ -1739,8 +1752,8 @@ size_t round_up(size_t x) { return (x + 255) / 256 * 256; }
 
 }  // namespace
 
-// Grouped-query heads on 16-bit KV take the MFMA decode (64-token steps);
-// everything else the VALU decode.  Both stream TPW steps per workgroup.
+// Grouped-query heads on 16-bit or fp8 KV take the MFMA decode (64-token
+// steps); everything else the VALU decode.  Both stream TPW steps per workgroup.
 bool use_mfma_decode(const Dims& d) {
   return d.dt != DT_F32 && (d.G == 4 || d.G == 8);
 }

@@ -7,13 +7,16 @@
 
 namespace tsv {
 
-enum : int { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2, DT_F8 = 3 };
+// KV types; DT_F8 is OCP E4M3, DT_F8E5 OCP E5M2.
+enum : int { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2, DT_F8 = 3, DT_F8E5 = 4 };
+
+constexpr bool is_fp8(int dt) { return dt == DT_F8 || dt == DT_F8E5; }
 
 // Bytes of one KV element.
-constexpr int kv_bytes(int dt) { return dt == DT_F32 ? 4 : dt == DT_F8 ? 1 : 2; }
+constexpr int kv_bytes(int dt) { return dt == DT_F32 ? 4 : is_fp8(dt) ? 1 : 2; }
 // Consecutive channels of one row a lane loads at once: one 16-byte load, or
 // 8 bytes for fp8 (so a lane holds as many channels as for 16-bit data).
-constexpr int kv_vec(int dt) { return dt == DT_F8 ? 8 : 16 / kv_bytes(dt); }
+constexpr int kv_vec(int dt) { return is_fp8(dt) ? 8 : 16 / kv_bytes(dt); }
 
 // Selection policy of one call: forced sink pages, forced most recent pages,
 // and whether the G query heads' box bounds are summed (else maxed).

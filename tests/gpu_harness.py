@@ -13,7 +13,7 @@ import numpy as np
 import oracle as O
 import workloads as W
 
-TOL = {W.F32: 1e-5, W.F16: 2e-3, W.BF16: 2e-3, W.F8: 2e-3}
+TOL = {W.F32: 1e-5, W.F16: 2e-3, W.BF16: 2e-3, W.F8: 2e-3, W.F8E5: 2e-3}
 
 
 def say(*a):

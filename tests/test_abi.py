@@ -77,7 +77,8 @@ def test_sizes(tsv):
     assert tsv.tsv_meta_bytes(s) == 20 * 2 * 2 * 64 * 2
     assert tsv.tsv_meta_bytes(shape(kv_dtype=0)) == 20 * 2 * 2 * 64 * 4
     assert tsv.tsv_meta_bytes(shape(kv_dtype=3)) == 20 * 2 * 2 * 64 * 1  # fp8 E4M3
-    assert tsv.tsv_meta_bytes(shape(kv_dtype=4)) == 0
+    assert tsv.tsv_meta_bytes(shape(kv_dtype=4)) == 20 * 2 * 2 * 64 * 1  # fp8 E5M2
+    assert tsv.tsv_meta_bytes(shape(kv_dtype=5)) == 0
     ws = tsv.tsv_workspace_bytes(s, 8)
     assert ws > 0 and ws % 256 == 0
     assert tsv.tsv_workspace_bytes(s, 16) >= ws

@@ -34,10 +34,12 @@ def test_full_config(name):
     _case(wl)
 
 
-@pytest.mark.parametrize("name", ["tinyllama", "llama_long", "ragged"])
-def test_full_config_fp8(name):
-    """The same full-size steps with the KV cache stored as fp8 E4M3."""
-    wl = W.make(name, kv_dtype=W.F8)
+@pytest.mark.parametrize("name,dt", [("tinyllama", W.F8), ("llama_long", W.F8),
+                                     ("ragged", W.F8), ("tinyllama", W.F8E5),
+                                     ("ragged", W.F8E5)])
+def test_full_config_fp8(name, dt):
+    """The same full-size steps with the KV cache stored as fp8 (E4M3, E5M2)."""
+    wl = W.make(name, kv_dtype=dt)
     _case(wl)
 
 
@@ -61,13 +63,19 @@ def test_full_config_fp8(name):
     ("gpt2", dict(batch=2, context=700, head_dim=128, kv_dtype=W.F8)),
     ("ragged", dict(batch=6, lens_range=(100, 2000), kv_dtype=W.F8)),
     ("ragged", dict(batch=4, lens_range=(1, 1500), kv_dtype=W.F8, num_q_heads=64)),
+    # fp8 E5M2 KV: MFMA decode (G = 8, 4), VALU decode (G = 1), 8-token pages
+    ("tinyllama", dict(batch=3, context=1001, kv_dtype=W.F8E5)),
+    ("tinyllama", dict(batch=2, context=777, page_size=8, kv_dtype=W.F8E5)),
+    ("gpt2", dict(batch=3, context=500, kv_dtype=W.F8E5)),
+    ("ragged", dict(batch=6, lens_range=(100, 2000), kv_dtype=W.F8E5)),
+    ("llama_long", dict(batch=2, context=3000, kv_dtype=W.F8E5)),
 ])
 def test_small_variants(name, kw):
     wl = W.make(name, **kw)
     _case(wl)
 
 
-@pytest.mark.parametrize("dtype", [W.F32, W.F16, W.BF16, W.F8])
+@pytest.mark.parametrize("dtype", [W.F32, W.F16, W.BF16, W.F8, W.F8E5])
 @pytest.mark.parametrize("G", [1, 4])
 def test_tie_heavy(dtype, G):
     wl = W.tie_heavy(31 + G, kv_dtype=dtype, num_q_heads=2 * G, num_kv_heads=2, context=777,
@@ -124,7 +132,8 @@ def test_poisoned_unused_slots():
     for name, kw in [("gpt2", dict(batch=4, context=301)),
                      ("ragged", dict(batch=8, lens_range=(5, 900))),
                      ("tinyllama", dict(batch=3, context=333, kv_dtype=W.F8)),
-                     ("gpt2", dict(batch=3, context=250, kv_dtype=W.F8))]:
+                     ("gpt2", dict(batch=3, context=250, kv_dtype=W.F8)),
+                     ("tinyllama", dict(batch=3, context=333, kv_dtype=W.F8E5))]:
         wl = W.make(name, **kw)
         W.poison_unused(wl)
         g, _ = _case(wl)
