@@ -66,14 +66,14 @@ KERNEL_SOURCES = [os.path.join(ROOT, "query_aware_sparse_bbox_amd", "csrc", f)
 # hex digits).  Keys: configuration, or configuration:KV type when the
 # configuration's KV type is overridden.
 TRAFFIC = {
-    "tinyllama": {"source": "d7928a1ee7236120", "bytes_per_step": 22874839, "read": 22184663, "written": 690176},
-    "tiny": {"source": "d7928a1ee7236120", "bytes_per_step": 563459, "read": 562179, "written": 1280},
-    "gpt2": {"source": "d7928a1ee7236120", "bytes_per_step": 42650226, "read": 42470002, "written": 180224},
-    "llama_long": {"source": "d7928a1ee7236120", "bytes_per_step": 202173638, "read": 202034374, "written": 139264},
-    "ragged": {"source": "d7928a1ee7236120", "bytes_per_step": 402929022, "read": 401433400, "written": 1495621},
-    "tinyllama:fp8e4m3": {"source": "d7928a1ee7236120", "bytes_per_step": 12498696, "read": 11808520, "written": 690176},
-    "llama_long:fp8e4m3": {"source": "d7928a1ee7236120", "bytes_per_step": 101440454, "read": 101301190, "written": 139264},
-    "ragged:fp8e4m3": {"source": "d7928a1ee7236120", "bytes_per_step": 204259017, "read": 202904924, "written": 1354093},
+    "tinyllama": {"source": "0d0c0663bbc2eea1", "bytes_per_step": 22901515, "read": 22211339, "written": 690176},
+    "tiny": {"source": "0d0c0663bbc2eea1", "bytes_per_step": 552819, "read": 551539, "written": 1280},
+    "gpt2": {"source": "0d0c0663bbc2eea1", "bytes_per_step": 42685976, "read": 42505752, "written": 180224},
+    "llama_long": {"source": "0d0c0663bbc2eea1", "bytes_per_step": 202176501, "read": 202037237, "written": 139264},
+    "ragged": {"source": "0d0c0663bbc2eea1", "bytes_per_step": 402889145, "read": 401393566, "written": 1495579},
+    "tinyllama:fp8e4m3": {"source": "0d0c0663bbc2eea1", "bytes_per_step": 12480041, "read": 11789865, "written": 690176},
+    "llama_long:fp8e4m3": {"source": "0d0c0663bbc2eea1", "bytes_per_step": 101453842, "read": 101314578, "written": 139264},
+    "ragged:fp8e4m3": {"source": "0d0c0663bbc2eea1", "bytes_per_step": 204239420, "read": 202885382, "written": 1354038},
 }
 
 
