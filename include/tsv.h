@@ -106,6 +106,15 @@ enum {
 /* Library version (TSV_VERSION). */
 int tsv_version(void);
 
+/* Testing hook, process-wide.  When a row's step is spread over several
+   workgroups they exchange page scores; a workgroup that finds the others'
+   scores missing after `polls` reads of the row's counter scores the rest of
+   the row itself, which gives bit-identical results (only the time differs).
+   polls >= 0 sets the limit for later calls and returns the previous one;
+   polls < 0 only returns the current one (default 16384).  Tests set 0 to
+   drive that path. */
+int tsv_debug_exchange_polls(int32_t polls);
+
 /* Static description of a status code. */
 const char* tsv_status_string(int status);
 
@@ -117,17 +126,22 @@ size_t tsv_meta_bytes(const tsv_shape* shape);
    tsv_sparse_decode and tsv_decode_step need for rows of k_max selected
    pages; 0 when the shape is invalid or unsupported.  The workspace holds the
    page-score keys, the selected pages' physical indices and the split
-   decode's partial softmax states.  It must be 256-byte aligned and needs no
-   initialisation; calls that may run at the same time (different streams)
-   need separate workspaces. */
+   decode's partial softmax states.  It must be 256-byte aligned.  Its first
+   TSV_WORKSPACE_ZERO_BYTES bytes hold counters through which the workgroups
+   of one row synchronise: they must be zero before the workspace is first
+   used (for example hipMemsetAsync once after allocation), and every call
+   leaves them zero, whatever the shape; the rest needs no initialisation.
+   Calls that may run at the same time (different streams) need separate
+   workspaces. */
+#define TSV_WORKSPACE_ZERO_BYTES 16384
 size_t tsv_workspace_bytes(const tsv_shape* shape, int32_t k_max);
 
 /* Kernel launches one tsv_decode_step makes for `shape` (with_append != 0:
-   with k_new / v_new).  1 or 2 when the whole step of a (sequence, KV head)
-   runs in workgroups of its own, which needs the block-table row and the
-   decode staging to fit 64 KiB of local memory: 1 when each row has one
-   workgroup, 2 when B*Hkv is small enough that each row is spread over
-   several workgroups and a merge pass follows.  Otherwise 3 or 4 (append,
+   with k_new / v_new).  1 when the whole step of a (sequence, KV head) runs
+   in workgroups of its own, which needs the block-table row and the decode
+   staging to fit 64 KiB of local memory (when B*Hkv <= 128 each row may be
+   spread over several workgroups, which share the scoring and merge their
+   shares in the same kernel).  Otherwise 3 or 4 (append,
    score and select, split decode, merge).  0 when the shape is invalid or
    unsupported.  Informational only. */
 int tsv_decode_step_launches(const tsv_shape* shape, int32_t k_max, int32_t with_append);
@@ -192,8 +206,7 @@ int tsv_sparse_decode(const tsv_shape* shape, const float* q,
    out agrees with tsv_sparse_decode within the rounding of a different
    summation order.  Where tsv_decode_step_launches() is 1 or 2, each
    (sequence, KV head) is handled by workgroups of its own that append,
-   score, select and attend in one kernel (plus a merge of the split partial
-   states when 2).  As for tsv_meta_append, the page receiving the new token
+   score, select and attend in one kernel.  As for tsv_meta_append, the page receiving the new token
    must belong to one sequence only. */
 int tsv_decode_step(const tsv_shape* shape, const float* q, const void* k_new,
                     const void* v_new, void* k_pool, void* v_pool, void* meta,

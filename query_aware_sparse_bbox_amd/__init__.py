@@ -28,7 +28,7 @@ TSV_AGG_MAX, TSV_AGG_SUM = 0, 1
 EXPORTS = ("tsv_version", "tsv_status_string", "tsv_meta_bytes", "tsv_workspace_bytes",
            "tsv_decode_step_launches", "tsv_meta_build", "tsv_meta_append",
            "tsv_select_pages", "tsv_sparse_decode", "tsv_decode_step",
-           "tsv_select_pages_ex", "tsv_decode_step_ex")
+           "tsv_select_pages_ex", "tsv_decode_step_ex", "tsv_debug_exchange_polls")
 
 
 class TsvError(RuntimeError):
@@ -59,6 +59,7 @@ _SP = ctypes.POINTER(Shape)
 _OP = ctypes.POINTER(SelectOpts)
 _SIGS = {
     "tsv_version": ([], ctypes.c_int),
+    "tsv_debug_exchange_polls": ([_I], ctypes.c_int),
     "tsv_status_string": ([ctypes.c_int], ctypes.c_char_p),
     "tsv_meta_bytes": ([_SP], _Z),
     "tsv_workspace_bytes": ([_SP, _I], _Z),
@@ -109,6 +110,13 @@ def tsv_version() -> int:
     return _lib.tsv_version()
 
 
+def tsv_debug_exchange_polls(polls: int) -> int:
+    """Testing hook: polls >= 0 sets how long a split row's workgroup waits for
+    the others' page scores before scoring the rest itself (returns the
+    previous limit); polls < 0 returns the current limit."""
+    return _lib.tsv_debug_exchange_polls(int(polls))
+
+
 def status_string(status: int) -> str:
     return _lib.tsv_status_string(status).decode()
 
@@ -150,12 +158,13 @@ def tsv_select_pages(shape, q, meta, block_table, seq_lens, k_max, k_per_seq, n_
 
 
 def new_workspace(shape, k_max, device="cuda"):
-    """A workspace of tsv_workspace_bytes(shape, k_max) bytes (no initialisation needed)."""
+    """A zero-filled workspace of tsv_workspace_bytes(shape, k_max) bytes (its
+    first TSV_WORKSPACE_ZERO_BYTES must start at zero; every call leaves them so)."""
     import torch
     n = tsv_workspace_bytes(shape, k_max)
     if n == 0:
         raise ValueError("shape or k_max not supported")
-    return torch.empty(n, dtype=torch.uint8, device=device)
+    return torch.zeros(n, dtype=torch.uint8, device=device)
 
 
 def tsv_sparse_decode(shape, q, k_pool, v_pool, block_table, seq_lens, sel, sel_count,

@@ -6,6 +6,8 @@
 #include "../../include/tsv.h"
 #include "tsv_launch.h"
 
+static_assert(tsv::kSyncBytes == TSV_WORKSPACE_ZERO_BYTES, "zeroed workspace prefix");
+
 namespace {
 
 using tsv::Dims;
@@ -102,6 +104,10 @@ extern "C" {
 
 int tsv_version(void) { return TSV_VERSION; }
 
+int tsv_debug_exchange_polls(int32_t polls) {
+  return polls < 0 ? tsv::exchange_polls() : tsv::set_exchange_polls(polls);
+}
+
 const char* tsv_status_string(int status) {
   switch (status) {
     case TSV_OK: return "ok";
@@ -127,7 +133,7 @@ size_t tsv_workspace_bytes(const tsv_shape* shape, int32_t k_max) {
 int tsv_decode_step_launches(const tsv_shape* shape, int32_t k_max, int32_t with_append) {
   Dims d;
   if (check_shape(shape, &d) != TSV_OK || k_max < 1) return 0;
-  if (tsv::step_fits(d)) return tsv::step_splits(d, k_max) > 1 ? 2 : 1;
+  if (tsv::step_fits(d)) return 1;
   return (with_append ? 1 : 0) + 1 + 1 + (tsv::decode_splits(d, k_max) > 1 ? 1 : 0);
 }
 

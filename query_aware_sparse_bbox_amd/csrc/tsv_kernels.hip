@@ -4,7 +4,13 @@
 // the keys, a query-to-box score, the highest-scoring pages kept, masked
 // attention over those pages only.
 //
-// Kernels, in the order a decode step runs them:
+// The fused step is one kernel, k_step: every (sequence, KV head) row is
+// handled by workgroups of its own that append, score, select and attend
+// (rows too few to fill the chip are spread over several workgroups, which
+// share the scoring and merge their shares without another launch).
+//
+// Phased kernels (separate select / decode calls, and rows too wide for the
+// one-launch step's local memory), in the order a decode step runs them:
 //   k_meta_append    write the new token, widen its page's box
 //   k_score_select   one workgroup per (sequence, KV head): stream the page
 //                    boxes (coalesced 16-byte rows), score them on the VALU
@@ -20,6 +26,7 @@
 #include <math.h>
 
 #include <algorithm>
+#include <atomic>
 #include <type_traits>
 
 #include "tsv_launch.h"
@@ -210,6 +217,24 @@ __device__ __forceinline__ uint32_t order_key(float s) {
 
 __device__ __forceinline__ float key_to_score(uint32_t k) {
   return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+
+// Device-scope (agent) atomic stores and loads: coherent across every CU and
+// XCD of the GPU without cache-wide maintenance; used for the few words that
+// workgroups of one launch exchange.
+template <class T>
+__device__ __forceinline__ void st_dev(T* p, T v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <class T>
+__device__ __forceinline__ T ld_dev(const T* p) {
+  return __hip_atomic_load(const_cast<T*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Returns once this thread's earlier stores have completed at their scope
+// (s_waitcnt vmcnt(0); the fence keeps the compiler from moving them past).
+__device__ __forceinline__ void stores_done() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), expcnt and lgkmcnt not waited on
 }
 
 __device__ __forceinline__ int clampi(int x, int lo, int hi) {
@@ -812,56 +837,15 @@ __global__ __launch_bounds__(256) void k_merge(
     out[(size_t)gw * D + lane + kWave * i] = l > 0.f ? acc[i] / l : 0.f;
 }
 
-// Merge of the one-workgroup step's splits: every split of a row left a
-// partial state in its slot (one with max -inf when it had no tokens), so one
-// wave per (sequence, query head) reads all S slots in one round of loads.
+// Most workgroups a row of the one-launch step is spread over.
 constexpr int kStepMaxSplits = 8;
-
-template <int D>
-__global__ __launch_bounds__(256) void k_merge_step(const float* __restrict__ partials, int BHq,
-                                                    int S, float* __restrict__ out) {
-  constexpr int PER = D / kWave;
-  const int gw = blockIdx.x * 4 + threadIdx.x / kWave;
-  const int lane = threadIdx.x & (kWave - 1);
-  if (gw >= BHq) return;
-  const float* base = partials + (size_t)gw * S * (D + 2);
-  float m[kStepMaxSplits], l[kStepMaxSplits], a[kStepMaxSplits][PER];
-#pragma unroll
-  for (int s = 0; s < kStepMaxSplits; ++s) {
-    if (s >= S) break;
-    const float* ps = base + (size_t)s * (D + 2);
-    m[s] = ps[D];
-    l[s] = ps[D + 1];
-#pragma unroll
-    for (int i = 0; i < PER; ++i) a[s][i] = ps[lane + kWave * i];
-  }
-  float M = -INFINITY;
-#pragma unroll
-  for (int s = 0; s < kStepMaxSplits; ++s) {
-    if (s >= S) break;
-    M = fmaxf(M, m[s]);
-  }
-  float L = 0.f, acc[PER];
-#pragma unroll
-  for (int i = 0; i < PER; ++i) acc[i] = 0.f;
-#pragma unroll
-  for (int s = 0; s < kStepMaxSplits; ++s) {
-    if (s >= S) break;
-    if (m[s] == -INFINITY) continue;  // an empty slot: its sums were never written
-    const float w = __builtin_amdgcn_exp2f(m[s] - M);
-    L = __builtin_fmaf(w, l[s], L);
-#pragma unroll
-    for (int i = 0; i < PER; ++i) acc[i] = __builtin_fmaf(w, a[s][i], acc[i]);
-  }
-#pragma unroll
-  for (int i = 0; i < PER; ++i) out[(size_t)gw * D + lane + kWave * i] = L > 0.f ? acc[i] / L : 0.f;
-}
 
 // End of a split: wave w left its unnormalised sum in s_acc[w][g][0..D),
 // its denominator in s_acc[w][g][D] and its running max in s_mw[w][g].  A
 // unit covered by one split writes out directly; otherwise the split's
-// (max, denominator, sum) goes to `partials` for k_merge.
-template <int D, int G, int NT, int NW>
+// (max, denominator, sum) goes to `partials` for k_merge (DEV: with
+// device-scope stores, for a merge by another workgroup of the same launch).
+template <int D, int G, int NT, int NW, bool DEV = false>
 __device__ __forceinline__ void finish_split(float (*s_acc)[G][D + 1], float (*s_mw)[G],
                              float* __restrict__ partials, float* __restrict__ out, int b,
                              int h, int Hq, int S_max, int split, int ns) {
@@ -882,7 +866,14 @@ __device__ __forceinline__ void finish_split(float (*s_acc)[G][D + 1], float (*s
       if (d < D) out[((size_t)b * Hq + h * G + g) * D + d] = l > 0.f ? sum / l : 0.f;
     } else {
       float* dst = partials + (((size_t)b * Hq + h * G + g) * S_max + split) * (D + 2);
-      if (d < D) {
+      if constexpr (DEV) {
+        if (d < D) {
+          st_dev(dst + d, sum);
+        } else {
+          st_dev(dst + D, M);
+          st_dev(dst + D + 1, l);
+        }
+      } else if (d < D) {
         dst[d] = sum;
       } else {
         dst[D] = M;
@@ -1553,10 +1544,11 @@ __global__ __launch_bounds__(256, D == 128 ? 2 : 3) void k_decode_mfma(
 // ---------------------------------------------------------------------------
 //
 // [append the new token] -> score every page -> block-wide top-K -> decode
-// the kept pages' tokens with all waves -> combine the waves -> out.  No
-// state crosses workgroups, so the step is one launch with no merge pass; the
+// the kept pages' tokens with all waves -> combine the waves -> out.  The
 // selection stays in LDS between the phases (it is also written to sel /
-// sel_count for the caller).
+// sel_count for the caller).  A row spread over S workgroups exchanges page
+// keys once (each scores 1/S of the pages) and the last of them to finish
+// merges the S partial states, so the step stays one launch.
 // A split of a row covers at least this many 16-token steps per wave.
 constexpr int kStepMinSpanSteps = 2;
 
@@ -1576,6 +1568,88 @@ constexpr size_t step_decode_lds() {
 template <int DT, int D, int G, int NT>
 constexpr int step_min_blocks() { return NT == 256 && (G <= 4 || DT != DT_F32) ? 2 : 1; }
 
+// Split rows: the S workgroups of a row meet twice through the row's line of
+// counters in the workspace (word 0: arrivals at the score exchange, word 1:
+// set when all have arrived, word 2: finished decodes; all zero between
+// calls).  Everything they exchange (page keys, partial states, counters) is
+// written and read with device-scope atomic stores and loads, which are
+// coherent across the chip on their own; a writer waits for its stores to
+// complete before it counts itself in.  No cache-wide writeback or
+// invalidation is needed.
+constexpr int kSyncArrive = 0, kSyncAll = 1, kSyncDone = 2;
+
+// Score exchange of one split row, called by one thread after every thread
+// of the workgroup stored its keys and waited for them.  Returns 1 when all S
+// splits have arrived (their keys can then be read), 0 when `polls` reads of
+// the row's flag found it still clear.  The last split to arrive re-arms the
+// arrival count and sets the flag.
+__device__ __forceinline__ int row_exchange(uint32_t* c, int S, int polls) {
+  const uint32_t o =
+      __hip_atomic_fetch_add(c + kSyncArrive, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (o == (uint32_t)S - 1) {
+    st_dev(c + kSyncArrive, 0u);
+    st_dev(c + kSyncAll, 1u);
+    return 1;
+  }
+  for (int it = 0; it < polls; ++it) {
+    if (ld_dev(c + kSyncAll) != 0u) return 1;
+    __builtin_amdgcn_s_sleep(2);
+  }
+  return 0;
+}
+
+// Called by one thread after every thread of the workgroup stored its share
+// of the partial state and waited for it: 1 for the last of the row's S
+// splits to finish (which then merges), else 0.  Never waits.  Every split
+// gets here after it has left the score exchange (and the split that set the
+// flag has waited for that store), so the last one also clears the flag: the
+// row's counters are all zero again when the kernel ends.
+__device__ __forceinline__ int row_finish(uint32_t* c, int S) {
+  const uint32_t o =
+      __hip_atomic_fetch_add(c + kSyncDone, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (o != (uint32_t)S - 1) return 0;
+  st_dev(c + kSyncDone, 0u);
+  st_dev(c + kSyncAll, 0u);
+  return 1;
+}
+
+// Merge of a split row's S partial states (one with max -inf when its split
+// had no tokens) into out, splits in increasing order whichever workgroup
+// runs it, so the result does not depend on which split finished last.
+template <int D, int G, int NT>
+__device__ __forceinline__ void merge_row(const float* __restrict__ partials, int S,
+                                          float* __restrict__ orow, size_t hq0) {
+  for (int i = threadIdx.x; i < G * D; i += NT) {
+    const int g = i / D, d = i - g * D;
+    const float* base = partials + (hq0 + g) * S * (D + 2);
+    float m[kStepMaxSplits], l[kStepMaxSplits], a[kStepMaxSplits];
+#pragma unroll
+    for (int s = 0; s < kStepMaxSplits; ++s) {
+      if (s >= S) break;
+      const float* ps = base + (size_t)s * (D + 2);
+      m[s] = ld_dev(ps + D);
+      l[s] = ld_dev(ps + D + 1);
+      a[s] = ld_dev(ps + d);
+    }
+    float M = -INFINITY;
+#pragma unroll
+    for (int s = 0; s < kStepMaxSplits; ++s) {
+      if (s >= S) break;
+      M = fmaxf(M, m[s]);
+    }
+    float L = 0.f, acc = 0.f;
+#pragma unroll
+    for (int s = 0; s < kStepMaxSplits; ++s) {
+      if (s >= S) break;
+      if (m[s] == -INFINITY) continue;  // an empty slot: its sums were never written
+      const float w = __builtin_amdgcn_exp2f(m[s] - M);
+      L = __builtin_fmaf(w, l[s], L);
+      acc = __builtin_fmaf(w, a[s], acc);
+    }
+    orow[i] = L > 0.f ? acc / L : 0.f;
+  }
+}
+
 template <int DT, int D, int G, int NT>
 __global__ __launch_bounds__(NT, (step_min_blocks<DT, D, G, NT>())) void k_step(
     const float* __restrict__ q, const void* __restrict__ k_new,
@@ -1583,10 +1657,12 @@ __global__ __launch_bounds__(NT, (step_min_blocks<DT, D, G, NT>())) void k_step(
     void* __restrict__ meta, const int32_t* __restrict__ bt,
     const int32_t* __restrict__ seq_lens, int units, int Hq, int Hkv, int log2P, int MP,
     int NP, int k_max, const int32_t* __restrict__ k_per_seq, SelectPolicy pol, float qscale,
-    int S, int32_t* __restrict__ sel, int32_t* __restrict__ sel_count,
-    float* __restrict__ scores_out, float* __restrict__ partials, float* __restrict__ out) {
+    int S, int polls, int32_t* __restrict__ sel, int32_t* __restrict__ sel_count,
+    float* __restrict__ scores_out, uint32_t* __restrict__ sync, uint32_t* __restrict__ keys,
+    float* __restrict__ partials, float* __restrict__ out) {
   constexpr int NW = NT / kWave;
   constexpr bool MF = step_uses_mfma<DT, D, G>();
+  constexpr int PB = ScoreCfg<DT, D, G, NT>::PB;
   extern __shared__ __align__(16) uint32_t smem[];
   const int MPa = (MP + 3) & ~3;
   uint32_t* s_phys = smem;
@@ -1594,15 +1670,17 @@ __global__ __launch_bounds__(NT, (step_min_blocks<DT, D, G, NT>())) void k_step(
   char* dec = reinterpret_cast<char*>(smem + 2 * MPa);
   __shared__ SelectLds<NT> sl;
   __shared__ float s_mw[NW][G];
+  __shared__ int s_flag;
 
   // workgroup -> (row, split): the S splits of a row share blockIdx mod 8,
-  // i.e. one XCD and its L2, which then serves their repeated box reads
+  // i.e. one XCD and its L2, which then serves the keys they exchange
   const int grp = blockIdx.x / (8 * S), within = blockIdx.x - grp * 8 * S;
   const int split = within >> 3, unit = grp * 8 + (within & 7);
   if (unit >= units) return;
   const int b = unit / Hkv, h = unit - b * Hkv;
   const int tid = threadIdx.x;
   const int P = 1 << log2P;
+  uint32_t* rsync = sync + (size_t)unit * kSyncWordsPerRow;  // used only when S > 1
   if (tid == 0) {
     sl.red[0] = -1;
     sl.red[1] = 0;
@@ -1612,9 +1690,11 @@ __global__ __launch_bounds__(NT, (step_min_blocks<DT, D, G, NT>())) void k_step(
   const int len = clampi(seq_lens[b], 0, MP * P);
   const int kb = clampi(k_per_seq ? k_per_seq[b] : k_max, 1, k_max);
   const int n = (len + P - 1) >> log2P;
-  if (k_new != nullptr && split == 0 && len >= 1 && tid < D) {
+  if (k_new != nullptr && len >= 1 && tid < D) {
     // the new token is slot (len-1) mod P of page (len-1)/P; its box widens
-    // (or opens, on slot 0) before any box of the row is read
+    // (or opens, on slot 0) before any box of the row is read.  Every split
+    // of a row writes the same values, so each sees the appended token
+    // whatever the order in which the splits run.
     const int pos = len - 1, p = pos >> log2P, slot = pos & (P - 1);
     const size_t phys = (size_t)clampi(bt_row[p], 0, NP - 1);
     const size_t i = ((size_t)b * Hkv + h) * D + tid;
@@ -1633,10 +1713,37 @@ __global__ __launch_bounds__(NT, (step_min_blocks<DT, D, G, NT>())) void k_step(
     }
   }
   __syncthreads();  // block-table row staged; the appended token visible to the workgroup
-  if (pol.group_sum)  // uniform branch: one copy of the scoring loop per aggregation
-    score_pages<DT, D, G, NT, true>(q, meta, s_phys, b, h, Hq, Hkv, n, 0, 1, s_key);
-  else
-    score_pages<DT, D, G, NT, false>(q, meta, s_phys, b, h, Hq, Hkv, n, 0, 1, s_key);
+  // Scoring.  A split row's S workgroups score every S-th batch of pages
+  // each and exchange the keys through the workspace; a split whose wait
+  // times out scores the remaining batches itself (bit-identical keys).
+  const int nbatch = (n + PB - 1) / PB;
+  bool share = S > 1 && nbatch > 1;
+  uint32_t* krow = keys + (size_t)unit * MP;
+  for (int bstart = share ? split : 0, bstride = share ? S : 1;;) {
+    if (pol.group_sum)  // uniform branch: one copy of the scoring loop per aggregation
+      score_pages<DT, D, G, NT, true>(q, meta, s_phys, b, h, Hq, Hkv, n, bstart, bstride, s_key);
+    else
+      score_pages<DT, D, G, NT, false>(q, meta, s_phys, b, h, Hq, Hkv, n, bstart, bstride, s_key);
+    if (!share) break;
+    __syncthreads();
+    for (int bi = split; bi < nbatch; bi += S)
+      for (int i = tid; i < PB; i += NT) {
+        const int p = bi * PB + i;
+        if (p < n) st_dev(krow + p, s_key[p]);
+      }
+    stores_done();
+    __syncthreads();
+    if (tid == 0) s_flag = row_exchange(rsync, S, polls);
+    __syncthreads();
+    if (s_flag) {
+      for (int p = tid; p < n; p += NT)
+        if ((p / PB) % S != split) s_key[p] = ld_dev(krow + p);
+      break;
+    }
+    share = false;  // timed out: score every batch here
+    bstart = 0;
+    bstride = 1;
+  }
   __syncthreads();
   if (scores_out && split == 0) {
     float* srow_out = scores_out + (size_t)unit * MP;
@@ -1648,55 +1755,47 @@ __global__ __launch_bounds__(NT, (step_min_blocks<DT, D, G, NT>())) void k_step(
   const int cnt =
       select_block<NT>(s_key, s_phys, n, keff, f, r, k_max, nullptr, nullptr, nullptr, sl);
   int32_t* srow = sel + (size_t)unit * k_max;
-  float* orow = out + ((size_t)b * Hq + h * G) * D;
-  // with S > 1 every split leaves a partial state for k_merge_step; a split
-  // without tokens leaves an empty one (max -inf)
-  auto empty_partial = [&]() {
-    for (int g = tid; g < G; g += NT) {
-      float* dst = partials + (((size_t)b * Hq + h * G + g) * S + split) * (D + 2);
-      dst[D] = -INFINITY;
-      dst[D + 1] = 0.f;
-    }
-  };
-  if (cnt == 0) {
-    if (split == 0) {
-      if (S == 1)
-        for (int i = tid; i < G * D; i += NT) orow[i] = 0.f;
-      for (int i = tid; i < k_max; i += NT) srow[i] = -1;
-      if (tid == 0) sel_count[unit] = 0;
-    }
-    if (S > 1) empty_partial();
-    return;
-  }
-  // this split's share of the selected-token stream
+  const size_t hq0 = (size_t)b * Hq + h * G;
+  float* orow = out + hq0 * D;
+  // this split's share of the selected-token stream (none when cnt == 0)
   const long t_all = (long)cnt << log2P;
   const long span = S > 1 ? step_span(t_all, S, kStepMinSpanSteps * 16 * NW) : t_all;
   const long t0 = (long)split * span, t_end = min(t_all, t0 + span);
-  const int ns = S > 1 ? S : 1;  // S > 1: always a partial state, merged by k_merge_step
-  if (t0 >= t_end) {  // split 0 always has tokens
-    empty_partial();
-    return;
-  }
-  const TokenList tl{reinterpret_cast<const int*>(s_key), s_phys, cnt, 0, len, log2P, Hkv, h, D};
-  const float* qg0 = q + ((size_t)b * Hq + h * G) * D;
-  const char* kbp = reinterpret_cast<const char*>(k_pool);
-  const char* vbp = reinterpret_cast<const char*>(v_pool);
-  typedef float AccRow[G][D + 1];
-  AccRow* s_acc = reinterpret_cast<AccRow*>(dec);
-  if constexpr (MF) {
-    mfma_decode_range<DT, D, G, NW, D == 64 ? 4 : 2>(qg0, kbp, vbp, tl, t0, t_end, qscale,
-                                                     s_acc, s_mw);
+  if (t0 < t_end) {
+    const TokenList tl{reinterpret_cast<const int*>(s_key), s_phys, cnt, 0, len, log2P, Hkv, h, D};
+    const float* qg0 = q + hq0 * D;
+    const char* kbp = reinterpret_cast<const char*>(k_pool);
+    const char* vbp = reinterpret_cast<const char*>(v_pool);
+    typedef float AccRow[G][D + 1];
+    AccRow* s_acc = reinterpret_cast<AccRow*>(dec);
+    if constexpr (MF)
+      mfma_decode_range<DT, D, G, NW, D == 64 ? 4 : 2>(qg0, kbp, vbp, tl, t0, t_end, qscale,
+                                                       s_acc, s_mw);
+    else
+      valu_decode_range<DT, D, G, NT>(qg0, kbp, vbp, tl, t0, t_end, qscale, s_acc, s_mw);
     __syncthreads();
-    finish_split<D, G, NT, NW>(s_acc, s_mw, partials, out, b, h, Hq, S, split, ns);
-  } else {
-    valu_decode_range<DT, D, G, NT>(qg0, kbp, vbp, tl, t0, t_end, qscale, s_acc, s_mw);
-    __syncthreads();
-    finish_split<D, G, NT, NW>(s_acc, s_mw, partials, out, b, h, Hq, S, split, ns);
+    finish_split<D, G, NT, NW, true>(s_acc, s_mw, partials, out, b, h, Hq, S, split, S);
+  } else if (S == 1) {  // no tokens at all
+    for (int i = tid; i < G * D; i += NT) orow[i] = 0.f;
+  } else {  // a split without tokens leaves an empty state (max -inf)
+    for (int g = tid; g < G; g += NT) {
+      float* dst = partials + ((hq0 + g) * S + split) * (D + 2);
+      st_dev(dst + D, -INFINITY);
+      st_dev(dst + D + 1, 0.f);
+    }
   }
   if (split == 0) {
     for (int i = tid; i < k_max; i += NT) srow[i] = i < cnt ? (int32_t)s_key[i] : -1;
     if (tid == 0) sel_count[unit] = cnt;
   }
+  if (S == 1) return;
+  // the last split of the row to get here merges the S partial states
+  stores_done();
+  __syncthreads();
+  if (tid == 0) s_flag = row_finish(rsync, S);
+  __syncthreads();
+  if (!s_flag) return;
+  merge_row<D, G, NT>(partials, S, orow, hq0);
 }
 
 // ---------------------------------------------------------------------------
@@ -1780,7 +1879,8 @@ int decode_splits(const Dims& d, int k_max) {
 
 size_t workspace_layout(const Dims& d, int k_max, void* base, Workspace* ws) {
   const size_t units = (size_t)d.B * d.Hkv;
-  const size_t o_keys = 0;
+  const size_t o_sync = 0;
+  const size_t o_keys = o_sync + kSyncBytes;
   const size_t o_phys = o_keys + round_up(units * d.MP * sizeof(uint32_t));
   const size_t o_part = o_phys + round_up(units * k_max * sizeof(int32_t));
   const size_t splits = std::max(decode_splits(d, k_max), step_splits(d, k_max));
@@ -1788,6 +1888,7 @@ size_t workspace_layout(const Dims& d, int k_max, void* base, Workspace* ws) {
                                          partial_stride(d) * sizeof(float));
   if (base && ws) {
     char* c = static_cast<char*>(base);
+    ws->sync = reinterpret_cast<uint32_t*>(c + o_sync);
     ws->keys = reinterpret_cast<uint32_t*>(c + o_keys);
     ws->sel_phys = reinterpret_cast<int32_t*>(c + o_phys);
     ws->partials = reinterpret_cast<float*>(c + o_part);
@@ -1888,13 +1989,25 @@ size_t step_lds_bytes(const Dims& d) {
 bool step_fits(const Dims& d) { return step_lds_bytes(d) <= kStepMaxLds; }
 
 // Workgroups per row: rows that leave most of the 256 CUs idle are spread
-// over up to 8 workgroups each (every one scores and selects the whole row,
-// then decodes its share of the kept tokens), as far as k_max pages give each
-// split its minimum span; the split partial states are combined by k_merge.
+// over up to 8 workgroups each (they share the scoring, every one selects the
+// whole row, then decodes its share of the kept tokens), as far as k_max
+// pages give each split its minimum span; the last split to finish merges.
+// Only the first kSyncRows rows have synchronisation counters.
+// Polls of a row's generation word before a split stops waiting for the
+// row's other workgroups and scores the rest of the row itself (several
+// milliseconds by default: only reached if they are not resident at the
+// same time).  Changed only by the testing hook tsv_debug_exchange_polls.
+static std::atomic<int> g_exchange_polls{1 << 14};
+
+int exchange_polls() { return g_exchange_polls.load(std::memory_order_relaxed); }
+
+int set_exchange_polls(int polls) { return g_exchange_polls.exchange(polls); }
+
 int step_splits(const Dims& d, int k_max) {
   const long units = (long)d.B * d.Hkv;
   const long minspan = kStepMinSpanSteps * 16 * (step_threads(d) / kWave);
   const long by_tokens = (long)k_max * d.P / minspan;
+  if (units > kSyncRows) return 1;
   return (int)std::max(1L, std::min({(long)kStepMaxSplits, 256 / units, by_tokens}));
 }
 
@@ -1918,23 +2031,15 @@ hipError_t launch_step(const Dims& d, const float* q, const void* k_new, const v
       constexpr int nthr = decltype(NTc)::value;
       hipLaunchKernelGGL((k_step<dt, hd, g, nthr>), grid, dim3(nthr), lds, s, q, k_new, v_new,
                          k_pool, v_pool, meta, bt, seq_lens, units, d.Hq, d.Hkv, log2P, d.MP,
-                         d.NP, k_max, k_per_seq, pol, qscale, S, sel, sel_count,
-                         scores_out, ws.partials, out);
+                         d.NP, k_max, k_per_seq, pol, qscale, S, exchange_polls(), sel,
+                         sel_count, scores_out, ws.sync, ws.keys, ws.partials, out);
       return hipGetLastError();
     };
     if constexpr (g == 1)
       if (nt == 1024) return go(IC<1024>{});
     return nt == 256 ? go(IC<256>{}) : go(IC<512>{});
   });
-  if (e != hipSuccess || S == 1) return e;
-  const int waves = d.B * d.Hq;
-  if (d.D == 64)
-    hipLaunchKernelGGL(k_merge_step<64>, dim3((waves + 3) / 4), dim3(256), 0, s, ws.partials,
-                       waves, S, out);
-  else
-    hipLaunchKernelGGL(k_merge_step<128>, dim3((waves + 3) / 4), dim3(256), 0, s, ws.partials,
-                       waves, S, out);
-  return hipGetLastError();
+  return e;
 }
 
 hipError_t launch_decode(const Dims& d, const float* q, const void* k_pool,

@@ -38,8 +38,18 @@ int decode_splits(const Dims& d, int k_max);
 // Partial-state floats per (sequence, query head, split).
 inline int partial_stride(const Dims& d) { return d.D + 2; }
 
-// Regions of the caller's workspace (no initialisation needed).
+// Rows whose step is spread over several workgroups synchronise through
+// counters at the start of the workspace: one 128-byte line per row (rows are
+// split only when B*Hkv <= 128), zero before the first call and left zero by
+// every call.  The region does not depend on the shape, so a workspace reused
+// for other shapes keeps it intact.
+constexpr int kSyncRows = 128;
+constexpr int kSyncWordsPerRow = 32;
+constexpr size_t kSyncBytes = (size_t)kSyncRows * kSyncWordsPerRow * sizeof(uint32_t);
+
+// Regions of the caller's workspace (only `sync` needs initialisation).
 struct Workspace {
+  uint32_t* sync;      // [kSyncRows][kSyncWordsPerRow] split-row counters
   uint32_t* keys;      // [B*Hkv][MP] order keys of the page scores
   int32_t* sel_phys;   // [B*Hkv][k_max] physical page of each selection
   float* partials;     // [B*Hq][splits][D+2] tile softmax states
@@ -75,15 +85,20 @@ hipError_t launch_decode(const Dims& d, const float* q, const void* k_pool,
                          hipStream_t s);
 
 // The whole step of one (sequence, KV head) in one workgroup (or in
-// step_splits(d) workgroups that each score and select the whole row and
-// decode a share of it, merged by a second launch): [append] -> score ->
-// top-K -> decode.  Usable when step_fits(d) (its LDS, which grows with
-// max_pages_per_seq, stays within kStepMaxLds).
+// step_splits(d) workgroups that share the row's scoring, each select the
+// whole row and decode a share of it; the last one to finish merges the
+// shares): [append] -> score -> top-K -> decode, one launch.  Usable when
+// step_fits(d) (its LDS, which grows with max_pages_per_seq, stays within
+// kStepMaxLds).
 constexpr size_t kStepMaxLds = 64 * 1024;
 size_t step_lds_bytes(const Dims& d);
 bool step_fits(const Dims& d);
-// Workgroups per row of the one-workgroup step (k_merge runs when > 1).
+// Workgroups per row of the one-workgroup step.
 int step_splits(const Dims& d, int k_max);
+// Polls a split of a row makes while it waits for the row's other splits'
+// page keys; set_exchange_polls returns the previous value.
+int exchange_polls();
+int set_exchange_polls(int polls);
 hipError_t launch_step(const Dims& d, const float* q, const void* k_new, const void* v_new,
                        void* k_pool, void* v_pool, void* meta, const int32_t* bt,
                        const int32_t* seq_lens, int k_max, const int32_t* k_per_seq,

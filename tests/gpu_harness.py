@@ -14,6 +14,7 @@ import oracle as O
 import workloads as W
 
 TOL = {W.F32: 1e-5, W.F16: 2e-3, W.BF16: 2e-3, W.F8: 2e-3, W.F8E5: 2e-3}
+SYNC_BYTES = 16384  # TSV_WORKSPACE_ZERO_BYTES: zero before and after every call
 
 
 def say(*a):
@@ -45,9 +46,11 @@ def oracle_run(wl, k_max=None, k_per_seq="wl", n_sink=None, step=0, n_recent=0, 
 
 
 def gpu_run(wl, k_max=None, k_per_seq="wl", n_sink=None, step=0, separate=False, n_recent=0,
-            group_agg=0):
+            group_agg=0, ws=None):
     """HIP results of the same step; `separate` uses the three-call path.  With
-    selection options the _ex entry points are called, else the plain ones."""
+    selection options the _ex entry points are called, else the plain ones.
+    `ws`: a workspace to use (default: a new zero-filled one); the result's
+    "sync" holds its counter prefix after the call."""
     import torch
 
     import query_aware_sparse_bbox_amd as T
@@ -62,7 +65,8 @@ def gpu_run(wl, k_max=None, k_per_seq="wl", n_sink=None, step=0, separate=False,
     cnt = torch.full((B, Hkv), -7, dtype=torch.int32, device="cuda")
     sc = torch.full((B, Hkv, MP), float("nan"), dtype=torch.float32, device="cuda")
     out = torch.full((B, Hq, D), float("nan"), dtype=torch.float32, device="cuda")
-    ws = T.new_workspace(sh, k_max)
+    if ws is None:
+        ws = T.new_workspace(sh, k_max)
     k_new = v_new = None
     if wl.steps:
         st = wl.steps[step]
@@ -100,7 +104,8 @@ def gpu_run(wl, k_max=None, k_per_seq="wl", n_sink=None, step=0, separate=False,
     torch.cuda.synchronize()
     return dict(meta=WD.kv_numpy(d.meta, sh.kv_dtype), sel=sel.cpu().numpy(),
                 cnt=cnt.cpu().numpy(), scores=sc.cpu().numpy(), out=out.cpu().numpy(),
-                k_pool=WD.kv_numpy(d.k_pool, sh.kv_dtype), v_pool=WD.kv_numpy(d.v_pool, sh.kv_dtype))
+                k_pool=WD.kv_numpy(d.k_pool, sh.kv_dtype), v_pool=WD.kv_numpy(d.v_pool, sh.kv_dtype),
+                sync=ws[:SYNC_BYTES].cpu().numpy())
 
 
 def n_pages(wl, step=0):

@@ -12,7 +12,7 @@ import numpy as np
 import pytest
 
 import workloads as W
-from gpu_harness import compare, gpu_run, oracle_run, say
+from gpu_harness import SYNC_BYTES, compare, gpu_run, oracle_run, say
 
 pytestmark = pytest.mark.gpu
 
@@ -178,9 +178,9 @@ def test_one_launch_and_phased_paths_both_covered():
 
     for name in W.CONFIG_ORDER:
         wl = W.make(name)
-        # 64 rows of 64 pages: each row over several workgroups, then a merge
-        want = 2 if name == "tinyllama" else 1
-        assert T.tsv_decode_step_launches(wl.shape, wl.k_max, bool(wl.steps)) == want, name
+        # one launch each (tinyllama's 64 rows are each spread over several
+        # workgroups that merge in the same kernel)
+        assert T.tsv_decode_step_launches(wl.shape, wl.k_max, bool(wl.steps)) == 1, name
     wl = W.make("ragged", batch=2, lens_range=(65500, 65535), kv_dtype=W.BF16, num_q_heads=64)
     assert wl.shape.max_pages_per_seq >= 4064
     assert T.tsv_decode_step_launches(wl.shape, wl.k_max, True) == 4
@@ -365,9 +365,12 @@ def test_permuted_pool_same_selection():
     assert np.array_equal(ga["out"].view(np.uint32), gb["out"].view(np.uint32))
 
 
-@pytest.mark.parametrize("kw", [dict(batch=16), dict(batch=8, kv_dtype=W.F8)])
+@pytest.mark.parametrize("kw", [dict(batch=16), dict(batch=8, kv_dtype=W.F8),
+                                dict(batch=4), dict(batch=2, kv_dtype=W.F8E5)])
 def test_ragged_appends_seventeen_steps(kw):
-    """17 consecutive appends cover every slot residue mod 16 and page opens."""
+    """17 consecutive appends cover every slot residue mod 16 and page opens.
+    With 4 and 2 sequences every row is spread over several workgroups, each
+    of which appends the token before reading any box or slot."""
     import torch
 
     import oracle as O
@@ -413,3 +416,47 @@ def test_ragged_appends_seventeen_steps(kw):
                               W.storage_to_f32(r[phys], sh.kv_dtype))
     assert np.array_equal(WD.kv_numpy(d.k_pool, sh.kv_dtype), kp)
     assert np.array_equal(WD.kv_numpy(d.v_pool, sh.kv_dtype), vp)
+    assert not ws[:SYNC_BYTES].cpu().numpy().any(), "split-row counters left non-zero"
+
+
+def test_split_rows_exchange_fallback_bit_identical():
+    """Rows spread over several workgroups share their page scoring through the
+    workspace.  With the wait cut to zero polls, every split but the last to
+    arrive scores the rest of its row itself: scores, selections and outputs
+    are the same bits, and the counters are left at zero either way."""
+    import query_aware_sparse_bbox_amd as T
+
+    wl = W.make("tinyllama", batch=4, context=4096)
+    assert T.tsv_decode_step_launches(wl.shape, wl.k_max, False) == 1
+    o = oracle_run(wl)
+    a = gpu_run(wl)
+    compare(wl, a, o)
+    prev = T.tsv_debug_exchange_polls(0)
+    try:
+        b = gpu_run(wl)
+        wl8 = W.make("tinyllama", batch=2, context=4096, kv_dtype=W.F8)
+        compare(wl8, gpu_run(wl8), oracle_run(wl8))
+    finally:
+        T.tsv_debug_exchange_polls(prev)
+    for k in ("sel", "cnt"):
+        assert np.array_equal(a[k], b[k]), k
+    for k in ("scores", "out"):
+        assert np.array_equal(a[k].view(np.uint32), b[k].view(np.uint32)), k
+    assert not a["sync"].any() and not b["sync"].any()
+
+
+def test_split_rows_workspace_shared_by_shapes():
+    """One zero-filled workspace serves split-row steps of different shapes (and
+    a phased call in between); each call leaves the counter prefix at zero."""
+    import query_aware_sparse_bbox_amd as T
+
+    a = W.make("tinyllama", batch=4, context=4096)
+    b = W.make("ragged", batch=3, lens_range=(200, 3000), append_steps=1)
+    n = max(T.tsv_workspace_bytes(a.shape, a.k_max), T.tsv_workspace_bytes(b.shape, b.k_max))
+    import torch
+    ws = torch.zeros(n, dtype=torch.uint8, device="cuda")
+    for wl, kw in ((a, {}), (b, {}), (a, dict(separate=True)), (b, {}), (a, {})):
+        say(f"[case] shared workspace: {wl.name} {wl.shape} {kw}")
+        g = gpu_run(wl, ws=ws, **kw)
+        compare(wl, g, oracle_run(wl))
+        assert not g["sync"].any()
