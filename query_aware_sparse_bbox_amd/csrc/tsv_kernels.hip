@@ -375,7 +375,7 @@ __device__ __forceinline__ uint32_t wave_reduce(uint32_t x, Op op) {
 // written before a barrier that precedes the call).
 template <int NT>
 struct SelectLds {
-  int hist[2][256];  // passes alternate, so a pass's scan overlaps the next clear
+  alignas(16) int hist[2][256];  // passes alternate, so a pass's scan overlaps the next clear
   int red[8];
   int scan[NT / 64];
 };
@@ -553,6 +553,135 @@ __device__ __forceinline__ int select_block(uint32_t* s_key, uint32_t* s_phys, i
   }
   __syncthreads();
   return total;
+}
+
+// Rows of at most this many pages are selected by one wave (select_wave).
+constexpr int kWaveSelectMaxPages = 512;
+
+// Top-K of one row by wave 0 of the workgroup, with the same result as
+// select_block: pages [0, f) and [n - r, n) always kept, the other
+// R = keff - f - r slots to the largest order keys among pages [f, n - r),
+// equal keys lowest page first; the kept pages left ascending in s_key /
+// s_phys [0, cnt).  Lane l holds pages l, l + 64, ... (round i: page
+// 64 i + l) in registers, so no barrier is needed until the end: the shared
+// high bits of the candidates are fixed by a wave AND / OR, then 8-bit digits
+// are counted in an LDS histogram (LDS operations of one wave complete in
+// order) until the boundary bucket is taken whole or no bits are left.  The
+// output position of a kept page is the number of kept pages before it: the
+// total of earlier rounds plus the kept lanes below it in this round (a
+// ballot), so the pages come out ascending without a sort.  All threads
+// return the count; ends with a barrier.
+template <int NT>
+__device__ __forceinline__ int select_wave(uint32_t* s_key, uint32_t* s_phys, int n, int keff,
+                                           int f, int r, int k_max, SelectLds<NT>& sl) {
+  constexpr int MAXR = kWaveSelectMaxPages / kWave;
+  const int lane = threadIdx.x & (kWave - 1);
+  if (threadIdx.x < kWave) {
+    const int R = keff - f - r, pr = n - r, ncand = pr - f;
+    const bool take_all = R >= ncand, radix = R > 0 && R < ncand;
+    const int rounds = (n + kWave - 1) / kWave;
+    int* hist = sl.hist[0];
+    uint32_t kk[MAXR], ph[MAXR];
+#pragma unroll
+    for (int i = 0; i < MAXR; ++i) {
+      if (i >= rounds) break;  // uniform
+      const int p = min(i * kWave + lane, max(n - 1, 0));
+      kk[i] = s_key[p];
+      ph[i] = s_phys[p];
+    }
+    auto is_cand = [&](int i) {
+      const int p = i * kWave + lane;
+      return p >= f && p < pr;
+    };
+    uint32_t tmask = 0, tau = 0;  // (key & tmask) > tau: kept; == tau: the first `need`
+    int need = 0;
+    if (radix) {
+      uint32_t a = ~0u, o = 0u;
+#pragma unroll
+      for (int i = 0; i < MAXR; ++i) {
+        if (i >= rounds) break;
+        if (is_cand(i)) {
+          a &= kk[i];
+          o |= kk[i];
+        }
+      }
+      a = wave_reduce(a, [](uint32_t u, uint32_t v) { return u & v; });
+      o = wave_reduce(o, [](uint32_t u, uint32_t v) { return u | v; });
+      int remaining = R;
+      if (a == o) {  // every candidate has the same key: lowest pages win
+        tmask = ~0u;
+        tau = a;
+      } else {
+        int top = 31 - __clz(a ^ o);
+        tmask = top == 31 ? 0u : ~((2u << top) - 1u);
+        tau = a & tmask;
+        for (;;) {
+          const int width = min(8, top + 1), shift = top + 1 - width;
+          const uint32_t dmask = (1u << width) - 1u;
+          const int nb = 1 << width;
+          reinterpret_cast<int4*>(hist)[lane] = int4{0, 0, 0, 0};  // 256 bins
+#pragma unroll
+          for (int i = 0; i < MAXR; ++i) {
+            if (i >= rounds) break;
+            if (is_cand(i) && (kk[i] & tmask) == tau) atomicAdd(&hist[(kk[i] >> shift) & dmask], 1);
+          }
+          __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+          int c[4], sum = 0;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {  // digits in decreasing order
+            const int bin = nb - 1 - 4 * lane - j;
+            c[j] = bin >= 0 ? hist[bin] : 0;
+            sum += c[j];
+          }
+          int before = wave_incl_scan(sum, lane) - sum;  // keys in higher digits
+          int dg = -1, rem = 0, cb = 0;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            if (before < remaining && before + c[j] >= remaining) {
+              dg = nb - 1 - 4 * lane - j;
+              rem = remaining - before;
+              cb = c[j];
+            }
+            before += c[j];
+          }
+          const int src = __ffsll(__ballot(dg >= 0)) - 1;  // exactly one lane
+          dg = __builtin_amdgcn_readlane(dg, src);
+          remaining = __builtin_amdgcn_readlane(rem, src);
+          cb = __builtin_amdgcn_readlane(cb, src);
+          tau |= (uint32_t)dg << shift;
+          tmask |= dmask << shift;
+          if (remaining == cb || shift == 0) break;
+          top = shift - 1;
+          __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+        }
+      }
+      need = remaining;
+    }
+    const unsigned long long below = (1ull << lane) - 1ull;
+    int base = 0, eqseen = 0;
+#pragma unroll
+    for (int i = 0; i < MAXR; ++i) {
+      if (i >= rounds) break;
+      const int p = i * kWave + lane;
+      const bool valid = p < n, cand = valid && is_cand(i);
+      const uint32_t km = kk[i] & tmask;
+      const bool eq = radix && cand && km == tau;
+      bool keep = (valid && (p < f || p >= pr)) || (cand && (take_all || (radix && km > tau)));
+      const unsigned long long beq = __ballot(eq);
+      if (eq) keep = eqseen + __popcll(beq & below) < need;
+      eqseen += __popcll(beq);
+      const unsigned long long bk = __ballot(keep);
+      const int pos = base + __popcll(bk & below);
+      base += __popcll(bk);
+      if (keep && pos < k_max) {  // pos < k_max always: at most min(K_b, n_b) are kept
+        s_key[pos] = (uint32_t)p;
+        s_phys[pos] = ph[i];
+      }
+    }
+    if (lane == 0) sl.red[5] = min(base, k_max);
+  }
+  __syncthreads();
+  return sl.red[5];
 }
 
 // Scores batches bstart, bstart + bstride, ... of one unit's n pages into
@@ -1753,7 +1882,9 @@ __global__ __launch_bounds__(NT, (step_min_blocks<DT, D, G, NT>())) void k_step(
   // the selection stays in LDS; it is written out at the end, so that no
   // barrier before the decode waits for those stores
   const int cnt =
-      select_block<NT>(s_key, s_phys, n, keff, f, r, k_max, nullptr, nullptr, nullptr, sl);
+      n <= kWaveSelectMaxPages
+          ? select_wave<NT>(s_key, s_phys, n, keff, f, r, k_max, sl)
+          : select_block<NT>(s_key, s_phys, n, keff, f, r, k_max, nullptr, nullptr, nullptr, sl);
   int32_t* srow = sel + (size_t)unit * k_max;
   const size_t hq0 = (size_t)b * Hq + h * G;
   float* orow = out + hq0 * D;
@@ -1768,9 +1899,10 @@ __global__ __launch_bounds__(NT, (step_min_blocks<DT, D, G, NT>())) void k_step(
     const char* vbp = reinterpret_cast<const char*>(v_pool);
     typedef float AccRow[G][D + 1];
     AccRow* s_acc = reinterpret_cast<AccRow*>(dec);
+    // chunks of two 16-token steps: a split's waves often hold only two steps,
+    // and longer chunks unroll into more code that every workgroup fetches once
     if constexpr (MF)
-      mfma_decode_range<DT, D, G, NW, D == 64 ? 4 : 2>(qg0, kbp, vbp, tl, t0, t_end, qscale,
-                                                       s_acc, s_mw);
+      mfma_decode_range<DT, D, G, NW, 2>(qg0, kbp, vbp, tl, t0, t_end, qscale, s_acc, s_mw);
     else
       valu_decode_range<DT, D, G, NT>(qg0, kbp, vbp, tl, t0, t_end, qscale, s_acc, s_mw);
     __syncthreads();
