@@ -13,8 +13,8 @@ Prints one JSON line:
   value        (sequence x query head) / s of the whole step
   roofline     the step's algorithmic bytes / its mean duration (HIP events
                around the graph-replayed steps on their stream) against 8 TB/s;
-               the step is one kernel (k_step), or k_step + k_merge where rows
-               are spread over several workgroups; `traffic` = HBM bytes per
+               the step is one kernel (k_step; rows spread over several
+               workgroups merge inside it); `traffic` = HBM bytes per
                step from rocprofv3 counters when they were taken on the current
                kernel source, else null
   cpu_baseline the CPU oracle (single thread) on a bounded sample of the step
@@ -66,14 +66,14 @@ KERNEL_SOURCES = [os.path.join(ROOT, "query_aware_sparse_bbox_amd", "csrc", f)
 # hex digits).  Keys: configuration, or configuration:KV type when the
 # configuration's KV type is overridden.
 TRAFFIC = {
-    "tinyllama": {"source": "0d0c0663bbc2eea1", "bytes_per_step": 22901515, "read": 22211339, "written": 690176},
-    "tiny": {"source": "0d0c0663bbc2eea1", "bytes_per_step": 552819, "read": 551539, "written": 1280},
-    "gpt2": {"source": "0d0c0663bbc2eea1", "bytes_per_step": 42685976, "read": 42505752, "written": 180224},
-    "llama_long": {"source": "0d0c0663bbc2eea1", "bytes_per_step": 202176501, "read": 202037237, "written": 139264},
-    "ragged": {"source": "0d0c0663bbc2eea1", "bytes_per_step": 402889145, "read": 401393566, "written": 1495579},
-    "tinyllama:fp8e4m3": {"source": "0d0c0663bbc2eea1", "bytes_per_step": 12480041, "read": 11789865, "written": 690176},
-    "llama_long:fp8e4m3": {"source": "0d0c0663bbc2eea1", "bytes_per_step": 101453842, "read": 101314578, "written": 139264},
-    "ragged:fp8e4m3": {"source": "0d0c0663bbc2eea1", "bytes_per_step": 204239420, "read": 202885382, "written": 1354038},
+    "tinyllama": {"source": "18c10dba9f05dfd4", "bytes_per_step": 23214630, "read": 22219302, "written": 995328},
+    "tiny": {"source": "18c10dba9f05dfd4", "bytes_per_step": 568179, "read": 566899, "written": 1280},
+    "gpt2": {"source": "18c10dba9f05dfd4", "bytes_per_step": 42712610, "read": 42532386, "written": 180224},
+    "llama_long": {"source": "18c10dba9f05dfd4", "bytes_per_step": 202225348, "read": 202086083, "written": 139265},
+    "ragged": {"source": "18c10dba9f05dfd4", "bytes_per_step": 403159530, "read": 401663677, "written": 1495853},
+    "tinyllama:fp8e4m3": {"source": "18c10dba9f05dfd4", "bytes_per_step": 12828389, "read": 11833061, "written": 995328},
+    "llama_long:fp8e4m3": {"source": "18c10dba9f05dfd4", "bytes_per_step": 101564851, "read": 101425587, "written": 139264},
+    "ragged:fp8e4m3": {"source": "18c10dba9f05dfd4", "bytes_per_step": 204439628, "read": 203085718, "written": 1353910},
 }
 
 
@@ -386,8 +386,7 @@ def main():
     tkey = args.config if kv_dtype == own_dtype else f"{args.config}:{W.DTYPE_NAMES[kv_dtype]}"
     tr = None if variant else TRAFFIC.get(tkey)
     traffic = tr["bytes_per_step"] if tr and tr["source"] == src else None
-    kernel = {1: "k_step (append, score, select, decode of every row)",
-              2: "k_step + k_merge (rows spread over several workgroups, then merged)"}.get(
+    kernel = {1: "k_step (append, score, select, decode of every row)"}.get(
         launches, f"tsv_decode_step phased path ({launches} kernels)")
     line = {
         "metric": METRIC,
