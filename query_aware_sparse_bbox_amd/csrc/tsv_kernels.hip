@@ -145,6 +145,22 @@ constexpr int kRowHalfMirror = 0x141;
 constexpr int kRowMirror = 0x140;
 constexpr int kRowRor8 = 0x128;
 
+// The value of lane ^ 32 / lane ^ 16, by the gfx950 lane-swap instructions
+// (v_permlane32_swap / v_permlane16_swap: plain VALU, where a shuffle would
+// take the LDS crossbar).  With x in both operands, the swap leaves lane l's
+// partner value in the first result when bit 5 (bit 4) of l is set, else in
+// the second.  All 64 lanes must be active.
+__device__ __forceinline__ float xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float((threadIdx.x & 32) ? r[0] : r[1]);
+}
+__device__ __forceinline__ float xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float((threadIdx.x & 16) ? r[0] : r[1]);
+}
+
 // Sum over aligned groups of L lanes.  Lane k of a group holds the partial
 // sum of its own contiguous channel run; every step adds the sibling subtree
 // (after a step all lanes of a subtree hold the same value, so the mirror
@@ -156,8 +172,8 @@ __device__ __forceinline__ float group_sum(float x) {
   if constexpr (L >= 4) x = x + dpp<kQuadXor2>(x);
   if constexpr (L >= 8) x = x + dpp<kRowHalfMirror>(x);
   if constexpr (L >= 16) x = x + dpp<kRowMirror>(x);
-  if constexpr (L >= 32) x = x + __shfl_xor(x, 16);
-  if constexpr (L >= 64) x = x + __shfl_xor(x, 32);
+  if constexpr (L >= 32) x = x + xor16(x);
+  if constexpr (L >= 64) x = x + xor32(x);
   return x;
 }
 
@@ -167,8 +183,8 @@ template <int L, class Op>
 __device__ __forceinline__ float across_slots(float x, Op op) {
   static_assert(L >= 8, "slot reduction assumes at least 8 lanes per slot");
   if constexpr (L <= 8) x = op(x, dpp<kRowRor8>(x));
-  if constexpr (L <= 16) x = op(x, __shfl_xor(x, 16));
-  if constexpr (L <= 32) x = op(x, __shfl_xor(x, 32));
+  if constexpr (L <= 16) x = op(x, xor16(x));
+  if constexpr (L <= 32) x = op(x, xor32(x));
   return x;
 }
 
@@ -1016,7 +1032,8 @@ __device__ __forceinline__ void finish_split(float (*s_acc)[G][D + 1], float (*s
 template <int MASK>
 __device__ __forceinline__ float xor_lane(float x) {
   if constexpr (MASK == 8) return dpp<kRowRor8>(x);
-  else return __shfl_xor(x, MASK);
+  else if constexpr (MASK == 16) return xor16(x);
+  else return xor32(x);
 }
 
 // Fold the running softmax state of the partner slot (lane ^ MASK) into
@@ -1532,8 +1549,8 @@ __device__ __forceinline__ void mfma_decode_range(const float* __restrict__ qg0,
 #pragma unroll
     for (int cc = 0; cc < CH; ++cc)
       tm = fmaxf(tm, fmaxf(fmaxf(z[cc][0], z[cc][1]), fmaxf(z[cc][2], z[cc][3])));
-    tm = fmaxf(tm, __shfl_xor(tm, 16));
-    tm = fmaxf(tm, __shfl_xor(tm, 32));
+    tm = fmaxf(tm, xor16(tm));
+    tm = fmaxf(tm, xor32(tm));
     const float mn = fmaxf(m_run, tm);
     const float alpha = mn == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run - mn);
     const float ms = mn == -INFINITY ? 0.f : mn;
@@ -1606,15 +1623,15 @@ __device__ __forceinline__ void mfma_decode_range(const float* __restrict__ qg0,
     load(0, ca);
     compute(0, ca);
   }
-  l_run += __shfl_xor(l_run, 16);
-  l_run += __shfl_xor(l_run, 32);
+  l_run += xor16(l_run);
+  l_run += xor32(l_run);
   // out fragment: row 4*c4 + r, channel W*n16 + e; rows g (c4 < 2) and
   // g + 8 (c4 + 2) hold the hi and lo parts of head g
 #pragma unroll
   for (int e = 0; e < NDT; ++e)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const float sum = o[e][r] + __shfl_xor(o[e][r], 32);
+      const float sum = o[e][r] + xor32(o[e][r]);
       const int g = 4 * c4 + r;
       if (g < G) s_acc[wave][g][NDT * n16 + e] = sum * (1.f / M::kPScale);
     }
