@@ -66,14 +66,14 @@ KERNEL_SOURCES = [os.path.join(ROOT, "query_aware_sparse_bbox_amd", "csrc", f)
 # hex digits).  Keys: configuration, or configuration:KV type when the
 # configuration's KV type is overridden.
 TRAFFIC = {
-    "tinyllama": {"source": "18c10dba9f05dfd4", "bytes_per_step": 23214630, "read": 22219302, "written": 995328},
-    "tiny": {"source": "18c10dba9f05dfd4", "bytes_per_step": 568179, "read": 566899, "written": 1280},
-    "gpt2": {"source": "18c10dba9f05dfd4", "bytes_per_step": 42712610, "read": 42532386, "written": 180224},
-    "llama_long": {"source": "18c10dba9f05dfd4", "bytes_per_step": 202225348, "read": 202086083, "written": 139265},
-    "ragged": {"source": "18c10dba9f05dfd4", "bytes_per_step": 403159530, "read": 401663677, "written": 1495853},
-    "tinyllama:fp8e4m3": {"source": "18c10dba9f05dfd4", "bytes_per_step": 12828389, "read": 11833061, "written": 995328},
-    "llama_long:fp8e4m3": {"source": "18c10dba9f05dfd4", "bytes_per_step": 101564851, "read": 101425587, "written": 139264},
-    "ragged:fp8e4m3": {"source": "18c10dba9f05dfd4", "bytes_per_step": 204439628, "read": 203085718, "written": 1353910},
+    "tinyllama": {"source": "bfcd777ef73f6a23", "bytes_per_step": 23228537, "read": 22233209, "written": 995328},
+    "tiny": {"source": "bfcd777ef73f6a23", "bytes_per_step": 585074, "read": 583794, "written": 1280},
+    "gpt2": {"source": "bfcd777ef73f6a23", "bytes_per_step": 42712704, "read": 42532480, "written": 180224},
+    "llama_long": {"source": "bfcd777ef73f6a23", "bytes_per_step": 202224362, "read": 202085098, "written": 139264},
+    "ragged": {"source": "bfcd777ef73f6a23", "bytes_per_step": 403173188, "read": 401677334, "written": 1495854},
+    "tinyllama:fp8e4m3": {"source": "bfcd777ef73f6a23", "bytes_per_step": 12821446, "read": 11826118, "written": 995328},
+    "llama_long:fp8e4m3": {"source": "bfcd777ef73f6a23", "bytes_per_step": 101566969, "read": 101427705, "written": 139264},
+    "ragged:fp8e4m3": {"source": "bfcd777ef73f6a23", "bytes_per_step": 204397178, "read": 203042668, "written": 1354510},
 }
 
 
