@@ -66,14 +66,14 @@ KERNEL_SOURCES = [os.path.join(ROOT, "query_aware_sparse_bbox_amd", "csrc", f)
 # hex digits).  Keys: configuration, or configuration:KV type when the
 # configuration's KV type is overridden.
 TRAFFIC = {
-    "tinyllama": {"source": "bfcd777ef73f6a23", "bytes_per_step": 23228537, "read": 22233209, "written": 995328},
-    "tiny": {"source": "bfcd777ef73f6a23", "bytes_per_step": 585074, "read": 583794, "written": 1280},
-    "gpt2": {"source": "bfcd777ef73f6a23", "bytes_per_step": 42712704, "read": 42532480, "written": 180224},
-    "llama_long": {"source": "bfcd777ef73f6a23", "bytes_per_step": 202224362, "read": 202085098, "written": 139264},
-    "ragged": {"source": "bfcd777ef73f6a23", "bytes_per_step": 403173188, "read": 401677334, "written": 1495854},
-    "tinyllama:fp8e4m3": {"source": "bfcd777ef73f6a23", "bytes_per_step": 12821446, "read": 11826118, "written": 995328},
-    "llama_long:fp8e4m3": {"source": "bfcd777ef73f6a23", "bytes_per_step": 101566969, "read": 101427705, "written": 139264},
-    "ragged:fp8e4m3": {"source": "bfcd777ef73f6a23", "bytes_per_step": 204397178, "read": 203042668, "written": 1354510},
+    "tinyllama": {"source": "928756b5314509d8", "bytes_per_step": 23229112, "read": 22233784, "written": 995328},
+    "tiny": {"source": "928756b5314509d8", "bytes_per_step": 598392, "read": 597112, "written": 1280},
+    "gpt2": {"source": "928756b5314509d8", "bytes_per_step": 42732534, "read": 42552310, "written": 180224},
+    "llama_long": {"source": "928756b5314509d8", "bytes_per_step": 202323770, "read": 202184506, "written": 139264},
+    "ragged": {"source": "928756b5314509d8", "bytes_per_step": 403169199, "read": 401673338, "written": 1495861},
+    "tinyllama:fp8e4m3": {"source": "928756b5314509d8", "bytes_per_step": 12806429, "read": 11811101, "written": 995328},
+    "llama_long:fp8e4m3": {"source": "928756b5314509d8", "bytes_per_step": 101613955, "read": 101474691, "written": 139264},
+    "ragged:fp8e4m3": {"source": "928756b5314509d8", "bytes_per_step": 204417300, "read": 203062955, "written": 1354344},
 }
 
 

@@ -2112,13 +2112,12 @@ hipError_t launch_score_select(const Dims& d, const float* q, const void* meta,
 
 // Threads of a k_step workgroup.  Rows that fill the chip twice over get 4
 // waves each, so two rows share a CU and one row's select / combine phases
-// overlap the other's streaming; fewer rows get 8 waves, and single-head
-// groups (whose scoring keeps only two query rows in registers) 16 while the
-// rows alone do not fill the chip.
+// overlap the other's streaming; fewer rows get 8 waves.  16-wave workgroups
+// for single-head groups measured slower than 8 (46.8 against 45.7 us on
+// 256 rows of 1024 pages, 9.5 against 8.5 us on 4 rows of 64).
 int step_threads(const Dims& d) {
   const long units = (long)d.B * d.Hkv;
-  if (units >= 512) return 256;
-  return d.G == 1 && units <= 256 ? 1024 : 512;
+  return units >= 512 ? 256 : 512;
 }
 
 size_t step_lds_bytes(const Dims& d) {
@@ -2128,8 +2127,6 @@ size_t step_lds_bytes(const Dims& d) {
     constexpr int dt = decltype(DT)::value, hd = decltype(HD)::value,
                   g = decltype(GG)::value;
     dec = nt == 256 ? step_decode_lds<dt, hd, g, 256>() : step_decode_lds<dt, hd, g, 512>();
-    if constexpr (g == 1)
-      if (nt == 1024) dec = step_decode_lds<dt, hd, g, 1024>();
     return hipSuccess;
   });
   return (size_t)2 * ((d.MP + 3) & ~3) * sizeof(uint32_t) + dec;
@@ -2184,8 +2181,6 @@ hipError_t launch_step(const Dims& d, const float* q, const void* k_new, const v
                          sel_count, scores_out, ws.sync, ws.keys, ws.partials, out);
       return hipGetLastError();
     };
-    if constexpr (g == 1)
-      if (nt == 1024) return go(IC<1024>{});
     return nt == 256 ? go(IC<256>{}) : go(IC<512>{});
   });
   return e;
