@@ -17,7 +17,9 @@ Prints one JSON line:
                workgroups merge inside it); `traffic` = HBM bytes per
                step from rocprofv3 counters when they were taken on the current
                kernel source, else null
-  cpu_baseline the CPU oracle (single thread) on a bounded sample of the step
+  cpu_baseline the CPU oracle, unchanged, on the same step: one sequence per
+               task on a pool of host threads (median of 3 runs), plus a
+               single-thread run; thread count and CPU model recorded
   selection_quality  share of the exact softmax mass (float64, sampled rows)
                that falls on the kept pages, and the same step with every page
                kept (dense) timed the same way
@@ -28,6 +30,7 @@ reference kernel for scaling the HBM byte counters) and exits.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import math
@@ -44,7 +47,7 @@ import workloads as W  # noqa: E402
 
 PEAK_HBM_GBS = 8000.0
 METRIC = "sparse decode attention: (seq·head)/s + achieved HBM GB/s vs peak"
-DEFAULT_CONFIG = "tinyllama"
+DEFAULT_CONFIG = "ragged"
 DESCR = {
     "tiny": "tiny MHA decode: B=1, 4 heads, D=64, 1024 tokens, page 16, top-8, fp32 KV",
     "tinyllama": "TinyLLaMA-1.1B-shaped GQA decode: B=16, 32/4 heads, D=64, 4096 tokens, "
@@ -57,7 +60,8 @@ DESCR = {
               "budget min(64, 20%), fp16 KV, shared shuffled pool, 1 append per step",
 }
 KERNEL_SOURCES = [os.path.join(ROOT, "query_aware_sparse_bbox_amd", "csrc", f)
-                  for f in ("tsv_kernels.hip", "tsv_api.hip", "tsv_launch.h")]
+                  for f in ("tsv_device.h", "tsv_kernels.hip", "tsv_host.hip", "tsv_api.hip",
+                            "tsv_launch.h")]
 
 # HBM bytes per step (all its kernels) from `rocprofv3 --pmc FETCH_SIZE` and
 # `--pmc WRITE_SIZE` runs of this script, each divided by the same counter's
@@ -111,6 +115,85 @@ def step_bytes(wl, lens, sel, cnt):
                 total=meta + kv + qo + table + append)
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def host_threads(requested: int) -> int:
+    """Threads for the oracle baseline: the CPUs this process may run on, at
+    most 16 (the host share of one GPU), unless given explicitly."""
+    if requested > 0:
+        return requested
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(n, 16))
+
+
+def cpu_baseline(wl, st, lens_np, q_np, kps_np, k_max, n_sink, scale, args, agg):
+    """The oracle's full step (append, score, select, attend) on the host."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    import oracle as O
+
+    sh = wl.shape
+    kp, vp = wl.k_pool.copy(), wl.v_pool.copy()
+    meta = O.meta_build(sh, kp, wl.block_table, lens_np - 1 if st else lens_np)
+    one = dataclasses.replace(sh, batch=1)
+    kn = st.k_new if st else None
+    vn = st.v_new if st else None
+
+    def seq_step(b):
+        O.decode_step(one, q_np[b:b + 1], kp, vp, meta, wl.block_table[b:b + 1],
+                      lens_np[b:b + 1], k_max, scale,
+                      None if kps_np is None else kps_np[b:b + 1], n_sink,
+                      None if kn is None else kn[b:b + 1],
+                      None if vn is None else vn[b:b + 1], args.recent, agg)
+
+    def full_step(pool):
+        if pool is None:
+            for b in range(sh.batch):
+                seq_step(b)
+        else:
+            list(pool.map(seq_step, range(sh.batch)))
+
+    def timed(pool, min_s):
+        reps, t = 0, 0.0
+        while reps == 0 or t < min_s:
+            c0 = time.perf_counter()
+            full_step(pool)
+            t += time.perf_counter() - c0
+            reps += 1
+        return t / reps, reps
+
+    # single thread first (it also initialises the oracle's lookup tables)
+    t1, reps1 = timed(None, args.cpu_seconds / 2)
+    nthr = host_threads(args.cpu_threads)
+    with ThreadPoolExecutor(max_workers=nthr) as pool:
+        runs = [timed(pool, min(1.0, args.cpu_seconds / 6)) for _ in range(3)]
+    tn = float(np.median([r[0] for r in runs]))
+    B, Hq = sh.batch, sh.num_q_heads
+    return {"value": B * Hq / tn, "unit": "(seq·head)/s", "cores": nthr, "kind": "oracle",
+            "sample": f"the full decode step of the same workload (append, score, select, "
+                      f"attend; boxes built beforehand), one sequence per task on {nthr} "
+                      f"host threads, median of 3 runs of {runs[0][1]}+ step(s); single "
+                      f"thread: {reps1} step(s)",
+            "threads_step_ms": tn * 1e3,
+            "runs_step_ms": [r[0] * 1e3 for r in runs],
+            "single_thread_value": B * Hq / t1,
+            "single_thread_step_ms": t1 * 1e3,
+            "cpu_model": cpu_model(),
+            "host_cpus_visible": os.cpu_count()}
+
+
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -125,7 +208,11 @@ def parse():
                     help="always keep the last N pages of every sequence (local window)")
     ap.add_argument("--rotate", type=int, default=0, help="pool copies (0: auto, >=512 MB)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
-                    help="CPU-oracle baseline budget (0 disables it)")
+                    help="CPU-oracle baseline: minimum seconds of each single-thread "
+                         "measurement (0 disables the leg)")
+    ap.add_argument("--cpu-threads", type=int, default=0,
+                    help="host threads of the threaded oracle run (0: the CPUs this "
+                         "process may use, at most 16)")
     ap.add_argument("--eager", action="store_true", help="launch steps one by one (no graph)")
     ap.add_argument("--no-quality", action="store_true",
                     help="skip the selection-quality / dense-speedup report")
@@ -246,19 +333,30 @@ def main():
 
     graphs = {}
 
-    def run(nsteps):
-        """Exactly nsteps steps, instance i % R for step i."""
+    def run(nsteps, marks=None):
+        """Exactly nsteps steps, instance i % R for step i.  With `marks`, an
+        event is recorded on the stream after every replay (every step when
+        eager) and appended with the number of steps it closes."""
+        def mark(count):
+            if marks is not None:
+                ev = torch.cuda.Event(enable_timing=True)
+                ev.record(stream)
+                marks.append((ev, count))
+
         if args.eager:
             for i in range(nsteps):
                 step(insts[i % R])
+                mark(1)
             return
         for _ in range(nsteps // R):
             graphs["full"].replay()
+            mark(R)
         rem = nsteps % R
         if rem:
             if rem not in graphs:
                 graphs[rem] = capture(insts[:rem])
             graphs[rem].replay()
+            mark(rem)
 
     if not args.eager:
         graphs["full"] = capture(insts)
@@ -277,13 +375,21 @@ def main():
     torch.cuda.synchronize()
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     wall0 = time.perf_counter()
+    marks = []
     t0.record(stream)
-    run(K)
+    run(K, marks)
     t1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms_step = t0.elapsed_time(t1) / K
-    print(f"[bench] step {ms_step * 1e3:.2f} us (wall {wall / K * 1e6:.2f} us/step)", flush=True)
+    # per-replay step times (each replay closes R steps, or 1 when eager)
+    per, prev = [], t0
+    for ev, count in marks:
+        per.append(prev.elapsed_time(ev) / count)
+        prev = ev
+    ms_median = float(np.median(per))
+    print(f"[bench] step {ms_step * 1e3:.2f} us mean, {ms_median * 1e3:.2f} us median over "
+          f"{len(per)} replays (wall {wall / K * 1e6:.2f} us/step)", flush=True)
 
     # selection quality: the share of exact softmax mass on the kept pages,
     # and the same step with every page kept (the dense baseline, same kernels)
@@ -360,25 +466,17 @@ def main():
               flush=True)
         del dense, gd
 
-    # CPU oracle baseline (single thread) on a bounded sample of the same step
+    # CPU oracle baseline on the same step: the oracle unchanged, one
+    # sequence per task (its own block-table row, query, budget and appended
+    # token; the pools are shared, each task writes only its own pages) on a
+    # pool of host threads (ctypes releases the GIL), median of 3 runs; and a
+    # single-thread run of the same tasks
     cpu = None
     if args.cpu_seconds > 0:
-        import oracle as O
-        kp, vp = wl.k_pool.copy(), wl.v_pool.copy()
-        meta = O.meta_build(sh, kp, wl.block_table, lens_np - 1 if st else lens_np)
-        reps, t_cpu = 0, 0.0
-        while t_cpu < args.cpu_seconds:
-            c0 = time.perf_counter()
-            O.decode_step(sh, q_np, kp, vp, meta, wl.block_table, lens_np, k_max, scale,
-                          kps_np, n_sink, st.k_new if st else None, st.v_new if st else None,
-                          args.recent, agg)
-            t_cpu += time.perf_counter() - c0
-            reps += 1
-        cpu = {"value": B * Hq * reps / t_cpu, "unit": "(seq·head)/s", "cores": 1,
-               "kind": "oracle",
-               "sample": f"{reps} full decode step(s) of the same workload "
-                         f"({t_cpu:.1f} s, single-threaded C oracle, boxes prebuilt)"}
-        print(f"[bench] cpu oracle {t_cpu / reps * 1e3:.1f} ms/step", flush=True)
+        cpu = cpu_baseline(wl, st, lens_np, q_np, kps_np, k_max, n_sink, scale, args, agg)
+        print(f"[bench] cpu oracle {cpu['threads_step_ms']:.1f} ms/step on "
+              f"{cpu['cores']} threads, {cpu['single_thread_step_ms']:.1f} ms/step on 1",
+              flush=True)
 
     value = B * Hq / (ms_step * 1e-3)
     step_gbs = nb["total"] / (ms_step * 1e-3) / 1e9
@@ -417,6 +515,8 @@ def main():
                      "algorithmic_bytes_per_step": nb["total"],
                      "launches_per_step": launches,
                      "mean_step_us": ms_step * 1e3,
+                     "median_step_us": ms_median * 1e3,
+                     "median_of": f"{len(per)} replays of {1 if args.eager else R} step(s)",
                      "timed_as": "HIP events on the launch stream around the graph-replayed "
                                  "steps, divided by the step count",
                      "kernel_source": src},

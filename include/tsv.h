@@ -106,15 +106,6 @@ enum {
 /* Library version (TSV_VERSION). */
 int tsv_version(void);
 
-/* Testing hook, process-wide.  When a row's step is spread over several
-   workgroups they exchange page scores; a workgroup that finds the others'
-   scores missing after `polls` reads of the row's counter scores the rest of
-   the row itself, which gives bit-identical results (only the time differs).
-   polls >= 0 sets the limit for later calls and returns the previous one;
-   polls < 0 only returns the current one (default 16384).  Tests set 0 to
-   drive that path. */
-int tsv_debug_exchange_polls(int32_t polls);
-
 /* Static description of a status code. */
 const char* tsv_status_string(int status);
 
@@ -154,7 +145,10 @@ int tsv_meta_build(const tsv_shape* shape, const void* k_pool, void* meta,
                    const int32_t* block_table, const int32_t* seq_lens,
                    void* stream);
 
-/* Append one token per sequence and keep its page's box current.
+/* Append one token per sequence and keep its page's box current (method
+   details, key design: every block keeps the bounding box of the keys it
+   holds, so the box of the block receiving a decoded token widens as the
+   token lands; the token also joins the cache that attention reads).
    seq_lens already counts the new token; k_new / v_new [B][Hkv][D] (KV dtype)
    go to slot (len_b-1) % P of physical page block_table[b][(len_b-1)/P],
    which the caller must have allocated.  Slot 0 resets the box to the new

@@ -1,10 +1,19 @@
 // C-ABI host layer of libtsv: argument validation, workspace carving and
 // kernel launches.  Every check runs before the first HIP call, so a rejected
 // call has touched neither the device nor the runtime.
+//
+// Built twice: the library proper, which keeps no state between calls, and a
+// testing library (TSV_TEST_HOOKS) that also exports the hook declared in
+// tsv_testing.h.
 #include <stdint.h>
+
+#include <atomic>
 
 #include "../../include/tsv.h"
 #include "tsv_launch.h"
+#ifdef TSV_TEST_HOOKS
+#include "../../include/tsv_testing.h"
+#endif
 
 static_assert(tsv::kSyncBytes == TSV_WORKSPACE_ZERO_BYTES, "zeroed workspace prefix");
 
@@ -98,15 +107,25 @@ int check_decode_args(const Dims& d, const float* q, const void* k_pool,
 
 int hip_status(hipError_t e) { return e == hipSuccess ? TSV_OK : TSV_ERR_HIP; }
 
+#ifdef TSV_TEST_HOOKS
+// Polls of a split row's score exchange, settable by tsv_debug_exchange_polls.
+std::atomic<int> g_exchange_polls{tsv::kDefaultExchangePolls};
+int exchange_polls() { return g_exchange_polls.load(std::memory_order_relaxed); }
+#else
+constexpr int exchange_polls() { return tsv::kDefaultExchangePolls; }
+#endif
+
 }  // namespace
 
 extern "C" {
 
 int tsv_version(void) { return TSV_VERSION; }
 
+#ifdef TSV_TEST_HOOKS
 int tsv_debug_exchange_polls(int32_t polls) {
-  return polls < 0 ? tsv::exchange_polls() : tsv::set_exchange_polls(polls);
+  return polls < 0 ? g_exchange_polls.load() : g_exchange_polls.exchange(polls);
 }
+#endif
 
 const char* tsv_status_string(int status) {
   switch (status) {
@@ -213,33 +232,41 @@ int tsv_sparse_decode(const tsv_shape* shape, const float* q, const void* k_pool
                                        (hipStream_t)stream));
 }
 
-int tsv_decode_step_ex(const tsv_shape* shape, const float* q, const void* k_new,
-                       const void* v_new, void* k_pool, void* v_pool, void* meta,
-                       const int32_t* block_table, const int32_t* seq_lens,
-                       int32_t k_max, const int32_t* k_per_seq, int32_t n_sink,
-                       const tsv_select_opts* opts, float scale, int32_t* sel,
-                       int32_t* sel_count, float* scores_out, float* out,
-                       void* workspace, size_t workspace_bytes, void* stream) {
-  Dims d;
-  int rc = check_shape(shape, &d);
+namespace {
+
+// Checks of tsv_decode_step_ex / tsv_decode_step_noalloc other than the
+// workspace's; fills d and pol.
+int check_step(const tsv_shape* shape, const float* q, const void* k_new, const void* v_new,
+               const void* k_pool, const void* v_pool, const void* meta,
+               const int32_t* block_table, const int32_t* seq_lens, int32_t k_max,
+               int32_t n_sink, const tsv_select_opts* opts, const int32_t* sel,
+               const int32_t* sel_count, const float* out, Dims* d, tsv::SelectPolicy* pol) {
+  int rc = check_shape(shape, d);
   if (rc) return rc;
   if ((k_new == nullptr) != (v_new == nullptr)) return TSV_ERR_INVALID_ARG;
-  rc = check_select_args(d, q, meta, block_table, seq_lens, k_max, sel, sel_count,
-                         workspace, workspace_bytes);
-  if (rc) return rc;
-  rc = check_decode_args(d, q, k_pool, v_pool, block_table, seq_lens, sel,
-                         sel_count, k_max, out, workspace, workspace_bytes);
-  if (rc) return rc;
-  tsv::SelectPolicy pol;
-  rc = make_policy(k_max, n_sink, opts, &pol);
-  if (rc) return rc;
-  hipStream_t s = (hipStream_t)stream;
+  if (!q || !meta || !block_table || !seq_lens || !sel || !sel_count || !k_pool || !v_pool ||
+      !out)
+    return TSV_ERR_INVALID_ARG;
+  if (k_max < 1) return TSV_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(meta, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16) ||
+      !aligned(out, 16))
+    return TSV_ERR_INVALID_ARG;
+  return make_policy(k_max, n_sink, opts, pol);
+}
+
+// The step on a checked call, with its workspace at `workspace`.
+int run_step(const Dims& d, const tsv::SelectPolicy& pol, const float* q, const void* k_new,
+             const void* v_new, void* k_pool, void* v_pool, void* meta,
+             const int32_t* block_table, const int32_t* seq_lens, int32_t k_max,
+             const int32_t* k_per_seq, float scale, int32_t* sel, int32_t* sel_count,
+             float* scores_out, float* out, void* workspace, hipStream_t s) {
   tsv::Workspace ws;
   tsv::workspace_layout(d, k_max, workspace, &ws);
   if (tsv::step_fits(d))  // every row's whole step in its own workgroup(s)
-    return hip_status(tsv::launch_step(d, q, k_new, v_new, k_pool, v_pool, meta,
-                                       block_table, seq_lens, k_max, k_per_seq, pol,
+    return hip_status(tsv::launch_step(d, exchange_polls(), q, k_new, v_new, k_pool, v_pool,
+                                       meta, block_table, seq_lens, k_max, k_per_seq, pol,
                                        scale, sel, sel_count, scores_out, ws, out, s));
+  int rc;
   if (k_new) {
     rc = hip_status(tsv::launch_meta_append(d, k_new, v_new, k_pool, v_pool, meta,
                                             block_table, seq_lens, s));
@@ -252,6 +279,27 @@ int tsv_decode_step_ex(const tsv_shape* shape, const float* q, const void* k_new
   return hip_status(tsv::launch_decode(d, q, k_pool, v_pool, block_table, seq_lens,
                                        sel, ws.sel_phys, sel_count, k_max, scale, ws,
                                        out, s));
+}
+
+}  // namespace
+
+int tsv_decode_step_ex(const tsv_shape* shape, const float* q, const void* k_new,
+                       const void* v_new, void* k_pool, void* v_pool, void* meta,
+                       const int32_t* block_table, const int32_t* seq_lens,
+                       int32_t k_max, const int32_t* k_per_seq, int32_t n_sink,
+                       const tsv_select_opts* opts, float scale, int32_t* sel,
+                       int32_t* sel_count, float* scores_out, float* out,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+  Dims d;
+  tsv::SelectPolicy pol;
+  int rc = check_step(shape, q, k_new, v_new, k_pool, v_pool, meta, block_table, seq_lens,
+                      k_max, n_sink, opts, sel, sel_count, out, &d, &pol);
+  if (rc) return rc;
+  rc = check_workspace(d, k_max, workspace, workspace_bytes);
+  if (rc) return rc;
+  return run_step(d, pol, q, k_new, v_new, k_pool, v_pool, meta, block_table, seq_lens, k_max,
+                  k_per_seq, scale, sel, sel_count, scores_out, out, workspace,
+                  (hipStream_t)stream);
 }
 
 int tsv_decode_step(const tsv_shape* shape, const float* q, const void* k_new,

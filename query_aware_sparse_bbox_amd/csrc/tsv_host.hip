@@ -1,0 +1,182 @@
+// Host-side launch planning of libtsv: workspace carving, decode split sizes,
+// the one-launch step's workgroup shape, and dispatch to the launchers of the
+// call's KV type.  No device code.
+#include <algorithm>
+#include <type_traits>
+
+#include "tsv_launch.h"
+
+namespace tsv {
+namespace {
+
+constexpr int kWave = 64;
+
+template <int V>
+using IC = std::integral_constant<int, V>;
+
+template <class Fn>
+hipError_t by_dtype(int dt, Fn&& fn) {
+  switch (dt) {
+    case DT_F32: return fn(IC<DT_F32>{});
+    case DT_F16: return fn(IC<DT_F16>{});
+    case DT_BF16: return fn(IC<DT_BF16>{});
+    case DT_F8: return fn(IC<DT_F8>{});
+    case DT_F8E5: return fn(IC<DT_F8E5>{});
+  }
+  return hipErrorInvalidValue;
+}
+
+size_t round_up(size_t x) { return (x + 255) / 256 * 256; }
+
+// A launch is checked with hipGetLastError, which also reports (and clears)
+// an error some earlier runtime call of the caller's thread left behind;
+// clearing it first makes the check see this call's launches only.
+void clear_stale_error() { (void)hipGetLastError(); }
+
+// Grouped-query heads on 16-bit or fp8 KV take the MFMA decode (64-token
+// steps); everything else the VALU decode.
+bool use_mfma_decode(const Dims& d) { return d.dt != DT_F32 && (d.G == 4 || d.G == 8); }
+
+// Tiles per workgroup: enough workgroups to fill the chip several times
+// over, each streaming as many tiles as that allows.
+int decode_tiles_per_split(const Dims& d, int k_max) {
+  const long tile = decode_tile_tokens(d);
+  const long tiles_per_row = ((long)k_max * d.P + tile - 1) / tile;
+  const long total = tiles_per_row * d.B * d.Hkv;
+  return (int)std::max(1L, std::min((long)kMaxTilesPerSplit, total / 1024));
+}
+
+// Threads of a k_step workgroup.  Rows that fill the chip twice over get 4
+// waves each, so two rows share a CU and one row's select / combine phases
+// overlap the other's streaming; fewer rows get 8 waves.  16-wave workgroups
+// for single-head groups measured slower than 8 (46.8 against 45.7 us on
+// 256 rows of 1024 pages, 9.5 against 8.5 us on 4 rows of 64).
+int step_threads(const Dims& d) {
+  const long units = (long)d.B * d.Hkv;
+  return units >= 512 ? 256 : 512;
+}
+
+// Dynamic LDS of k_step: block-table row and keys (MP words each, rounded to
+// 4), then every wave's combine area (G rows of D + 1 floats).
+size_t step_lds_bytes(const Dims& d) {
+  const int nw = step_threads(d) / kWave;
+  const size_t dec = (size_t)nw * d.G * (d.D + 1) * sizeof(float);
+  return (size_t)2 * ((d.MP + 3) & ~3) * sizeof(uint32_t) + dec;
+}
+
+// Workgroups per row: rows that leave most of the 256 CUs idle are spread
+// over up to 8 workgroups each (they share the scoring, every one selects the
+// whole row, then decodes its share of the kept tokens), as far as k_max
+// pages give each split its minimum span; the last split to finish merges.
+// Only the first kSyncRows rows have synchronisation counters.
+int step_splits(const Dims& d, int k_max) {
+  const long units = (long)d.B * d.Hkv;
+  const long minspan = kStepMinSpanSteps * 16 * (step_threads(d) / kWave);
+  const long by_tokens = (long)k_max * d.P / minspan;
+  if (units > kSyncRows) return 1;
+  return (int)std::max(1L, std::min({(long)kStepMaxSplits, 256 / units, by_tokens}));
+}
+
+}  // namespace
+
+int decode_tile_tokens(const Dims& d) {
+  if (use_mfma_decode(d)) return 64;
+  const int C = kv_vec(d.dt), L = d.D / C, SPW = kWave / L;
+  return 4 * (kDecodeThreads / kWave) * SPW;
+}
+
+int decode_splits(const Dims& d, int k_max) {
+  const long span = (long)decode_tile_tokens(d) * decode_tiles_per_split(d, k_max);
+  return (int)(((long)k_max * d.P + span - 1) / span);
+}
+
+DecodePlan plan_decode(const Dims& d, int k_max) {
+  return DecodePlan{decode_splits(d, k_max), decode_tiles_per_split(d, k_max),
+                    decode_tile_tokens(d)};
+}
+
+size_t workspace_layout(const Dims& d, int k_max, void* base, Workspace* ws) {
+  const size_t units = (size_t)d.B * d.Hkv;
+  const size_t o_sync = 0;
+  const size_t o_keys = o_sync + kSyncBytes;
+  const size_t o_phys = o_keys + round_up(units * d.MP * sizeof(uint32_t));
+  const size_t o_part = o_phys + round_up(units * k_max * sizeof(int32_t));
+  const size_t splits = std::max(decode_splits(d, k_max), step_splits(d, k_max));
+  const size_t total =
+      o_part + round_up((size_t)d.B * d.Hq * splits * partial_stride(d) * sizeof(float));
+  if (base && ws) {
+    char* c = static_cast<char*>(base);
+    ws->sync = reinterpret_cast<uint32_t*>(c + o_sync);
+    ws->keys = reinterpret_cast<uint32_t*>(c + o_keys);
+    ws->sel_phys = reinterpret_cast<int32_t*>(c + o_phys);
+    ws->partials = reinterpret_cast<float*>(c + o_part);
+  }
+  return total;
+}
+
+bool step_fits(const Dims& d) { return step_lds_bytes(d) <= kStepMaxLds; }
+
+StepPlan plan_step(const Dims& d, int k_max, int polls) {
+  return StepPlan{step_threads(d), step_splits(d, k_max), polls, step_lds_bytes(d)};
+}
+
+hipError_t launch_meta_build(const Dims& d, const void* k_pool, void* meta,
+                             const int32_t* bt, const int32_t* seq_lens, hipStream_t s) {
+  clear_stale_error();
+  return by_dtype(d.dt, [&](auto DT) {
+    return meta_build_t<decltype(DT)::value>(d, k_pool, meta, bt, seq_lens, s);
+  });
+}
+
+hipError_t launch_meta_append(const Dims& d, const void* k_new, const void* v_new,
+                              void* k_pool, void* v_pool, void* meta, const int32_t* bt,
+                              const int32_t* seq_lens, hipStream_t s) {
+  clear_stale_error();
+  return by_dtype(d.dt, [&](auto DT) {
+    return meta_append_t<decltype(DT)::value>(d, k_new, v_new, k_pool, v_pool, meta, bt,
+                                              seq_lens, s);
+  });
+}
+
+hipError_t launch_score_select(const Dims& d, const float* q, const void* meta,
+                               const int32_t* bt, const int32_t* seq_lens, int k_max,
+                               const int32_t* k_per_seq, const SelectPolicy& pol,
+                               int32_t* sel, int32_t* sel_count, float* scores_out,
+                               const Workspace& ws, hipStream_t s) {
+  clear_stale_error();
+  return by_dtype(d.dt, [&](auto DT) {
+    return score_select_t<decltype(DT)::value>(d, q, meta, bt, seq_lens, k_max, k_per_seq, pol,
+                                               sel, sel_count, scores_out, ws, s);
+  });
+}
+
+hipError_t launch_decode(const Dims& d, const float* q, const void* k_pool,
+                         const void* v_pool, const int32_t* bt, const int32_t* seq_lens,
+                         const int32_t* sel, const int32_t* sel_phys,
+                         const int32_t* sel_count, int k_max, float scale,
+                         const Workspace& ws, float* out, hipStream_t s) {
+  const DecodePlan plan = plan_decode(d, k_max);
+  clear_stale_error();
+  return by_dtype(d.dt, [&](auto DT) {
+    return decode_t<decltype(DT)::value>(d, plan, q, k_pool, v_pool, bt, seq_lens, sel,
+                                         sel_phys, sel_count, k_max, scale, ws, out, s);
+  });
+}
+
+hipError_t launch_step(const Dims& d, int polls, const float* q, const void* k_new,
+                       const void* v_new, void* k_pool, void* v_pool, void* meta,
+                       const int32_t* bt, const int32_t* seq_lens, int k_max,
+                       const int32_t* k_per_seq, const SelectPolicy& pol, float scale,
+                       int32_t* sel, int32_t* sel_count, float* scores_out,
+                       const Workspace& ws, float* out, hipStream_t s) {
+  const StepPlan plan = plan_step(d, k_max, polls);
+  if (plan.lds > kStepMaxLds) return hipErrorInvalidValue;
+  clear_stale_error();
+  return by_dtype(d.dt, [&](auto DT) {
+    return step_t<decltype(DT)::value>(d, plan, q, k_new, v_new, k_pool, v_pool, meta, bt,
+                                       seq_lens, k_max, k_per_seq, pol, scale, sel, sel_count,
+                                       scores_out, ws, out, s);
+  });
+}
+
+}  // namespace tsv

@@ -1,5 +1,7 @@
-// Internal interface between the C-ABI host layer (tsv_api.hip) and the
-// gfx950 kernels (tsv_kernels.hip).  Not installed; not part of the ABI.
+// Internal interface between the C-ABI host layer (tsv_api.hip), the host-side
+// launch planning (tsv_host.hip) and the gfx950 kernels (tsv_kernels.hip,
+// built once per KV type and kernel family).  Not installed; not part of the
+// ABI.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stddef.h>
@@ -30,6 +32,16 @@ struct Dims {
 };
 
 constexpr int kMaxPagesPerSeq = 4096;
+// Decode tiles one workgroup of the phased decode streams at most.
+constexpr int kMaxTilesPerSplit = 8;
+// Threads of a phased (VALU) decode workgroup.
+constexpr int kDecodeThreads = 256;
+// Most workgroups a row of the one-launch step is spread over.
+constexpr int kStepMaxSplits = 8;
+// A split of a row covers at least this many 16-token steps per wave.
+constexpr int kStepMinSpanSteps = 2;
+// Rows of at most this many pages are selected by one wave.
+constexpr int kWaveSelectMaxPages = 512;
 
 // Tokens of the selected-token stream one decode workgroup covers.
 int decode_tile_tokens(const Dims& d);
@@ -57,53 +69,82 @@ struct Workspace {
 // Total workspace bytes; with `base` non-null also fills `ws`.
 size_t workspace_layout(const Dims& d, int k_max, void* base, Workspace* ws);
 
+// Phased decode: S_max split slots per row, TPW tiles per split.
+struct DecodePlan {
+  int S_max, TPW, tile_tokens;
+};
+DecodePlan plan_decode(const Dims& d, int k_max);
+
+// One-launch step: nt threads per workgroup, S workgroups per row, lds bytes
+// of dynamic local memory, `polls` reads of a row's flag before a split stops
+// waiting for the row's other splits' page keys.
+struct StepPlan {
+  int nt, S, polls;
+  size_t lds;
+};
+// Polls when no testing hook overrides them (several milliseconds: only
+// reached if a row's workgroups are not resident at the same time).
+constexpr int kDefaultExchangePolls = 1 << 14;
+constexpr size_t kStepMaxLds = 64 * 1024;
+StepPlan plan_step(const Dims& d, int k_max, int polls);
+// The whole step of a (sequence, KV head) fits the one-launch kernel: its
+// local memory, which grows with max_pages_per_seq, stays within kStepMaxLds.
+bool step_fits(const Dims& d);
+
+// Launchers, one instantiation per KV type (defined in tsv_kernels.hip).
+template <int DT>
+hipError_t meta_build_t(const Dims& d, const void* k_pool, void* meta, const int32_t* bt,
+                        const int32_t* seq_lens, hipStream_t s);
+template <int DT>
+hipError_t meta_append_t(const Dims& d, const void* k_new, const void* v_new, void* k_pool,
+                         void* v_pool, void* meta, const int32_t* bt, const int32_t* seq_lens,
+                         hipStream_t s);
+template <int DT>
+hipError_t score_select_t(const Dims& d, const float* q, const void* meta, const int32_t* bt,
+                          const int32_t* seq_lens, int k_max, const int32_t* k_per_seq,
+                          const SelectPolicy& pol, int32_t* sel, int32_t* sel_count,
+                          float* scores_out, const Workspace& ws, hipStream_t s);
+template <int DT>
+hipError_t decode_t(const Dims& d, const DecodePlan& plan, const float* q, const void* k_pool,
+                    const void* v_pool, const int32_t* bt, const int32_t* seq_lens,
+                    const int32_t* sel, const int32_t* sel_phys, const int32_t* sel_count,
+                    int k_max, float scale, const Workspace& ws, float* out, hipStream_t s);
+template <int DT>
+hipError_t step_t(const Dims& d, const StepPlan& plan, const float* q, const void* k_new,
+                  const void* v_new, void* k_pool, void* v_pool, void* meta, const int32_t* bt,
+                  const int32_t* seq_lens, int k_max, const int32_t* k_per_seq,
+                  const SelectPolicy& pol, float scale, int32_t* sel, int32_t* sel_count,
+                  float* scores_out, const Workspace& ws, float* out, hipStream_t s);
+
+// Dispatch by KV type (tsv_host.hip).
 hipError_t launch_meta_build(const Dims& d, const void* k_pool, void* meta,
-                             const int32_t* bt, const int32_t* seq_lens,
-                             hipStream_t s);
-
-hipError_t launch_meta_append(const Dims& d, const void* k_new,
-                              const void* v_new, void* k_pool, void* v_pool,
-                              void* meta, const int32_t* bt,
+                             const int32_t* bt, const int32_t* seq_lens, hipStream_t s);
+hipError_t launch_meta_append(const Dims& d, const void* k_new, const void* v_new,
+                              void* k_pool, void* v_pool, void* meta, const int32_t* bt,
                               const int32_t* seq_lens, hipStream_t s);
-
 // Scores every page, keeps the top pages; also fills ws.sel_phys.
 hipError_t launch_score_select(const Dims& d, const float* q, const void* meta,
-                               const int32_t* bt, const int32_t* seq_lens,
-                               int k_max, const int32_t* k_per_seq,
-                               const SelectPolicy& pol, int32_t* sel, int32_t* sel_count,
-                               float* scores_out,
+                               const int32_t* bt, const int32_t* seq_lens, int k_max,
+                               const int32_t* k_per_seq, const SelectPolicy& pol,
+                               int32_t* sel, int32_t* sel_count, float* scores_out,
                                const Workspace& ws, hipStream_t s);
-
 // Split decode; units with several tiles are merged by a second kernel.
 // sel_phys (nullable): physical page of every selected entry, so the decode
 // skips the block-table lookup.
 hipError_t launch_decode(const Dims& d, const float* q, const void* k_pool,
-                         const void* v_pool, const int32_t* bt,
-                         const int32_t* seq_lens, const int32_t* sel,
-                         const int32_t* sel_phys, const int32_t* sel_count,
-                         int k_max, float scale, const Workspace& ws, float* out,
-                         hipStream_t s);
-
-// The whole step of one (sequence, KV head) in one workgroup (or in
-// step_splits(d) workgroups that share the row's scoring, each select the
-// whole row and decode a share of it; the last one to finish merges the
-// shares): [append] -> score -> top-K -> decode, one launch.  Usable when
-// step_fits(d) (its LDS, which grows with max_pages_per_seq, stays within
-// kStepMaxLds).
-constexpr size_t kStepMaxLds = 64 * 1024;
-size_t step_lds_bytes(const Dims& d);
-bool step_fits(const Dims& d);
-// Workgroups per row of the one-workgroup step.
-int step_splits(const Dims& d, int k_max);
-// Polls a split of a row makes while it waits for the row's other splits'
-// page keys; set_exchange_polls returns the previous value.
-int exchange_polls();
-int set_exchange_polls(int polls);
-hipError_t launch_step(const Dims& d, const float* q, const void* k_new, const void* v_new,
-                       void* k_pool, void* v_pool, void* meta, const int32_t* bt,
-                       const int32_t* seq_lens, int k_max, const int32_t* k_per_seq,
-                       const SelectPolicy& pol, float scale, int32_t* sel,
-                       int32_t* sel_count, float* scores_out, const Workspace& ws,
-                       float* out, hipStream_t s);
+                         const void* v_pool, const int32_t* bt, const int32_t* seq_lens,
+                         const int32_t* sel, const int32_t* sel_phys,
+                         const int32_t* sel_count, int k_max, float scale,
+                         const Workspace& ws, float* out, hipStream_t s);
+// The whole step of one (sequence, KV head) in one workgroup (or in plan.S
+// workgroups that share the row's scoring, each select the whole row and
+// decode a share of it; the last one to finish merges the shares): [append]
+// -> score -> top-K -> decode, one launch.  Usable when step_fits(d).
+hipError_t launch_step(const Dims& d, int polls, const float* q, const void* k_new,
+                       const void* v_new, void* k_pool, void* v_pool, void* meta,
+                       const int32_t* bt, const int32_t* seq_lens, int k_max,
+                       const int32_t* k_per_seq, const SelectPolicy& pol, float scale,
+                       int32_t* sel, int32_t* sel_count, float* scores_out,
+                       const Workspace& ws, float* out, hipStream_t s);
 
 }  // namespace tsv

@@ -46,14 +46,16 @@ def oracle_run(wl, k_max=None, k_per_seq="wl", n_sink=None, step=0, n_recent=0, 
 
 
 def gpu_run(wl, k_max=None, k_per_seq="wl", n_sink=None, step=0, separate=False, n_recent=0,
-            group_agg=0, ws=None):
+            group_agg=0, ws=None, lib=None):
     """HIP results of the same step; `separate` uses the three-call path.  With
     selection options the _ex entry points are called, else the plain ones.
     `ws`: a workspace to use (default: a new zero-filled one); the result's
-    "sync" holds its counter prefix after the call."""
+    "sync" holds its counter prefix after the call.  `lib`: the library to call
+    (default: the package's libtsv.so; the testing library for hooks)."""
     import torch
 
-    import query_aware_sparse_bbox_amd as T
+    import query_aware_sparse_bbox_amd as T_mod
+    T = lib if lib is not None else T_mod
     from workloads import device as WD
 
     sh = wl.shape

@@ -12,6 +12,7 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "tsv.h")
+TEST_HEADER = os.path.join(ROOT, "include", "tsv_testing.h")
 
 
 @pytest.fixture(scope="module")
@@ -27,9 +28,15 @@ def tsv():
     return m
 
 
-def declared_functions():
-    text = open(HEADER).read()
+def declared_functions(header=HEADER):
+    text = open(header).read()
     return sorted(set(re.findall(r"^\s*(?:int|size_t|const char\*)\s+(tsv_\w+)\s*\(", text, re.M)))
+
+
+def exported(path):
+    out = subprocess.run(["nm", "-D", "--defined-only", path], capture_output=True,
+                         text=True, check=True).stdout
+    return set(re.findall(r" T (tsv_\w+)$", out, re.M))
 
 
 def test_header_declares_the_boundary():
@@ -41,18 +48,26 @@ def test_header_declares_the_boundary():
 
 
 def test_library_exports_every_declared_symbol(tsv):
-    out = subprocess.run(["nm", "-D", "--defined-only", tsv.LIB_PATH], capture_output=True,
-                         text=True, check=True).stdout
-    exported = set(re.findall(r" T (tsv_\w+)$", out, re.M))
+    ex = exported(tsv.LIB_PATH)
     for n in declared_functions():
-        assert n in exported, n
+        assert n in ex, n
         assert getattr(tsv._lib, n)
     assert set(tsv.EXPORTS) == set(declared_functions())
+    # the library proper keeps no state: the testing hook is not in it
+    assert not ex & set(declared_functions(TEST_HEADER))
 
 
-def test_library_is_built_for_gfx950(tsv):
+def test_testing_library_exports_both_headers(tsv):
+    ex = exported(tsv.TESTHOOKS_PATH)
+    for n in declared_functions() + declared_functions(TEST_HEADER):
+        assert n in ex, n
+    assert set(tsv.TEST_EXPORTS) == set(declared_functions(TEST_HEADER))
+
+
+@pytest.mark.parametrize("which", ["LIB_PATH", "TESTHOOKS_PATH"])
+def test_library_is_built_for_gfx950(tsv, which):
     """The embedded device code targets gfx950 and nothing else."""
-    data = open(tsv.LIB_PATH, "rb").read()
+    data = open(getattr(tsv, which), "rb").read()
     targets = set(re.findall(rb"amdgcn-amd-amdhsa-+(gfx\w+)", data))
     assert targets == {b"gfx950"}
 
@@ -98,13 +113,16 @@ def test_workspace_zeroed_prefix(tsv):
 
 
 def test_exchange_polls_hook_round_trip(tsv):
-    """The testing hook only stores a number on the host (no HIP call)."""
-    cur = tsv.tsv_debug_exchange_polls(-1)
+    """The testing library's hook only stores a number on the host (no HIP
+    call); the library proper has no such state."""
+    t = tsv.testing_library()
+    cur = t.tsv_debug_exchange_polls(-1)
     assert cur == 16384
-    assert tsv.tsv_debug_exchange_polls(0) == cur
-    assert tsv.tsv_debug_exchange_polls(-1) == 0
-    assert tsv.tsv_debug_exchange_polls(cur) == 0
-    assert tsv.tsv_debug_exchange_polls(-1) == cur
+    assert t.tsv_debug_exchange_polls(0) == cur
+    assert t.tsv_debug_exchange_polls(-1) == 0
+    assert t.tsv_debug_exchange_polls(cur) == 0
+    assert t.tsv_debug_exchange_polls(-1) == cur
+    assert not hasattr(tsv._lib, "tsv_debug_exchange_polls")
 
 
 def test_decode_step_launch_plan(tsv):
@@ -187,3 +205,15 @@ def test_bad_selection_options_rejected_before_any_hip_call(tsv, n_sink, n_recen
                                  need, None) == status
     assert L.tsv_decode_step_ex(ctypes.byref(s), f, None, None, f, f, f, f, f, 4, None, n_sink,
                                 o, ctypes.c_float(0.1), f, f, None, f, f, need, None) == status
+
+
+def test_one_hip_runtime_whatever_the_import_order():
+    """Imported before torch, the package still binds the library to torch's
+    HIP runtime: a process must not hold two HIP runtimes (the library's
+    launches would then not see torch's memory)."""
+    code = ("import query_aware_sparse_bbox_amd, torch\n"
+            "print(sorted({l.split()[-1] for l in open('/proc/self/maps') if 'libamdhip64' in l}))")
+    out = subprocess.run(["python3", "-c", code], capture_output=True, text=True, check=True,
+                         cwd=ROOT, timeout=300).stdout.strip().splitlines()[-1]
+    libs = eval(out)
+    assert len(libs) == 1, libs

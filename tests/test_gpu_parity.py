@@ -147,6 +147,19 @@ def test_all_pages_is_dense_attention():
     _case(wl, k_max=wl.shape.max_pages_per_seq, k_per_seq=None)
 
 
+def test_scores_with_wide_single_wave_selection():
+    """Rows of at most 512 pages select in one wave, which overwrites the page
+    keys in local memory with page indices; with more than 64 pages kept the
+    exported scores must still be the page scores (300-page rows, budget
+    128), on the one-launch step and the three-call path."""
+    wl = W.make("tinyllama", batch=2, context=300 * 16 - 5)
+    assert wl.shape.max_pages_per_seq >= 300
+    g, o = _case(wl, k_max=128, k_per_seq=None)
+    assert o["cnt"].min() == 128
+    g = gpu_run(wl, k_max=128, k_per_seq=None, separate=True)
+    compare(wl, g, o)
+
+
 def test_three_calls_equal_fused_step():
     """tsv_meta_append + tsv_select_pages + tsv_sparse_decode give the same
     selection, boxes and pools as tsv_decode_step; both outputs are within
@@ -421,23 +434,25 @@ def test_ragged_appends_seventeen_steps(kw):
 
 def test_split_rows_exchange_fallback_bit_identical():
     """Rows spread over several workgroups share their page scoring through the
-    workspace.  With the wait cut to zero polls, every split but the last to
-    arrive scores the rest of its row itself: scores, selections and outputs
-    are the same bits, and the counters are left at zero either way."""
+    workspace.  With the wait cut to zero polls (testing library), every split
+    but the last to arrive scores the rest of its row itself: scores,
+    selections and outputs are the same bits, and the counters are left at
+    zero either way."""
     import query_aware_sparse_bbox_amd as T
 
+    t = T.testing_library()
     wl = W.make("tinyllama", batch=4, context=4096)
     assert T.tsv_decode_step_launches(wl.shape, wl.k_max, False) == 1
     o = oracle_run(wl)
     a = gpu_run(wl)
     compare(wl, a, o)
-    prev = T.tsv_debug_exchange_polls(0)
+    prev = t.tsv_debug_exchange_polls(0)
     try:
-        b = gpu_run(wl)
+        b = gpu_run(wl, lib=t)
         wl8 = W.make("tinyllama", batch=2, context=4096, kv_dtype=W.F8)
-        compare(wl8, gpu_run(wl8), oracle_run(wl8))
+        compare(wl8, gpu_run(wl8, lib=t), oracle_run(wl8))
     finally:
-        T.tsv_debug_exchange_polls(prev)
+        t.tsv_debug_exchange_polls(prev)
     for k in ("sel", "cnt"):
         assert np.array_equal(a[k], b[k]), k
     for k in ("scores", "out"):
