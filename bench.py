@@ -61,7 +61,7 @@ DESCR = {
 }
 KERNEL_SOURCES = [os.path.join(ROOT, "query_aware_sparse_bbox_amd", "csrc", f)
                   for f in ("tsv_device.h", "tsv_kernels.hip", "tsv_host.hip", "tsv_api.hip",
-                            "tsv_launch.h")]
+                            "tsv_launch.h", "tsv_scratch.hip")]
 
 # HBM bytes per step (all its kernels) from `rocprofv3 --pmc FETCH_SIZE` and
 # `--pmc WRITE_SIZE` runs of this script, each divided by the same counter's

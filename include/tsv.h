@@ -253,6 +253,31 @@ int tsv_decode_step_ex(const tsv_shape* shape, const float* q, const void* k_new
                        int32_t* sel_count, float* scores_out, float* out,
                        void* workspace, size_t workspace_bytes, void* stream);
 
+/* tsv_decode_step_ex for callers that cannot allocate device memory: code
+   under HIP graph capture that may not call hipMalloc, tight serving loops,
+   harnesses that forbid allocation.  There is no workspace argument: the
+   step's scratch (split-row counters, page-score keys, partial softmax
+   states) lives in a device array owned by the library,
+   TSV_NOALLOC_SCRATCH_BYTES on each GPU, which exists from the loading of the
+   library's device code on that GPU until the process ends.  The call
+   allocates nothing (no hipMalloc, no allocating library routine).  The
+   first call on a GPU also enqueues one small kernel on `stream` that clears
+   the array's counter prefix; every call leaves that prefix zero.  All calls
+   on one GPU share its array: calls that may run at the same time on one GPU
+   (different streams, or a graph replay overlapping another call) race on it
+   and must not be made.  TSV_ERR_UNSUPPORTED when tsv_workspace_bytes(shape,
+   k_max) exceeds TSV_NOALLOC_SCRATCH_BYTES; TSV_ERR_HIP when the array's
+   device address cannot be obtained; otherwise arguments, results and errors
+   as for tsv_decode_step_ex. */
+#define TSV_NOALLOC_SCRATCH_BYTES 33554432
+int tsv_decode_step_noalloc(const tsv_shape* shape, const float* q, const void* k_new,
+                            const void* v_new, void* k_pool, void* v_pool, void* meta,
+                            const int32_t* block_table, const int32_t* seq_lens,
+                            int32_t k_max, const int32_t* k_per_seq, int32_t n_sink,
+                            const tsv_select_opts* opts, float scale, int32_t* sel,
+                            int32_t* sel_count, float* scores_out, float* out,
+                            void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -35,7 +35,7 @@ TSV_AGG_MAX, TSV_AGG_SUM = 0, 1
 EXPORTS = ("tsv_version", "tsv_status_string", "tsv_meta_bytes", "tsv_workspace_bytes",
            "tsv_decode_step_launches", "tsv_meta_build", "tsv_meta_append",
            "tsv_select_pages", "tsv_sparse_decode", "tsv_decode_step",
-           "tsv_select_pages_ex", "tsv_decode_step_ex")
+           "tsv_select_pages_ex", "tsv_decode_step_ex", "tsv_decode_step_noalloc")
 # declared in include/tsv_testing.h, exported by the testing library only
 TEST_EXPORTS = ("tsv_debug_exchange_polls",)
 
@@ -84,6 +84,8 @@ _SIGS = {
                             ctypes.c_int),
     "tsv_decode_step_ex": ([_SP, _P, _P, _P, _P, _P, _P, _P, _P, _I, _P, _I, _OP, _F, _P, _P,
                             _P, _P, _P, _Z, _P], ctypes.c_int),
+    "tsv_decode_step_noalloc": ([_SP, _P, _P, _P, _P, _P, _P, _P, _P, _I, _P, _I, _OP, _F, _P,
+                                 _P, _P, _P, _P], ctypes.c_int),
 }
 _TEST_SIGS = {"tsv_debug_exchange_polls": ([_I], ctypes.c_int)}
 
@@ -220,6 +222,15 @@ class Library:
                    _ptr(scores_out), _ptr(out), _ptr(workspace), _nbytes(workspace),
                    _stream(stream))
 
+    def tsv_decode_step_noalloc(self, shape, q, k_new, v_new, k_pool, v_pool, meta,
+                                block_table, seq_lens, k_max, k_per_seq, n_sink, n_recent,
+                                group_agg, scale, sel, sel_count, scores_out, out, stream=None):
+        self._call("tsv_decode_step_noalloc", ctypes.byref(Shape.of(shape)), _ptr(q),
+                   _ptr(k_new), _ptr(v_new), _ptr(k_pool), _ptr(v_pool), _ptr(meta),
+                   _ptr(block_table), _ptr(seq_lens), int(k_max), _ptr(k_per_seq), int(n_sink),
+                   _opts(n_recent, group_agg), float(scale), _ptr(sel), _ptr(sel_count),
+                   _ptr(scores_out), _ptr(out), _stream(stream))
+
 
 # the library proper; the module-level functions are its methods
 _default = Library(LIB_PATH)
@@ -250,3 +261,4 @@ tsv_sparse_decode = _default.tsv_sparse_decode
 tsv_decode_step = _default.tsv_decode_step
 tsv_select_pages_ex = _default.tsv_select_pages_ex
 tsv_decode_step_ex = _default.tsv_decode_step_ex
+tsv_decode_step_noalloc = _default.tsv_decode_step_noalloc

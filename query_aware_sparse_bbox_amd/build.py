@@ -58,6 +58,7 @@ def units(extra=()):
         for pname, p in PARTS.items():
             cc("tsv_kernels.hip", f"kernels_{tname}_{pname}", [f"-DTSV_DT={t}", f"-DTSV_PART={p}"])
     cc("tsv_host.hip", "host")
+    cc("tsv_scratch.hip", "scratch")
     cc("tsv_api.hip", "api")
     cc("tsv_api.hip", "api_testhooks", ["-DTSV_TEST_HOOKS"])
     return out
@@ -80,7 +81,7 @@ def build(extra_flags=(), verbose=False, jobs=None):
     for lib, api in ((LIB, "api"), (LIB_TESTHOOKS, "api_testhooks")):
         tmp = lib + ".tmp"
         run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, objs[api],
-             objs["host"], *kernels])
+             objs["host"], objs["scratch"], *kernels])
         os.replace(tmp, lib)
     return LIB
 

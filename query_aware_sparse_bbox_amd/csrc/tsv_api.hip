@@ -16,6 +16,7 @@
 #endif
 
 static_assert(tsv::kSyncBytes == TSV_WORKSPACE_ZERO_BYTES, "zeroed workspace prefix");
+static_assert(tsv::kNoAllocScratchBytes == TSV_NOALLOC_SCRATCH_BYTES, "no-allocation scratch");
 
 namespace {
 
@@ -300,6 +301,28 @@ int tsv_decode_step_ex(const tsv_shape* shape, const float* q, const void* k_new
   return run_step(d, pol, q, k_new, v_new, k_pool, v_pool, meta, block_table, seq_lens, k_max,
                   k_per_seq, scale, sel, sel_count, scores_out, out, workspace,
                   (hipStream_t)stream);
+}
+
+int tsv_decode_step_noalloc(const tsv_shape* shape, const float* q, const void* k_new,
+                            const void* v_new, void* k_pool, void* v_pool, void* meta,
+                            const int32_t* block_table, const int32_t* seq_lens,
+                            int32_t k_max, const int32_t* k_per_seq, int32_t n_sink,
+                            const tsv_select_opts* opts, float scale, int32_t* sel,
+                            int32_t* sel_count, float* scores_out, float* out,
+                            void* stream) {
+  Dims d;
+  tsv::SelectPolicy pol;
+  int rc = check_step(shape, q, k_new, v_new, k_pool, v_pool, meta, block_table, seq_lens,
+                      k_max, n_sink, opts, sel, sel_count, out, &d, &pol);
+  if (rc) return rc;
+  if (tsv::workspace_layout(d, k_max, nullptr, nullptr) > tsv::kNoAllocScratchBytes)
+    return TSV_ERR_UNSUPPORTED;
+  hipStream_t s = (hipStream_t)stream;
+  void* scratch = nullptr;
+  rc = hip_status(tsv::noalloc_scratch(s, &scratch));
+  if (rc) return rc;
+  return run_step(d, pol, q, k_new, v_new, k_pool, v_pool, meta, block_table, seq_lens, k_max,
+                  k_per_seq, scale, sel, sel_count, scores_out, out, scratch, s);
 }
 
 int tsv_decode_step(const tsv_shape* shape, const float* q, const void* k_new,

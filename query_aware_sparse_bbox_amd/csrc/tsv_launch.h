@@ -69,6 +69,13 @@ struct Workspace {
 // Total workspace bytes; with `base` non-null also fills `ws`.
 size_t workspace_layout(const Dims& d, int k_max, void* base, Workspace* ws);
 
+// Scratch of tsv_decode_step_noalloc: a library-owned device array of this
+// many bytes per GPU (tsv_scratch.hip).  noalloc_scratch returns its device
+// address on the current device; the first call on a device also enqueues,
+// on stream s, the clearing of its split-row counter prefix.
+constexpr size_t kNoAllocScratchBytes = (size_t)32 << 20;
+hipError_t noalloc_scratch(hipStream_t s, void** out);
+
 // Phased decode: S_max split slots per row, TPW tiles per split.
 struct DecodePlan {
   int S_max, TPW, tile_tokens;

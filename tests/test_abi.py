@@ -207,6 +207,26 @@ def test_bad_selection_options_rejected_before_any_hip_call(tsv, n_sink, n_recen
                                 o, ctypes.c_float(0.1), f, f, None, f, f, need, None) == status
 
 
+def test_noalloc_rejects_shapes_beyond_its_scratch_before_any_hip_call(tsv):
+    """The no-allocation step checks its arguments, then that the shape's
+    scratch fits the library-owned array, before any HIP call."""
+    f = ctypes.c_void_p(1 << 20)
+    L = tsv._lib
+    big = shape(batch=512, num_q_heads=8, num_kv_heads=8, max_pages_per_seq=4096,
+                num_phys_pages=1 << 20)
+    assert L.tsv_workspace_bytes(ctypes.byref(big), 64) > 33554432
+    assert L.tsv_decode_step_noalloc(ctypes.byref(big), f, None, None, f, f, f, f, f, 64, None,
+                                     0, None, ctypes.c_float(0.1), f, f, None, f, None) == -2
+    s = shape()
+    # the same argument checks as the workspace entry point
+    assert L.tsv_decode_step_noalloc(ctypes.byref(s), None, None, None, f, f, f, f, f, 4, None,
+                                     0, None, ctypes.c_float(0.1), f, f, None, f, None) == -1
+    assert L.tsv_decode_step_noalloc(ctypes.byref(s), f, f, None, f, f, f, f, f, 4, None,
+                                     0, None, ctypes.c_float(0.1), f, f, None, f, None) == -1
+    assert L.tsv_decode_step_noalloc(ctypes.byref(s), f, None, None, f, f, f, f, f, 0, None,
+                                     0, None, ctypes.c_float(0.1), f, f, None, f, None) == -1
+
+
 def test_one_hip_runtime_whatever_the_import_order():
     """Imported before torch, the package still binds the library to torch's
     HIP runtime: a process must not hold two HIP runtimes (the library's
