@@ -41,7 +41,7 @@ def flags(extra=()):
     return [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
             "-ffp-contract=off", "-fno-gpu-flush-denormals-to-zero",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-            "-Wall", "-Wno-unused-function", "-Wno-pass-failed", "-I", os.path.join(ROOT, "include"), *extra]
+            "-Wall", "-Wno-unused-function", "-I", os.path.join(ROOT, "include"), *extra]
 
 
 def units(extra=()):

@@ -404,54 +404,51 @@ struct SelectLds {
 // among pages [f, n - r), equal keys lowest page first.
 //
 // Thread t owns the m = ceil(n/NT) consecutive pages [t*m, t*m + m) and keeps
-// their keys in registers.  The threshold is found most-significant digit
-// first: the bits every candidate shares are fixed at once (block AND / OR),
-// then 8-bit digits are resolved with an LDS histogram (a wave's most common
-// digit is added once) until the boundary bucket is taken whole or no bits
-// are left.  One block-wide scan of packed (kept-above, equal-to-threshold)
-// counts then gives every thread its output slots, so the pages come out in
-// ascending order without sorting.
+// their keys in registers (M >= m slots: every loop over them has a
+// compile-time trip count, so the arrays stay in registers without indexed
+// access).  The threshold is found most-significant digit first: the bits
+// every candidate shares are fixed at once (block AND / OR), then 8-bit
+// digits are counted in an LDS histogram (double-buffered: the waves that do
+// not scan it clear the next pass's) until the boundary bucket is taken
+// whole or no bits are left.  One block-wide scan of packed (kept-above,
+// equal-to-threshold) counts then gives every thread its output slots, so
+// the pages come out in ascending order without sorting.
 //
 // Leaves the kept pages, ascending, in LDS: s_key[0..cnt) logical pages,
 // s_phys[0..cnt) physical pages, and returns cnt.  With srow non-null also
 // writes the logical pages to srow (-1 padded to k_max), the physical pages
 // to prow (if non-null) and the count to *count.  Ends with a barrier.
-template <int NT>
-__device__ __forceinline__ int select_block(uint32_t* s_key, uint32_t* s_phys, int n,
-                                            int keff, int f, int r, int k_max,
-                                            int32_t* __restrict__ srow,
-                                            int32_t* __restrict__ prow,
-                                            int32_t* __restrict__ count, SelectLds<NT>& sl) {
-  constexpr int NW = NT / kWave, MAXM = kMaxPagesPerSeq / NT;
+template <int NT, int M>
+__device__ __forceinline__ int select_block_m(uint32_t* s_key, uint32_t* s_phys, int n,
+                                              int keff, int f, int r, int k_max,
+                                              int32_t* __restrict__ srow,
+                                              int32_t* __restrict__ prow,
+                                              int32_t* __restrict__ count, SelectLds<NT>& sl) {
+  constexpr int NW = NT / kWave;
   static_assert(NT >= 256, "one histogram bin per thread is cleared");
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
-  const int m = (n + NT - 1) / NT;
+  const int m = (n + NT - 1) / NT;  // <= M
   const int p0 = tid * m, nl = max(n - 1, 0);
   const int R = keff - f - r, ncand = n - f - r, pr = n - r;  // candidates [f, pr)
   const bool take_all = R >= ncand, radix = R > 0 && R < ncand;
-  uint32_t kk[MAXM], ph[MAXM];
+  uint32_t kk[M], ph[M];
+  bool cand[M], valid[M];
 #pragma unroll
-  for (int i = 0; i < MAXM; ++i) {
-    if (i >= m) break;
-    const int pc = min(p0 + i, nl);
+  for (int i = 0; i < M; ++i) {
+    const int p = p0 + i, pc = min(p, nl);
     kk[i] = s_key[pc];
     ph[i] = s_phys[pc];
+    valid[i] = i < m && p < n;
+    cand[i] = valid[i] && p >= f && p < pr;
   }
-  auto is_cand = [&](int i) {
-    const int p = p0 + i;
-    return i < m && p < pr && p >= f;
-  };
   uint32_t tmask = 0, tau = 0;  // (key & tmask) > tau: kept; == tau: the first `need`
   int need = 0;
   if (radix) {
     uint32_t a = ~0u, o = 0u;
 #pragma unroll
-    for (int i = 0; i < MAXM; ++i) {
-      if (i >= m) break;  // m is uniform
-      if (is_cand(i)) {
-        a &= kk[i];
-        o |= kk[i];
-      }
+    for (int i = 0; i < M; ++i) {
+      a &= cand[i] ? kk[i] : ~0u;
+      o |= cand[i] ? kk[i] : 0u;
     }
     a = wave_reduce(a, [](uint32_t u, uint32_t v) { return u & v; });
     o = wave_reduce(o, [](uint32_t u, uint32_t v) { return u | v; });
@@ -459,6 +456,7 @@ __device__ __forceinline__ int select_block(uint32_t* s_key, uint32_t* s_phys, i
       atomicAnd(reinterpret_cast<unsigned*>(&sl.red[0]), a);
       atomicOr(reinterpret_cast<unsigned*>(&sl.red[1]), o);
     }
+    if (tid < 256) sl.hist[0][tid] = 0;
     __syncthreads();
     a = (uint32_t)sl.red[0];
     o = (uint32_t)sl.red[1];
@@ -470,27 +468,14 @@ __device__ __forceinline__ int select_block(uint32_t* s_key, uint32_t* s_phys, i
       int top = 31 - __clz(a ^ o);
       tmask = top == 31 ? 0u : ~((2u << top) - 1u);
       tau = a & tmask;
-      if (tid < 256) sl.hist[0][tid] = 0;
-      __syncthreads();
       for (int pass = 0;; ++pass) {
         const int width = min(8, top + 1), shift = top + 1 - width;
         const uint32_t dmask = (1u << width) - 1u;
         const int nb = 1 << width;
         int* hist = sl.hist[pass & 1];
 #pragma unroll
-        for (int i = 0; i < MAXM; ++i) {
-          if (i >= m) break;
-          const bool in = is_cand(i) && (kk[i] & tmask) == tau;
-          const int d = in ? (int)((kk[i] >> shift) & dmask) : -1;
-          const unsigned long long act = __ballot(in);
-          if (act) {
-            const int src = __ffsll(act) - 1;
-            const int dl = __builtin_amdgcn_readlane(d, src);
-            const unsigned long long same = __ballot(d == dl);
-            if (lane == src) atomicAdd(&hist[dl], (int)__popcll(same));
-            else if (in && d != dl) atomicAdd(&hist[d], 1);
-          }
-        }
+        for (int i = 0; i < M; ++i)
+          if (cand[i] && (kk[i] & tmask) == tau) atomicAdd(&hist[(kk[i] >> shift) & dmask], 1);
         __syncthreads();
         if (wave == 0) {
           int c[4], sum = 0;
@@ -525,33 +510,22 @@ __device__ __forceinline__ int select_block(uint32_t* s_key, uint32_t* s_phys, i
     }
     need = remaining;
   }
-  auto flags = [&](int i, bool& keep, bool& eq) {
-    const int p = p0 + i;
-    const bool valid = i < m && p < n;
-    const bool cand = valid && p >= f && p < pr;
-    const uint32_t km = kk[i] & tmask;
-    eq = radix && cand && km == tau;
-    keep = (valid && (p < f || p >= pr)) || (cand && (take_all || (radix && km > tau)));
-  };
   int nkeep = 0, neq = 0;
 #pragma unroll
-  for (int i = 0; i < MAXM; ++i) {
-    if (i >= m) break;
-    bool keep, eq;
-    flags(i, keep, eq);
-    nkeep += keep;
-    neq += eq;
+  for (int i = 0; i < M; ++i) {
+    const uint32_t km = kk[i] & tmask;
+    nkeep += (valid[i] && !cand[i]) || (cand[i] && (take_all || (radix && km > tau)));
+    neq += radix && cand[i] && km == tau;
   }
   int tot;
   const int ex = block_excl_scan<NW>((neq << 16) | nkeep, sl.scan, &tot);
   int eqi = ex >> 16;
   int pos = (ex & 0xffff) + min(eqi, need);
 #pragma unroll
-  for (int i = 0; i < MAXM; ++i) {
-    if (i >= m) break;
-    bool keep, eq;
-    flags(i, keep, eq);
-    if (eq) keep = eqi++ < need;
+  for (int i = 0; i < M; ++i) {
+    const uint32_t km = kk[i] & tmask;
+    bool keep = (valid[i] && !cand[i]) || (cand[i] && (take_all || (radix && km > tau)));
+    if (radix && cand[i] && km == tau) keep = eqi++ < need;
     if (keep) {
       if (pos < k_max) {  // never false: the count is at most min(K_b, n_b)
         if (srow) srow[pos] = p0 + i;
@@ -574,56 +548,64 @@ __device__ __forceinline__ int select_block(uint32_t* s_key, uint32_t* s_phys, i
   return total;
 }
 
+// select_block_m for the row's m = ceil(n / NT) pages per thread, rounded up
+// to a power of two (a uniform branch).  s_red[0] / s_red[1] must hold
+// all-ones / zero, written before a barrier that precedes the call.
+template <int NT>
+__device__ __forceinline__ int select_block(uint32_t* s_key, uint32_t* s_phys, int n, int keff,
+                                            int f, int r, int k_max, int32_t* __restrict__ srow,
+                                            int32_t* __restrict__ prow,
+                                            int32_t* __restrict__ count, SelectLds<NT>& sl) {
+  constexpr int MAXM = kMaxPagesPerSeq / NT;
+  const int m = (n + NT - 1) / NT;
+  if (m <= 1)
+    return select_block_m<NT, 1>(s_key, s_phys, n, keff, f, r, k_max, srow, prow, count, sl);
+  if (m <= 2)
+    return select_block_m<NT, 2>(s_key, s_phys, n, keff, f, r, k_max, srow, prow, count, sl);
+  if constexpr (MAXM > 4) {
+    if (m <= 4)
+      return select_block_m<NT, 4>(s_key, s_phys, n, keff, f, r, k_max, srow, prow, count, sl);
+  }
+  if constexpr (MAXM > 8) {
+    if (m <= 8)
+      return select_block_m<NT, 8>(s_key, s_phys, n, keff, f, r, k_max, srow, prow, count, sl);
+  }
+  return select_block_m<NT, MAXM>(s_key, s_phys, n, keff, f, r, k_max, srow, prow, count, sl);
+}
 
-// Top-K of one row by wave 0 of the workgroup, with the same result as
-// select_block: pages [0, f) and [n - r, n) always kept, the other
-// R = keff - f - r slots to the largest order keys among pages [f, n - r),
-// equal keys lowest page first; the kept pages left ascending in s_key /
-// s_phys [0, cnt).  Lane l holds pages l, l + 64, ... (round i: page
-// 64 i + l) in registers, so no barrier is needed until the end: the shared
-// high bits of the candidates are fixed by a wave AND / OR, then 8-bit digits
-// are counted in an LDS histogram (LDS operations of one wave complete in
-// order) until the boundary bucket is taken whole or no bits are left.  The
-// output position of a kept page is the number of kept pages before it: the
-// total of earlier rounds plus the kept lanes below it in this round (a
-// ballot), so the pages come out ascending without a sort.  All threads
-// return the count; ends with a barrier.
+// Rows of at most this many pages are selected by one wave (select_wave),
+// one page per lane: faster than the workgroup's digit search only there.
+constexpr int kWaveSelectPages = kWave;
+
+// Top-K of one row of at most 64 pages by wave 0 of the workgroup, with the
+// same result as select_block: pages [0, f) and [n - r, n) always kept, the
+// other R = keff - f - r slots to the largest order keys among pages
+// [f, n - r), equal keys lowest page first; the kept pages left ascending in
+// s_key / s_phys [0, cnt).  Lane l holds page l in registers, so no barrier
+// is needed until the end: the shared high bits of the candidates are fixed
+// by a wave AND / OR, then 8-bit digits are counted in an LDS histogram (LDS
+// operations of one wave complete in order) until the boundary bucket is
+// taken whole or no bits are left.  The output position of a kept page is
+// the number of kept lanes below it (a ballot), so the pages come out
+// ascending without a sort.  All threads return the count; ends with a
+// barrier.
 template <int NT>
 __device__ __forceinline__ int select_wave(uint32_t* s_key, uint32_t* s_phys, int n, int keff,
                                            int f, int r, int k_max, SelectLds<NT>& sl) {
-  constexpr int MAXR = kWaveSelectMaxPages / kWave;
   const int lane = threadIdx.x & (kWave - 1);
   if (threadIdx.x < kWave) {
     const int R = keff - f - r, pr = n - r, ncand = pr - f;
     const bool take_all = R >= ncand, radix = R > 0 && R < ncand;
-    const int rounds = (n + kWave - 1) / kWave;
     int* hist = sl.hist[0];
-    uint32_t kk[MAXR], ph[MAXR];
-#pragma unroll
-    for (int i = 0; i < MAXR; ++i) {
-      if (i >= rounds) break;  // uniform
-      const int p = min(i * kWave + lane, max(n - 1, 0));
-      kk[i] = s_key[p];
-      ph[i] = s_phys[p];
-    }
-    auto is_cand = [&](int i) {
-      const int p = i * kWave + lane;
-      return p >= f && p < pr;
-    };
+    const int p = lane, pc = min(p, max(n - 1, 0));
+    const uint32_t kk = s_key[pc], ph = s_phys[pc];
+    const bool valid = p < n, cand = valid && p >= f && p < pr;
     uint32_t tmask = 0, tau = 0;  // (key & tmask) > tau: kept; == tau: the first `need`
     int need = 0;
     if (radix) {
-      uint32_t a = ~0u, o = 0u;
-#pragma unroll
-      for (int i = 0; i < MAXR; ++i) {
-        if (i >= rounds) break;
-        if (is_cand(i)) {
-          a &= kk[i];
-          o |= kk[i];
-        }
-      }
-      a = wave_reduce(a, [](uint32_t u, uint32_t v) { return u & v; });
-      o = wave_reduce(o, [](uint32_t u, uint32_t v) { return u | v; });
+      const uint32_t a =
+          wave_reduce(cand ? kk : ~0u, [](uint32_t u, uint32_t v) { return u & v; });
+      const uint32_t o = wave_reduce(cand ? kk : 0u, [](uint32_t u, uint32_t v) { return u | v; });
       int remaining = R;
       if (a == o) {  // every candidate has the same key: lowest pages win
         tmask = ~0u;
@@ -637,11 +619,7 @@ __device__ __forceinline__ int select_wave(uint32_t* s_key, uint32_t* s_phys, in
           const uint32_t dmask = (1u << width) - 1u;
           const int nb = 1 << width;
           reinterpret_cast<int4*>(hist)[lane] = int4{0, 0, 0, 0};  // 256 bins
-#pragma unroll
-          for (int i = 0; i < MAXR; ++i) {
-            if (i >= rounds) break;
-            if (is_cand(i) && (kk[i] & tmask) == tau) atomicAdd(&hist[(kk[i] >> shift) & dmask], 1);
-          }
+          if (cand && (kk & tmask) == tau) atomicAdd(&hist[(kk >> shift) & dmask], 1);
           __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
           int c[4], sum = 0;
 #pragma unroll
@@ -675,27 +653,17 @@ __device__ __forceinline__ int select_wave(uint32_t* s_key, uint32_t* s_phys, in
       need = remaining;
     }
     const unsigned long long below = (1ull << lane) - 1ull;
-    int base = 0, eqseen = 0;
-#pragma unroll
-    for (int i = 0; i < MAXR; ++i) {
-      if (i >= rounds) break;
-      const int p = i * kWave + lane;
-      const bool valid = p < n, cand = valid && is_cand(i);
-      const uint32_t km = kk[i] & tmask;
-      const bool eq = radix && cand && km == tau;
-      bool keep = (valid && (p < f || p >= pr)) || (cand && (take_all || (radix && km > tau)));
-      const unsigned long long beq = __ballot(eq);
-      if (eq) keep = eqseen + __popcll(beq & below) < need;
-      eqseen += __popcll(beq);
-      const unsigned long long bk = __ballot(keep);
-      const int pos = base + __popcll(bk & below);
-      base += __popcll(bk);
-      if (keep && pos < k_max) {  // pos < k_max always: at most min(K_b, n_b) are kept
-        s_key[pos] = (uint32_t)p;
-        s_phys[pos] = ph[i];
-      }
+    const uint32_t km = kk & tmask;
+    const bool eq = radix && cand && km == tau;
+    bool keep = (valid && !cand) || (cand && (take_all || (radix && km > tau)));
+    if (eq) keep = __popcll(__ballot(eq) & below) < need;
+    const unsigned long long bk = __ballot(keep);
+    const int pos = __popcll(bk & below);
+    if (keep && pos < k_max) {  // pos < k_max always: at most min(K_b, n_b) are kept
+      s_key[pos] = (uint32_t)p;
+      s_phys[pos] = ph;
     }
-    if (lane == 0) sl.red[5] = min(base, k_max);
+    if (lane == 0) sl.red[5] = min(__popcll(bk), k_max);
   }
   __syncthreads();
   return sl.red[5];
@@ -1898,7 +1866,7 @@ __global__ __launch_bounds__(NT, (step_min_blocks<DT, D, G, NT>())) void k_step(
   // the selection stays in LDS; it is written out at the end, so that no
   // barrier before the decode waits for those stores
   const int cnt =
-      n <= kWaveSelectMaxPages
+      n <= kWaveSelectPages
           ? select_wave<NT>(s_key, s_phys, n, keff, f, r, k_max, sl)
           : select_block<NT>(s_key, s_phys, n, keff, f, r, k_max, nullptr, nullptr, nullptr, sl);
   int32_t* srow = sel + (size_t)unit * k_max;

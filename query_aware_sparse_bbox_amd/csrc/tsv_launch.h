@@ -40,8 +40,6 @@ constexpr int kDecodeThreads = 256;
 constexpr int kStepMaxSplits = 8;
 // A split of a row covers at least this many 16-token steps per wave.
 constexpr int kStepMinSpanSteps = 2;
-// Rows of at most this many pages are selected by one wave.
-constexpr int kWaveSelectMaxPages = 512;
 
 // Tokens of the selected-token stream one decode workgroup covers.
 int decode_tile_tokens(const Dims& d);
