@@ -96,7 +96,7 @@ enum {
      n_sink outside [0, k_max], misaligned pointer, workspace too small or
      not 256-byte aligned */
   TSV_ERR_INVALID_ARG = -1,
-  /* head_dim not 64/128, page_size not 8/16/32/64, G not 1/2/4/8,
+  /* head_dim not 64/128, page_size not 8/16/32/64, G not 1/2/4/8/16,
      unknown dtype, max_pages_per_seq > 4096 */
   TSV_ERR_UNSUPPORTED = -2,
   /* a kernel launch failed (hipGetLastError after the launch) */

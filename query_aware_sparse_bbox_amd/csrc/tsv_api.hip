@@ -42,7 +42,7 @@ int check_shape(const tsv_shape* s, Dims* d) {
   if (s->page_size != 8 && s->page_size != 16 && s->page_size != 32 &&
       s->page_size != 64)
     return TSV_ERR_UNSUPPORTED;
-  if (G != 1 && G != 2 && G != 4 && G != 8) return TSV_ERR_UNSUPPORTED;
+  if (G != 1 && G != 2 && G != 4 && G != 8 && G != 16) return TSV_ERR_UNSUPPORTED;
   if (s->max_pages_per_seq > tsv::kMaxPagesPerSeq) return TSV_ERR_UNSUPPORTED;
   // element offsets are computed in 64 bits; token positions in 32 bits
   if ((int64_t)s->max_pages_per_seq * s->page_size > INT32_MAX / 2)

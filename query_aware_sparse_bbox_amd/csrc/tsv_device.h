@@ -191,6 +191,14 @@ __device__ __forceinline__ float across_slots(float x, Op op) {
   return x;
 }
 
+// The value of lane ^ MASK (MASK = 8, 16, 32).
+template <int MASK>
+__device__ __forceinline__ float xor_lane(float x) {
+  if constexpr (MASK == 8) return dpp<kRowRor8>(x);
+  else if constexpr (MASK == 16) return xor16(x);
+  else return xor32(x);
+}
+
 // Balanced pairwise fp32 sum of t[0..N): T(lo,hi) = T(lo,mid) + T(mid,hi).
 template <int N>
 __device__ __forceinline__ float tree_sum(const float* t) {
@@ -365,7 +373,10 @@ constexpr int score_threads() { return G <= 1 ? 1024 : 512; }
 template <int DT, int D, int G, int NTH>
 struct ScoreCfg {
   static constexpr int EB = KV<DT>::bytes, C = KV<DT>::vec, L = D / C;
-  static constexpr int PPW = kWave / L;  // pages per wave per load
+  // a lane holds the queries of at most 8 heads; a group of 16 splits its
+  // heads over HS = 2 slices of L lanes that load the same box channels
+  static constexpr int HS = G > 8 ? 2 : 1, GH = G / HS;
+  static constexpr int PPW = kWave / (L * HS);  // pages per wave per load
   static constexpr int U = G >= 4 ? 1 : 4;  // rows per lane per batch
   static constexpr int NT = NTH, NW = NT / kWave;
   static constexpr int PB = NW * PPW * U;  // pages per batch
@@ -681,14 +692,15 @@ __device__ __forceinline__ void score_pages(const float* __restrict__ q,
                                             uint32_t* s_key) {
   using Cfg = ScoreCfg<DT, D, G, NT>;
   constexpr int EB = Cfg::EB, C = Cfg::C, L = Cfg::L, PPW = Cfg::PPW, U = Cfg::U;
-  constexpr int NW = Cfg::NW, PB = Cfg::PB;
+  constexpr int NW = Cfg::NW, PB = Cfg::PB, HS = Cfg::HS, GH = Cfg::GH;
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   const int nbatch = (n + PB - 1) / PB;
-  const int chunk = lane % L, slot = lane / L;
-  float qp[G][C], qn[G][C];
+  // lane: channel run `chunk` of page slot `slot`, heads hs*GH .. hs*GH+GH-1
+  const int chunk = lane % L, hs = (lane / L) % HS, slot = lane / (L * HS);
+  float qp[GH][C], qn[GH][C];
 #pragma unroll
-  for (int g = 0; g < G; ++g) {
-    const float* qg = q + ((size_t)b * Hq + h * G + g) * D + chunk * C;
+  for (int g = 0; g < GH; ++g) {
+    const float* qg = q + ((size_t)b * Hq + h * G + hs * GH + g) * D + chunk * C;
 #pragma unroll
     for (int cc = 0; cc < C; cc += 4) {
       const float4 x4 = *reinterpret_cast<const float4*>(qg + cc);
@@ -719,19 +731,29 @@ __device__ __forceinline__ void score_pages(const float* __restrict__ q,
       float mn[C], mx[C];
       unpack<DT, C>(rmn[u], mn);
       unpack<DT, C>(rmx[u], mx);
-      float best = 0.f;
+      float best = 0.f, sc[GH];
 #pragma unroll
-      for (int g = 0; g < G; ++g) {
+      for (int g = 0; g < GH; ++g) {
         float t[C];
 #pragma unroll
         for (int cc = 0; cc < C; ++cc)
           t[cc] = __builtin_fmaf(qn[g][cc], mn[cc], qp[g][cc] * mx[cc]);
-        const float sc = group_sum<L>(tree_sum<C>(t));
-        if constexpr (GSUM) best = g == 0 ? sc : best + sc;
-        else best = g == 0 ? sc : fmaxf(best, sc);
+        sc[g] = group_sum<L>(tree_sum<C>(t));
+        if constexpr (GSUM) best = g == 0 ? sc[g] : best + sc[g];
+        else best = g == 0 ? sc[g] : fmaxf(best, sc[g]);
+      }
+      if constexpr (HS == 2) {
+        // slice 0 combines slice 1's heads: the max is exact in any order,
+        // the sum continues head by head (heads 8..15 after 0..7)
+        if constexpr (GSUM) {
+#pragma unroll
+          for (int g = 0; g < GH; ++g) best = best + xor_lane<L>(sc[g]);
+        } else {
+          best = fmaxf(best, xor_lane<L>(best));
+        }
       }
       best = best == 0.f ? 0.f : best;  // -0 -> +0
-      if (p < n && chunk == 0) s_key[p] = order_key(best);
+      if (p < n && chunk == 0 && hs == 0) s_key[p] = order_key(best);
     }
   };
   // a ring of DEPTH batches in flight: batch bi's slot is refilled with
@@ -995,13 +1017,6 @@ __device__ __forceinline__ void finish_split(float (*s_acc)[G][D + 1], float (*s
   }
 }
 
-// Lanes `lane` and `lane ^ MASK` (MASK = 8, 16, 32: other token slots).
-template <int MASK>
-__device__ __forceinline__ float xor_lane(float x) {
-  if constexpr (MASK == 8) return dpp<kRowRor8>(x);
-  else if constexpr (MASK == 16) return xor16(x);
-  else return xor32(x);
-}
 
 // Fold the running softmax state of the partner slot (lane ^ MASK) into
 // this lane's: both end with the combined state.
@@ -1111,13 +1126,13 @@ struct ValuDecode {
   static constexpr int TILE = J * TPI;
 };
 
-template <int DT, int D, int G, int NT>
+template <int DT, int D, int G, int NT, int GS = G>
 __device__ __forceinline__ void valu_decode_range(const float* __restrict__ qg0,
                                                   const char* __restrict__ kb,
                                                   const char* __restrict__ vb,
                                                   const TokenList& tl, long t0, long t_end,
-                                                  float qscale, float (*s_acc)[G][D + 1],
-                                                  float (*s_mw)[G]) {
+                                                  float qscale, float (*s_acc)[GS][D + 1],
+                                                  float (*s_mw)[GS], int g0 = 0) {
   using VD = ValuDecode<DT, D, G, NT>;
   constexpr int EB = VD::EB, C = VD::C, L = VD::L, SPW = VD::SPW, TPI = VD::TPI, J = VD::J;
   constexpr int TILE = VD::TILE;
@@ -1219,14 +1234,21 @@ __device__ __forceinline__ void valu_decode_range(const float* __restrict__ qg0,
 #pragma unroll
     for (int g = 0; g < G; ++g) {
 #pragma unroll
-      for (int c = 0; c < C; ++c) s_acc[wave][g][chunk * C + c] = acc[g][c];
+      for (int c = 0; c < C; ++c) s_acc[wave][g0 + g][chunk * C + c] = acc[g][c];
       if (chunk == 0) {
-        s_acc[wave][g][D] = l_run[g];
-        s_mw[wave][g] = m_run[g];
+        s_acc[wave][g0 + g][D] = l_run[g];
+        s_mw[wave][g0 + g] = m_run[g];
       }
     }
   }
 }
+
+template <int DT, int D, int G, int NT, bool MF, int CH>
+__device__ __forceinline__ void decode_group(const float* __restrict__ qg0,
+                                             const char* __restrict__ kb,
+                                             const char* __restrict__ vb, const TokenList& tl,
+                                             long t0, long t_end, float qscale,
+                                             float (*s_acc)[G][D + 1], float (*s_mw)[G]);
 
 // Stages sel entries [e0, e0 + ecap) of a unit (logical page, physical
 // page) into LDS for a split decode workgroup.
@@ -1282,7 +1304,7 @@ __global__ __launch_bounds__(NT) void k_decode_split(
   }
   __syncthreads();
   const TokenList tl{s_lp, s_ph, min(cnt - e0, ecap), e0, len, log2P, Hkv, h, D};
-  valu_decode_range<DT, D, G, NT>(q + ((size_t)b * Hq + h * G) * D,
+  decode_group<DT, D, G, NT, false, 1>(q + ((size_t)b * Hq + h * G) * D,
                                   reinterpret_cast<const char*>(k_pool),
                                   reinterpret_cast<const char*>(v_pool), tl, t0, t_end, qscale,
                                   s_acc, s_mw);
@@ -1393,13 +1415,13 @@ struct MfmaDecode {
 // lane keeps one K and one V address per step.  Ends with each wave's state
 // in s_acc[wave] / s_mw[wave] (no barrier).  fp8 KV is widened to bf16 in
 // registers (exactly) and takes the bf16 instructions.
-template <int DT, int D, int G, int NW, int CH>
+template <int DT, int D, int G, int NW, int CH, int GS = G>
 __device__ __forceinline__ void mfma_decode_range(const float* __restrict__ qg0,
                                                   const char* __restrict__ kb,
                                                   const char* __restrict__ vb,
                                                   const TokenList& tl, long t0, long t_end,
-                                                  float qscale, float (*s_acc)[G][D + 1],
-                                                  float (*s_mw)[G]) {
+                                                  float qscale, float (*s_acc)[GS][D + 1],
+                                                  float (*s_mw)[GS], int g0 = 0) {
   constexpr int MDT = is_fp8(DT) ? DT_BF16 : DT;  // MFMA operand type
   constexpr int EB = KV<DT>::bytes;
   using M = Mma<MDT>;
@@ -1600,11 +1622,35 @@ __device__ __forceinline__ void mfma_decode_range(const float* __restrict__ qg0,
     for (int r = 0; r < 4; ++r) {
       const float sum = o[e][r] + xor32(o[e][r]);
       const int g = 4 * c4 + r;
-      if (g < G) s_acc[wave][g][NDT * n16 + e] = sum * (1.f / M::kPScale);
+      if (g < G) s_acc[wave][g0 + g][NDT * n16 + e] = sum * (1.f / M::kPScale);
     }
   if (lane < G) {
-    s_acc[wave][lane][D] = l_run;
-    s_mw[wave][lane] = m_run;
+    s_acc[wave][g0 + lane][D] = l_run;
+    s_mw[wave][g0 + lane] = m_run;
+  }
+}
+
+// Decode of all G heads of a group into the waves' combine areas s_acc /
+// s_mw [NW][G]: on MFMA (MF) or the VALU.  A lane holds the queries and sums
+// of at most 8 heads (4 with fp32 KV, whose lanes hold 4 channels of twice
+// the bytes), so larger groups run as several passes over the same tokens,
+// the later ones mostly reading them from L2.
+template <int DT, int D, int G, int NT, bool MF, int CH>
+__device__ __forceinline__ void decode_group(const float* __restrict__ qg0,
+                                             const char* __restrict__ kb,
+                                             const char* __restrict__ vb, const TokenList& tl,
+                                             long t0, long t_end, float qscale,
+                                             float (*s_acc)[G][D + 1], float (*s_mw)[G]) {
+  constexpr int GMAX = DT == DT_F32 ? 4 : 8;
+  constexpr int GP = G > GMAX ? GMAX : G;  // heads per pass
+#pragma unroll
+  for (int g0 = 0; g0 < G; g0 += GP) {
+    if constexpr (MF)
+      mfma_decode_range<DT, D, GP, NT / kWave, CH, G>(qg0 + (size_t)g0 * D, kb, vb, tl, t0,
+                                                      t_end, qscale, s_acc, s_mw, g0);
+    else
+      valu_decode_range<DT, D, GP, NT, G>(qg0 + (size_t)g0 * D, kb, vb, tl, t0, t_end, qscale,
+                                          s_acc, s_mw, g0);
   }
 }
 
@@ -1643,7 +1689,7 @@ __global__ __launch_bounds__(256, D == 128 ? 2 : 3) void k_decode_mfma(
   }
   __syncthreads();
   const TokenList tl{s_lp, s_ph, min(cnt - e0, ecap), e0, len, log2P, Hkv, h, D};
-  mfma_decode_range<DT, D, G, NW, 1>(q + ((size_t)b * Hq + h * G) * D,
+  decode_group<DT, D, G, NT, true, 1>(q + ((size_t)b * Hq + h * G) * D,
                                   reinterpret_cast<const char*>(k_pool),
                                   reinterpret_cast<const char*>(v_pool), tl, t0, t_end, qscale,
                                   s_acc, s_mw);
@@ -1664,7 +1710,7 @@ __global__ __launch_bounds__(256, D == 128 ? 2 : 3) void k_decode_mfma(
 // merges the S partial states, so the step stays one launch.
 
 template <int DT, int D, int G>
-constexpr bool step_uses_mfma() { return DT != DT_F32 && (G == 4 || G == 8); }
+constexpr bool step_uses_mfma() { return DT != DT_F32 && (G == 4 || G == 8 || G == 16); }
 
 // Dynamic LDS of k_step: block-table row and keys (MP words each, rounded to
 // 4), then the decode staging area.
@@ -1886,9 +1932,9 @@ __global__ __launch_bounds__(NT, (step_min_blocks<DT, D, G, NT>())) void k_step(
     // chunks of two 16-token steps: a split's waves often hold only two steps,
     // and longer chunks unroll into more code that every workgroup fetches once
     if constexpr (MF)
-      mfma_decode_range<DT, D, G, NW, 2>(qg0, kbp, vbp, tl, t0, t_end, qscale, s_acc, s_mw);
+      decode_group<DT, D, G, NT, true, 2>(qg0, kbp, vbp, tl, t0, t_end, qscale, s_acc, s_mw);
     else
-      valu_decode_range<DT, D, G, NT>(qg0, kbp, vbp, tl, t0, t_end, qscale, s_acc, s_mw);
+      decode_group<DT, D, G, NT, false, 2>(qg0, kbp, vbp, tl, t0, t_end, qscale, s_acc, s_mw);
     __syncthreads();
     finish_split<D, G, NT, NW, true>(s_acc, s_mw, partials, out, b, h, Hq, S, split, S);
   } else if (S == 1) {  // no tokens at all

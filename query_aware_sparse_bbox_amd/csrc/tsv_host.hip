@@ -33,9 +33,11 @@ size_t round_up(size_t x) { return (x + 255) / 256 * 256; }
 // clearing it first makes the check see this call's launches only.
 void clear_stale_error() { (void)hipGetLastError(); }
 
-// Grouped-query heads on 16-bit or fp8 KV take the MFMA decode (64-token
-// steps); everything else the VALU decode.
-bool use_mfma_decode(const Dims& d) { return d.dt != DT_F32 && (d.G == 4 || d.G == 8); }
+// Grouped-query heads (groups of 4, 8 or 16) on 16-bit or fp8 KV take the
+// MFMA decode (64-token steps); everything else the VALU decode.
+bool use_mfma_decode(const Dims& d) {
+  return d.dt != DT_F32 && (d.G == 4 || d.G == 8 || d.G == 16);
+}
 
 // Tiles per workgroup: enough workgroups to fill the chip several times
 // over, each streaming as many tiles as that allows.

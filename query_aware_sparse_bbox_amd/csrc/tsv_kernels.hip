@@ -28,6 +28,7 @@ hipError_t by_d_g(const Dims& d, Fn&& fn) {
       case 2: return fn(HD, IC<2>{});
       case 4: return fn(HD, IC<4>{});
       case 8: return fn(HD, IC<8>{});
+      case 16: return fn(HD, IC<16>{});
     }
     return hipErrorInvalidValue;
   };
@@ -117,7 +118,7 @@ hipError_t decode_t(const Dims& d, const DecodePlan& plan, const float* q, const
   const float qscale = scale * kLog2e;  // exp2 in the softmax
   hipError_t e = by_d_g(d, [&](auto HD, auto GG) -> hipError_t {
     constexpr int hd = decltype(HD)::value, g = decltype(GG)::value;
-    if constexpr (dt != DT_F32 && (g == 4 || g == 8)) {
+    if constexpr (dt != DT_F32 && (g == 4 || g == 8 || g == 16)) {
       hipLaunchKernelGGL((k_decode_mfma<dt, hd, g>), dim3(d.B * d.Hkv * S_max), dim3(256), 0, s,
                          q, k_pool, v_pool, bt, seq_lens, sel, sel_phys, sel_count, d.Hq, d.Hkv,
                          log2P, d.MP, d.NP, k_max, S_max, TPW, qscale, ws.partials, out);

@@ -125,6 +125,14 @@ def test_exchange_polls_hook_round_trip(tsv):
     assert not hasattr(tsv._lib, "tsv_debug_exchange_polls")
 
 
+def test_group_sizes_accepted(tsv):
+    """Groups of 1, 2, 4, 8 and 16 query heads per KV head are accepted."""
+    for g in (1, 2, 4, 8, 16):
+        s = shape(num_q_heads=2 * g, num_kv_heads=2)
+        assert tsv.tsv_workspace_bytes(s, 8) > 0, g
+        assert tsv.tsv_decode_step_launches(s, 8, True) >= 1, g
+
+
 def test_decode_step_launch_plan(tsv):
     # short block-table rows: the whole step of a row runs in workgroups of
     # its own, one launch (rows that leave the chip idle are spread over
@@ -145,6 +153,8 @@ def test_decode_step_launch_plan(tsv):
 @pytest.mark.parametrize("kw,status", [
     (dict(head_dim=96), -2), (dict(head_dim=32), -2), (dict(page_size=12), -2),
     (dict(kv_dtype=7), -2), (dict(kv_dtype=-1), -2), (dict(num_q_heads=24, num_kv_heads=8), -2),  # G = 3
+    (dict(num_q_heads=64, num_kv_heads=2), -2),  # G = 32
+    (dict(num_q_heads=48, num_kv_heads=4), -2),  # G = 12
     (dict(num_q_heads=7), -1), (dict(batch=0), -1), (dict(num_phys_pages=0), -1),
     (dict(max_pages_per_seq=5000), -2),
 ])

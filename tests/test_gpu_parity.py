@@ -147,6 +147,53 @@ def test_all_pages_is_dense_attention():
     _case(wl, k_max=wl.shape.max_pages_per_seq, k_per_seq=None)
 
 
+# Accepted shapes that the configurations above do not reach, each on the
+# one-launch step and on the three-call (phased) path: the MFMA decode with
+# 32- and 64-token pages (groups of 4 and 8, 16-bit and fp8 KV) and with
+# 8-token pages on fp16, fp32 KV with groups of 2, 8 and 16, and groups of 16
+# query heads (scoring in two head slices, decode in passes) in every KV type,
+# with the maximum and the sum over the group.
+SWEEP = [
+    ("tinyllama", dict(batch=2, context=1500, page_size=32, kv_dtype=W.BF16), {}),
+    ("tinyllama", dict(batch=2, context=3000, page_size=64, kv_dtype=W.F16), {}),
+    ("tinyllama", dict(batch=2, context=1500, page_size=32, kv_dtype=W.F8), {}),
+    ("tinyllama", dict(batch=2, context=3000, page_size=64, kv_dtype=W.F8E5), {}),
+    ("ragged", dict(batch=3, lens_range=(100, 2000), page_size=32), {}),
+    ("ragged", dict(batch=3, lens_range=(100, 3000), page_size=64, kv_dtype=W.BF16), {}),
+    ("ragged", dict(batch=3, lens_range=(100, 1500), page_size=32, kv_dtype=W.F8), {}),
+    ("tinyllama", dict(batch=2, context=700, page_size=8, kv_dtype=W.F16), {}),
+    ("tinyllama", dict(batch=2, context=900, num_q_heads=8, num_kv_heads=4, kv_dtype=W.F32), {}),
+    ("tinyllama", dict(batch=2, context=900, kv_dtype=W.F32), {}),
+    ("tinyllama", dict(batch=2, context=900, head_dim=128, kv_dtype=W.F32), {}),
+    ("tinyllama", dict(batch=2, context=1200, num_q_heads=64, num_kv_heads=4), {}),
+    ("tinyllama", dict(batch=2, context=1200, num_q_heads=64, num_kv_heads=4),
+     dict(group_agg=1)),
+    ("tinyllama", dict(batch=2, context=1200, num_q_heads=32, num_kv_heads=2, head_dim=128,
+                       kv_dtype=W.F16), {}),
+    ("tinyllama", dict(batch=2, context=800, num_q_heads=32, num_kv_heads=2, kv_dtype=W.F32),
+     {}),
+    ("tinyllama", dict(batch=2, context=800, num_q_heads=32, num_kv_heads=2, head_dim=128,
+                       kv_dtype=W.F32), dict(group_agg=1)),
+    ("tinyllama", dict(batch=2, context=1000, num_q_heads=64, num_kv_heads=4, kv_dtype=W.F8),
+     {}),
+    ("tinyllama", dict(batch=2, context=1000, num_q_heads=64, num_kv_heads=4,
+                       kv_dtype=W.F8E5, page_size=32), dict(group_agg=1, n_recent=2)),
+    ("ragged", dict(batch=2, lens_range=(50, 1500), num_q_heads=128), {}),
+    ("ragged", dict(batch=2, lens_range=(50, 1500), num_q_heads=128, kv_dtype=W.F32),
+     dict(group_agg=1)),
+]
+
+
+@pytest.mark.parametrize("name,kw,opts", SWEEP,
+                         ids=[f"{n}-{i}" for i, (n, _, _) in enumerate(SWEEP)])
+def test_shape_sweep(name, kw, opts):
+    wl = W.make(name, **kw)
+    o = oracle_run(wl, **opts)
+    compare(wl, gpu_run(wl, **opts), o)
+    compare(wl, gpu_run(wl, separate=True, **opts), o)
+    say(f"  {name} {kw} {opts}: one-launch and phased paths match")
+
+
 def test_scores_with_wide_single_wave_selection():
     """Rows of at most 512 pages select in one wave, which overwrites the page
     keys in local memory with page indices; with more than 64 pages kept the
