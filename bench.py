@@ -375,14 +375,19 @@ def main():
     torch.cuda.synchronize()
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     wall0 = time.perf_counter()
-    marks = []
     t0.record(stream)
-    run(K, marks)
+    run(K)
     t1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms_step = t0.elapsed_time(t1) / K
-    # per-replay step times (each replay closes R steps, or 1 when eager)
+    # the median of per-replay step times, from a second pass of K steps with
+    # an event after every replay (each closes R steps, or 1 when eager); the
+    # events add small gaps, so the mean above is taken without them
+    marks = []
+    t0.record(stream)
+    run(K, marks)
+    torch.cuda.synchronize()
     per, prev = [], t0
     for ev, count in marks:
         per.append(prev.elapsed_time(ev) / count)
@@ -516,7 +521,8 @@ def main():
                      "launches_per_step": launches,
                      "mean_step_us": ms_step * 1e3,
                      "median_step_us": ms_median * 1e3,
-                     "median_of": f"{len(per)} replays of {1 if args.eager else R} step(s)",
+                     "median_of": f"{len(per)} replays of {1 if args.eager else R} step(s), "
+                                  "timed in a second pass with an event after each replay",
                      "timed_as": "HIP events on the launch stream around the graph-replayed "
                                  "steps, divided by the step count",
                      "kernel_source": src},
