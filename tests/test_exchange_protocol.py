@@ -1,0 +1,236 @@
+"""The split-row counter protocol of the one-launch step, checked on the CPU.
+
+A row of the step split over S workgroups meets twice through three counter
+words: the score exchange (`row_exchange`: arrivals, then an all-arrived flag
+that waiting splits poll a bounded number of times) and the finish
+(`row_finish`: the last split to finish merges and clears the words).  Those
+two functions and their call sites in `k_step` are the whole protocol, and
+the model below is a transcription of them:
+
+* every store is relaxed: it is issued into a per-split set of stores in
+  flight, each of which may land in memory at any later point, in any order;
+* `stores_done()` (s_waitcnt vmcnt(0)) is a step that is enabled only once all
+  of the split's stores in flight have landed;
+* a fetch-add, a load or a landed store acts on one coherent copy of each
+  word (device-scope atomics are performed at the chip's shared cache level);
+* each split's operations are issued in program order.
+
+Every interleaving of S <= 4 splits, with every poll budget from 0 (every
+waiting split times out at once) to 3, is explored over two consecutive calls
+(the second call starts from the memory the first one left).  In every
+reachable state: a split that leaves the exchange with the flag set reads
+every other split's keys of the current call, the merging split reads every
+split's partial state of the current call, and the three words are zero once
+a call has ended, which is what the next call starts from.  The structure of
+the model is tied to the source: the test reads the two functions and the
+step kernel from the device header and checks that they perform the same
+operations in the same order.
+"""
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+DEVICE_H = os.path.join(ROOT, "query_aware_sparse_bbox_amd", "csrc", "tsv_device.h")
+
+# program counters of one split
+(KEY_STORE, KEY_WAIT, ARRIVE, REARM, SET_FLAG, POLL, READ_KEYS, PART_STORE, PART_WAIT, FINISH,
+ CLEAR_DONE, CLEAR_FLAG, MERGE, END) = range(14)
+
+# memory: arrive, flag, done, key[0..S-1], part[0..S-1]
+ARRIVE_W, FLAG_W, DONE_W = 0, 1, 2
+
+
+def explore(S, polls, calls=2, mistake=None):
+    """Depth-first search of every interleaving; returns (states, calls ended).
+
+    `mistake` plants one error in the protocol, to show that the checks
+    catch it: "no_key_wait" (a split counts itself in before its keys
+    land), "no_part_wait" (likewise before its partial state lands),
+    "flag_left_set" (the last split to finish does not clear the flag) or
+    "no_rearm" (the last split to arrive does not reset the arrivals)."""
+    key = lambda s: 3 + s
+    part = lambda s: 3 + S + s
+    mem0 = (0,) * (3 + 2 * S)
+    # split state: (pc, polls left, stores in flight)
+    split0 = tuple((KEY_STORE, 0, frozenset()) for _ in range(S))
+    start = (1, mem0, split0)
+    seen = {start}
+    stack = [start]
+    ended = 0
+
+    def succ(state):
+        call, mem, sp = state
+        out = []
+        for s, (pc, left, pend) in enumerate(sp):
+            # a store in flight lands
+            for loc, val in pend:
+                m = list(mem)
+                m[loc] = val
+                ns = list(sp)
+                ns[s] = (pc, left, pend - {(loc, val)})
+                out.append((call, tuple(m), tuple(ns)))
+
+            def go(pc2, left2=left, pend2=pend, mem2=mem):
+                ns = list(sp)
+                ns[s] = (pc2, left2, pend2)
+                out.append((call, mem2, tuple(ns)))
+
+            def with_word(loc, val):
+                m = list(mem)
+                m[loc] = val
+                return tuple(m)
+
+            if pc == KEY_STORE:
+                go(ARRIVE if mistake == "no_key_wait" else KEY_WAIT,
+                   pend2=pend | {(key(s), call)})
+            elif pc == KEY_WAIT:
+                if not pend:
+                    go(ARRIVE)
+            elif pc == ARRIVE:
+                got = mem[ARRIVE_W]
+                m = with_word(ARRIVE_W, got + 1)
+                if got == S - 1:
+                    go(SET_FLAG if mistake == "no_rearm" else REARM, mem2=m)
+                else:
+                    go(POLL, left2=polls, mem2=m)
+            elif pc == REARM:
+                go(SET_FLAG, pend2=pend | {(ARRIVE_W, 0)})
+            elif pc == SET_FLAG:
+                go(READ_KEYS, pend2=pend | {(FLAG_W, 1)})
+            elif pc == POLL:
+                if left == 0:
+                    go(PART_STORE)  # timed out: this split scores every page itself
+                elif mem[FLAG_W] != 0:
+                    go(READ_KEYS)
+                else:
+                    go(POLL, left2=left - 1)
+            elif pc == READ_KEYS:
+                # every key read at once: keys only ever change to the current
+                # call's, so this is at least as strict as reading them one
+                # after the other
+                for k in range(S):
+                    assert mem[key(k)] == call, (
+                        f"S={S} polls={polls}: split {s} read split {k}'s keys of call "
+                        f"{mem[key(k)]} in call {call}")
+                go(PART_STORE)
+            elif pc == PART_STORE:
+                go(FINISH if mistake == "no_part_wait" else PART_WAIT,
+                   pend2=pend | {(part(s), call)})
+            elif pc == PART_WAIT:
+                if not pend:
+                    go(FINISH)
+            elif pc == FINISH:
+                got = mem[DONE_W]
+                m = with_word(DONE_W, got + 1)
+                go(CLEAR_DONE if got == S - 1 else END, mem2=m)
+            elif pc == CLEAR_DONE:
+                go(MERGE if mistake == "flag_left_set" else CLEAR_FLAG,
+                   pend2=pend | {(DONE_W, 0)})
+            elif pc == CLEAR_FLAG:
+                go(MERGE, pend2=pend | {(FLAG_W, 0)})
+            elif pc == MERGE:
+                for k in range(S):
+                    assert mem[part(k)] == call, (
+                        f"S={S} polls={polls}: the merge read split {k}'s partial state of call "
+                        f"{mem[part(k)]} in call {call}")
+                go(END)
+        return out
+
+    while stack:
+        state = stack.pop()
+        call, mem, sp = state
+        nxt = succ(state)
+        if not nxt:
+            # every split ended and every store landed: the launch is over
+            assert all(x[0] == END and not x[2] for x in sp), f"stuck state {state}"
+            assert mem[ARRIVE_W] == 0 and mem[FLAG_W] == 0 and mem[DONE_W] == 0, (
+                f"S={S} polls={polls}: counters {mem[:3]} left after call {call}")
+            ended += 1
+            if call < calls:
+                nxt = [(call + 1, mem, split0)]
+        for n in nxt:
+            if n not in seen:
+                seen.add(n)
+                stack.append(n)
+    return len(seen), ended
+
+
+@pytest.mark.parametrize("S", [1, 2, 3, 4])
+@pytest.mark.parametrize("polls", [0, 1, 2, 3])
+def test_every_interleaving(S, polls):
+    states, ended = explore(S, polls)
+    assert ended >= 1 and states > S
+
+
+@pytest.mark.parametrize("mistake,pattern", [
+    ("no_key_wait", "keys of call"),
+    ("no_part_wait", "partial state of call"),
+    ("flag_left_set", "left after call|keys of call"),
+    ("no_rearm", "left after call"),
+])
+def test_model_catches_planted_mistakes(mistake, pattern):
+    with pytest.raises(AssertionError, match=pattern):
+        explore(2, 2, mistake=mistake)
+
+
+# --- the model's operations, read from the source -------------------------
+
+def function_body(text, signature):
+    i = text.index(signature)
+    i = text.index("{", i)
+    depth = 0
+    for k in range(i, len(text)):
+        if text[k] == "{":
+            depth += 1
+        elif text[k] == "}":
+            depth -= 1
+            if depth == 0:
+                return text[i:k + 1]
+    raise AssertionError("unbalanced braces")
+
+
+def ops(body):
+    """The counter operations of a function body, in source order."""
+    pat = re.compile(r"__hip_atomic_fetch_add\(c \+ (\w+)|st_dev\(c \+ (\w+), (\w+)\)|"
+                     r"ld_dev\(c \+ (\w+)\)")
+    out = []
+    for m in pat.finditer(body):
+        if m.group(1):
+            out.append(("fetch_add", m.group(1)))
+        elif m.group(2):
+            out.append(("store", m.group(2), m.group(3)))
+        else:
+            out.append(("load", m.group(4)))
+    return out
+
+
+def test_model_matches_the_source():
+    text = open(DEVICE_H).read()
+    ex = function_body(text, "int row_exchange(uint32_t* c, int S, int polls)")
+    assert ops(ex) == [("fetch_add", "kSyncArrive"), ("store", "kSyncArrive", "0u"),
+                       ("store", "kSyncAll", "1u"), ("load", "kSyncAll")]
+    # the re-arm and flag stores sit in the last arrival's branch, the poll in
+    # a loop bounded by `polls`
+    assert re.search(r"if \(o == \(uint32_t\)S - 1\) \{[^}]*st_dev\(c \+ kSyncArrive, 0u\);\s*"
+                     r"st_dev\(c \+ kSyncAll, 1u\);\s*return 1;", ex)
+    assert re.search(r"for \(int it = 0; it < polls; \+\+it\) \{\s*if \(ld_dev\(c \+ kSyncAll\) "
+                     r"!= 0u\) return 1;", ex)
+    fin = function_body(text, "int row_finish(uint32_t* c, int S)")
+    assert ops(fin) == [("fetch_add", "kSyncDone"), ("store", "kSyncDone", "0u"),
+                        ("store", "kSyncAll", "0u")]
+    assert re.search(r"if \(o != \(uint32_t\)S - 1\) return 0;", fin)
+    # call sites: each split's stores are waited for before it counts itself in
+    step = function_body(text, "void k_step(")
+    i_ex = step.index("row_exchange(rsync, S, polls)")
+    i_fin = step.index("row_finish(rsync, S)")
+    before_ex = step[:i_ex]
+    assert before_ex.rindex("stores_done();") > before_ex.rindex("st_dev(krow + p, s_key[p]);")
+    before_fin = step[:i_fin]
+    assert before_fin.rindex("stores_done();") > before_fin.rindex("finish_split<")
+    # keys are read only when the exchange succeeded; the merge only by the last
+    after_ex = step[i_ex:]
+    assert re.search(r"if \(s_flag\) \{\s*for \(int p = tid; p < n; p \+= NT\)\s*"
+                     r"if \(\(p / PB\) % S != split\) s_key\[p\] = ld_dev\(krow \+ p\);", after_ex)
+    assert re.search(r"if \(!s_flag\) return;\s*merge_row<", step[i_fin:])
