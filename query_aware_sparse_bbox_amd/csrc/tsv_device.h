@@ -65,6 +65,23 @@ __device__ __forceinline__ uint4 ldb(const void* p) {
   }
 }
 
+// The same lane load marked non-temporal (`nt`): for data that one step reads
+// once.  On the page boxes it measured 4-11% faster steps than plain loads;
+// on K/V it did not pay in the one-launch step.
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+template <int LB>
+__device__ __forceinline__ uint4 ldb_nt(const void* p) {
+  static_assert(LB == 8 || LB == 16, "lane loads are 8 or 16 bytes");
+  if constexpr (LB == 8) {
+    const u32x2_t x = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p));
+    return make_uint4(x.x, x.y, 0u, 0u);
+  } else {
+    const u32x4_t x = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+    return make_uint4(x.x, x.y, x.z, x.w);
+  }
+}
+
 // Four OCP fp8 values (bytes 0..3 of w; E4M3 for DT_F8, E5M2 for DT_F8E5)
 // widened to fp32, exactly.
 template <int DT>
@@ -720,8 +737,8 @@ __device__ __forceinline__ void score_pages(const float* __restrict__ q,
     for (int u = 0; u < U; ++u) {
       const int p = min(bi * PB + u * (NW * PPW) + wave * PPW + slot, n - 1);
       const size_t row = ((size_t)s_phys[p] * Hkv + h) * 2 * D + chunk * C;
-      mn[u] = ldb<C * EB>(mb + row * EB);
-      mx[u] = ldb<C * EB>(mb + (row + D) * EB);
+      mn[u] = ldb_nt<C * EB>(mb + row * EB);
+      mx[u] = ldb_nt<C * EB>(mb + (row + D) * EB);
     }
   };
   auto score_batch = [&](int bi, const uint4 (&rmn)[U], const uint4 (&rmx)[U]) {
@@ -757,25 +774,33 @@ __device__ __forceinline__ void score_pages(const float* __restrict__ q,
     }
   };
   // a ring of DEPTH batches in flight: batch bi's slot is refilled with
-  // batch bi + DEPTH*bstride right after bi is scored (indices past the
-  // last batch reload the last one, so the loads need no branch).  fp8 lanes
-  // load 8 bytes, so their ring is twice as deep for the same bytes in flight
-  // (single-row batches only: four-row batches would not fit 1024-thread
-  // workgroups' registers).
+  // batch bi + DEPTH*bstride right after bi is scored.  The loads take no
+  // branch (indices past the last batch reload the last one), and the
+  // steady-state loop refills every slot, so each wait in it leaves the same
+  // DEPTH-1 batches in flight: a load issued under a condition would make
+  // the compiler drain the whole ring at the top of every round.  fp8 lanes
+  // load 8 bytes, so their ring is twice as deep for the same bytes in
+  // flight (single-row batches only: four-row batches would not fit
+  // 1024-thread workgroups' registers).
   constexpr int DEPTH = U == 1 ? 4 * (16 / (C * EB)) : 2;
   if (bstart >= nbatch) return;
   uint4 rmn[DEPTH][U], rmx[DEPTH][U];
 #pragma unroll
-  for (int i = 0; i < DEPTH; ++i)
-    if (i == 0 || bstart + i * bstride < nbatch) load_batch(bstart + i * bstride, rmn[i], rmx[i]);
-  for (int base = bstart; base < nbatch; base += DEPTH * bstride) {
+  for (int i = 0; i < DEPTH; ++i) load_batch(min(bstart + i * bstride, nbatch - 1), rmn[i], rmx[i]);
+  int base = bstart;
+  for (; base + DEPTH * bstride < nbatch; base += DEPTH * bstride) {
 #pragma unroll
     for (int i = 0; i < DEPTH; ++i) {
       const int bi = base + i * bstride;
-      if (bi < nbatch) score_batch(bi, rmn[i], rmx[i]);
-      if (base + DEPTH * bstride < nbatch)
-        load_batch(min(bi + DEPTH * bstride, nbatch - 1), rmn[i], rmx[i]);
+      score_batch(bi, rmn[i], rmx[i]);
+      load_batch(min(bi + DEPTH * bstride, nbatch - 1), rmn[i], rmx[i]);
     }
+  }
+  // the last round: the batches still in the ring
+#pragma unroll
+  for (int i = 0; i < DEPTH; ++i) {
+    const int bi = base + i * bstride;
+    if (bi < nbatch) score_batch(bi, rmn[i], rmx[i]);
   }
 }
 
