@@ -66,8 +66,9 @@ __device__ __forceinline__ uint4 ldb(const void* p) {
 }
 
 // The same lane load marked non-temporal (`nt`): for data that one step reads
-// once.  On the page boxes it measured 4-11% faster steps than plain loads;
-// on K/V it did not pay in the one-launch step.
+// once.  On the page boxes it measured 4-11% faster steps than plain loads
+// (except fp8 boxes read four rows per lane, 7% slower); on K/V it did not
+// pay in the one-launch step.
 typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 template <int LB>
@@ -737,8 +738,13 @@ __device__ __forceinline__ void score_pages(const float* __restrict__ q,
     for (int u = 0; u < U; ++u) {
       const int p = min(bi * PB + u * (NW * PPW) + wave * PPW + slot, n - 1);
       const size_t row = ((size_t)s_phys[p] * Hkv + h) * 2 * D + chunk * C;
-      mn[u] = ldb_nt<C * EB>(mb + row * EB);
-      mx[u] = ldb_nt<C * EB>(mb + (row + D) * EB);
+      if constexpr (U == 1 || C * EB == 16) {
+        mn[u] = ldb_nt<C * EB>(mb + row * EB);
+        mx[u] = ldb_nt<C * EB>(mb + (row + D) * EB);
+      } else {  // 8-byte lanes, four rows each: plain loads measured faster
+        mn[u] = ldb<C * EB>(mb + row * EB);
+        mx[u] = ldb<C * EB>(mb + (row + D) * EB);
+      }
     }
   };
   auto score_batch = [&](int bi, const uint4 (&rmn)[U], const uint4 (&rmx)[U]) {
@@ -1146,8 +1152,11 @@ __device__ __forceinline__ StepMap step_map(const TokenList& tl, const char* kb,
 template <int DT, int D, int G, int NT>
 struct ValuDecode {
   static constexpr int EB = KV<DT>::bytes, C = KV<DT>::vec, L = D / C;
-  // loads in flight per lane and buffer: 16-wave workgroups hold half as many
-  static constexpr int SPW = kWave / L, NW = NT / kWave, TPI = NW * SPW, J = NT >= 1024 ? 2 : 4;
+  // loads in flight per lane and buffer: 16-wave workgroups hold half as many;
+  // fp8 lanes load 8 bytes, so they hold twice as many tokens for the same
+  // bytes in flight
+  static constexpr int SPW = kWave / L, NW = NT / kWave, TPI = NW * SPW,
+                       J = (NT >= 1024 ? 2 : 4) * (16 / (C * EB));
   static constexpr int TILE = J * TPI;
 };
 

@@ -83,8 +83,9 @@ int step_splits(const Dims& d, int k_max) {
 
 int decode_tile_tokens(const Dims& d) {
   if (use_mfma_decode(d)) return 64;
+  // the VALU decode's tile (ValuDecode::TILE for kDecodeThreads threads)
   const int C = kv_vec(d.dt), L = d.D / C, SPW = kWave / L;
-  return 4 * (kDecodeThreads / kWave) * SPW;
+  return 4 * (16 / (C * kv_bytes(d.dt))) * (kDecodeThreads / kWave) * SPW;
 }
 
 int decode_splits(const Dims& d, int k_max) {

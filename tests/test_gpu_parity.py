@@ -181,6 +181,9 @@ SWEEP = [
     ("ragged", dict(batch=2, lens_range=(50, 1500), num_q_heads=128), {}),
     ("ragged", dict(batch=2, lens_range=(50, 1500), num_q_heads=128, kv_dtype=W.F32),
      dict(group_agg=1)),
+    # VALU decode on fp8 (G = 1 and 2): tiles of twice the tokens of 16-bit KV
+    ("llama_long", dict(batch=2, context=4096, kv_dtype=W.F8), {}),
+    ("ragged", dict(batch=3, lens_range=(100, 3000), num_q_heads=16, kv_dtype=W.F8E5), {}),
 ]
 
 
