@@ -218,6 +218,9 @@ def parse():
                     help="skip the selection-quality / dense-speedup report")
     ap.add_argument("--copy-calibrate", type=float, default=0.0, metavar="MB",
                     help="only run a plain device copy of MB megabytes, 5 times, and exit")
+    ap.add_argument("--phases", action="store_true",
+                    help="only print the one-launch step's per-workgroup phase times, from the "
+                         "testing library's phase stamps over --steps eager steps, and exit")
     return ap.parse_args()
 
 
@@ -236,6 +239,67 @@ def copy_calibrate(mb):
     ms = t0.elapsed_time(t1) / 5
     print(json.dumps({"copy_bytes_each_way": n * 4, "ms": ms,
                       "gbs_read_plus_write": 2 * n * 4 / (ms * 1e-3) / 1e9}), flush=True)
+
+
+PHASES = [("stage", 0, 1, "start -> block-table row staged (and the token appended)"),
+          ("score", 1, 2, "page scoring, with a split row's key exchange"),
+          ("select", 2, 3, "top-K selection"),
+          ("decode", 3, 4, "attention over the kept pages' tokens"),
+          ("finish", 4, 5, "combine of the waves' states, output (merge of split rows)")]
+
+
+def phases(args, T, sh, wl, instance, q, k_new, v_new, bt, lens, k_max, kps, n_sink, scale,
+           launches):
+    """Phase times of the one-launch step from the testing library's stamps
+    (100 MHz real-time counter, 10 ns ticks), per workgroup, over the last
+    --steps eager steps (each read back right after its step)."""
+    import torch
+
+    if launches != 1:
+        print(f"[phases] {args.config}: the step takes {launches} launches; phase stamps "
+              "exist for the one-launch step only", flush=True)
+        return
+    t = T.testing_library()
+    R = max(2, args.rotate or 2)
+    insts = [instance() for _ in range(R)]
+    torch.cuda.synchronize()
+
+    def step(d):
+        t.tsv_decode_step(sh, q, k_new, v_new, d.k_pool, d.v_pool, d.meta, bt, lens, k_max, kps,
+                          n_sink, scale, d.sel, d.cnt, None, d.out, d.ws)
+
+    for i in range(args.warmup):
+        step(insts[i % R])
+    torch.cuda.synchronize()
+    per = {name: [] for name, *_ in PHASES}
+    spans, totals = [], []
+    for i in range(args.steps):
+        step(insts[i % R])
+        torch.cuda.synchronize()
+        st = t.tsv_debug_phase_stamps(sh.kv_dtype).astype(np.int64)
+        live = st[:, 5] > st[:, 0]
+        live &= st[:, 0] > 0
+        st = st[live]
+        t0 = st[:, 0].min()
+        spans.append((st[:, 5].max() - t0) / 100.0)
+        totals.append(np.median(st[:, 5] - st[:, 0]) / 100.0)
+        for name, a, b, _ in PHASES:
+            per[name].append((st[:, b] - st[:, a]) / 100.0)
+    cmd = "python3 bench.py " + " ".join(sys.argv[1:])
+    lines = [f"# {args.config}" + (f" (KV {args.kv_dtype})" if args.kv_dtype else "") +
+             ": one-launch step, phase times per workgroup", "",
+             f"  {cmd}", "",
+             f"  shape {sh}", f"  workgroups per step: {int(live.sum())}; "
+             f"{args.steps} eager steps after {args.warmup} warm-up, each read back right after it",
+             f"  kernel span (first start to last end) p50 {np.median(spans):.2f} us, "
+             f"min {np.min(spans):.2f}, max {np.max(spans):.2f}",
+             f"  workgroup life p50 {np.median(totals):.2f} us", "",
+             f"  {'phase':<8}{'p10 us':>9}{'p50 us':>9}{'p90 us':>9}{'max us':>9}  what"]
+    for name, a, b, what in PHASES:
+        x = np.concatenate(per[name])
+        lines.append(f"  {name:<8}{np.percentile(x, 10):>9.2f}{np.percentile(x, 50):>9.2f}"
+                     f"{np.percentile(x, 90):>9.2f}{x.max():>9.2f}  {what}")
+    print("\n".join(lines), flush=True)
 
 
 def main():
@@ -301,6 +365,11 @@ def main():
         else:
             T.tsv_decode_step(sh, q, k_new, v_new, d.k_pool, d.v_pool, d.meta, bt, lens, k_max,
                               kps, n_sink, scale, d.sel, d.cnt, None, d.out, d.ws)
+
+    if args.phases:
+        phases(args, T, sh, wl, instance, q, k_new, v_new, bt, lens, k_max, kps, n_sink, scale,
+               launches)
+        return
 
     first = instance()
     step(first)

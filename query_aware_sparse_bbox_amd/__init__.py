@@ -37,7 +37,7 @@ EXPORTS = ("tsv_version", "tsv_status_string", "tsv_meta_bytes", "tsv_workspace_
            "tsv_select_pages", "tsv_sparse_decode", "tsv_decode_step",
            "tsv_select_pages_ex", "tsv_decode_step_ex", "tsv_decode_step_noalloc")
 # declared in include/tsv_testing.h, exported by the testing library only
-TEST_EXPORTS = ("tsv_debug_exchange_polls",)
+TEST_EXPORTS = ("tsv_debug_exchange_polls", "tsv_debug_phase_stamps")
 
 
 class TsvError(RuntimeError):
@@ -87,7 +87,8 @@ _SIGS = {
     "tsv_decode_step_noalloc": ([_SP, _P, _P, _P, _P, _P, _P, _P, _P, _I, _P, _I, _OP, _F, _P,
                                  _P, _P, _P, _P], ctypes.c_int),
 }
-_TEST_SIGS = {"tsv_debug_exchange_polls": ([_I], ctypes.c_int)}
+_TEST_SIGS = {"tsv_debug_exchange_polls": ([_I], ctypes.c_int),
+              "tsv_debug_phase_stamps": ([_I, ctypes.c_void_p, ctypes.c_size_t], ctypes.c_int)}
 
 
 def _ptr(t):
@@ -150,6 +151,17 @@ class Library:
         itself (returns the previous limit); polls < 0 returns the current
         limit."""
         return self.lib.tsv_debug_exchange_polls(int(polls))
+
+    def tsv_debug_phase_stamps(self, kv_dtype: int):
+        """Testing library only: the last one-launch step's phase stamps of
+        KV type kv_dtype, a uint64 numpy array [8192][8] (slots as in
+        include/tsv_testing.h)."""
+        import numpy as np
+
+        buf = np.zeros((8192, 8), dtype=np.uint64)
+        self._call("tsv_debug_phase_stamps", int(kv_dtype), ctypes.c_void_p(buf.ctypes.data),
+                   buf.nbytes)
+        return buf
 
     def tsv_meta_bytes(self, shape) -> int:
         return self.lib.tsv_meta_bytes(ctypes.byref(Shape.of(shape)))
@@ -240,7 +252,8 @@ _testing = None
 
 def testing_library() -> Library:
     """The testing build (libtsv_testhooks.so): the same kernels and entry
-    points plus tsv_debug_exchange_polls.  Loaded on first use."""
+    points plus tsv_debug_exchange_polls and tsv_debug_phase_stamps (its
+    one-launch step kernels record phase stamps).  Loaded on first use."""
     global _testing
     if _testing is None:
         _testing = Library(TESTHOOKS_PATH, test_hooks=True)

@@ -5,8 +5,9 @@ once per KV type and kernel family (phased kernels, one-launch step) into
 separate objects, in parallel, then linked with the host layer into
 
   libtsv.so             the library proper (include/tsv.h)
-  libtsv_testhooks.so   the same kernels and entry points plus the testing hook
-                        of include/tsv_testing.h
+  libtsv_testhooks.so   the same entry points plus the testing hooks of
+                        include/tsv_testing.h; its one-launch step kernels
+                        record phase stamps (-DTSV_PHASE_STAMPS)
 
 Flags:
   -ffp-contract=off   no implicit multiply-add fusion: page scores must match
@@ -57,6 +58,9 @@ def units(extra=()):
     for tname, t in KV_TYPES.items():
         for pname, p in PARTS.items():
             cc("tsv_kernels.hip", f"kernels_{tname}_{pname}", [f"-DTSV_DT={t}", f"-DTSV_PART={p}"])
+        # the testing library's step kernels record phase stamps
+        cc("tsv_kernels.hip", f"stamped_{tname}_step",
+           [f"-DTSV_DT={t}", f"-DTSV_PART={PARTS['step']}", "-DTSV_PHASE_STAMPS"])
     cc("tsv_host.hip", "host")
     cc("tsv_scratch.hip", "scratch")
     cc("tsv_api.hip", "api")
@@ -78,10 +82,12 @@ def build(extra_flags=(), verbose=False, jobs=None):
         list(pool.map(run, [c for _, c in todo]))
     objs = {os.path.basename(o)[:-2]: o for o, _ in todo}
     kernels = [o for n, o in objs.items() if n.startswith("kernels_")]
-    for lib, api in ((LIB, "api"), (LIB_TESTHOOKS, "api_testhooks")):
+    testing = [o for n, o in objs.items()
+               if n.startswith("stamped_") or (n.startswith("kernels_") and n.endswith("_phased"))]
+    for lib, api, kobjs in ((LIB, "api", kernels), (LIB_TESTHOOKS, "api_testhooks", testing)):
         tmp = lib + ".tmp"
         run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, objs[api],
-             objs["host"], objs["scratch"], *kernels])
+             objs["host"], objs["scratch"], *kobjs])
         os.replace(tmp, lib)
     return LIB
 

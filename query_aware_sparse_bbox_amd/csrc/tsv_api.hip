@@ -126,6 +126,20 @@ int tsv_version(void) { return TSV_VERSION; }
 int tsv_debug_exchange_polls(int32_t polls) {
   return polls < 0 ? g_exchange_polls.load() : g_exchange_polls.exchange(polls);
 }
+
+int tsv_debug_phase_stamps(int32_t kv_dtype, void* host, size_t bytes) {
+  if (host == nullptr) return TSV_ERR_INVALID_ARG;
+  hipError_t e;
+  switch (kv_dtype) {
+    case TSV_F32: e = tsv::read_phase_stamps_t<tsv::DT_F32>(host, bytes); break;
+    case TSV_F16: e = tsv::read_phase_stamps_t<tsv::DT_F16>(host, bytes); break;
+    case TSV_BF16: e = tsv::read_phase_stamps_t<tsv::DT_BF16>(host, bytes); break;
+    case TSV_FP8_E4M3: e = tsv::read_phase_stamps_t<tsv::DT_F8>(host, bytes); break;
+    case TSV_FP8_E5M2: e = tsv::read_phase_stamps_t<tsv::DT_F8E5>(host, bytes); break;
+    default: return TSV_ERR_INVALID_ARG;
+  }
+  return e == hipSuccess ? TSV_OK : TSV_ERR_HIP;
+}
 #endif
 
 const char* tsv_status_string(int status) {

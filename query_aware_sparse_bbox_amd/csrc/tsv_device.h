@@ -36,6 +36,35 @@
 #include "tsv_launch.h"
 
 namespace tsv {
+
+#ifdef TSV_PHASE_STAMPS
+// Phase stamps of the testing build: thread 0 of every workgroup of the
+// one-launch step records the GPU's 100 MHz real-time counter at the step's
+// phase boundaries (slot 0 start, 1 block-table row staged, 2 scored (with
+// the split rows' key exchange), 3 selected, 4 decoded, 5 end), and its
+// (row, split) in slot 6.  The last launch's stamps are read back through
+// tsv_debug_phase_stamps.
+constexpr int kStampWorkgroups = 8192, kStampSlots = 8;
+__device__ unsigned long long g_phase_stamps[kStampWorkgroups][kStampSlots];
+#define TSV_STAMP(i)                                                      \
+  do {                                                                    \
+    if (threadIdx.x == 0 && blockIdx.x < kStampWorkgroups)                \
+      g_phase_stamps[blockIdx.x][i] = __builtin_amdgcn_s_memrealtime();   \
+  } while (0)
+#define TSV_STAMP_VALUE(i, v)                                             \
+  do {                                                                    \
+    if (threadIdx.x == 0 && blockIdx.x < kStampWorkgroups)                \
+      g_phase_stamps[blockIdx.x][i] = (v);                                \
+  } while (0)
+#else
+#define TSV_STAMP(i) \
+  do {               \
+  } while (0)
+#define TSV_STAMP_VALUE(i, v) \
+  do {                        \
+  } while (0)
+#endif
+
 namespace {
 
 constexpr int kWave = 64;
@@ -1865,9 +1894,11 @@ __global__ __launch_bounds__(NT, (step_min_blocks<DT, D, G, NT>())) void k_step(
 
   // workgroup -> (row, split): the S splits of a row share blockIdx mod 8,
   // i.e. one XCD and its L2, which then serves the keys they exchange
+  TSV_STAMP(0);
   const int grp = blockIdx.x / (8 * S), within = blockIdx.x - grp * 8 * S;
   const int split = within >> 3, unit = grp * 8 + (within & 7);
   if (unit >= units) return;
+  TSV_STAMP_VALUE(6, ((unsigned long long)unit << 32) | (unsigned)split);
   const int b = unit / Hkv, h = unit - b * Hkv;
   const int tid = threadIdx.x;
   const int P = 1 << log2P;
@@ -1904,6 +1935,7 @@ __global__ __launch_bounds__(NT, (step_min_blocks<DT, D, G, NT>())) void k_step(
     }
   }
   __syncthreads();  // block-table row staged; the appended token visible to the workgroup
+  TSV_STAMP(1);
   // Scoring.  A split row's S workgroups score every S-th batch of pages
   // each and exchange the keys through the workspace; a split whose wait
   // times out scores the remaining batches itself (bit-identical keys).
@@ -1936,6 +1968,7 @@ __global__ __launch_bounds__(NT, (step_min_blocks<DT, D, G, NT>())) void k_step(
     bstride = 1;
   }
   __syncthreads();
+  TSV_STAMP(2);
   if (scores_out && split == 0) {  // uniform over the workgroup
     float* srow_out = scores_out + (size_t)unit * MP;
     for (int p = tid; p < n; p += NT) srow_out[p] = key_to_score(s_key[p]);
@@ -1949,6 +1982,7 @@ __global__ __launch_bounds__(NT, (step_min_blocks<DT, D, G, NT>())) void k_step(
       n <= kWaveSelectPages
           ? select_wave<NT>(s_key, s_phys, n, keff, f, r, k_max, sl)
           : select_block<NT>(s_key, s_phys, n, keff, f, r, k_max, nullptr, nullptr, nullptr, sl);
+  TSV_STAMP(3);
   int32_t* srow = sel + (size_t)unit * k_max;
   const size_t hq0 = (size_t)b * Hq + h * G;
   float* orow = out + hq0 * D;
@@ -1970,6 +2004,7 @@ __global__ __launch_bounds__(NT, (step_min_blocks<DT, D, G, NT>())) void k_step(
     else
       decode_group<DT, D, G, NT, false, 2>(qg0, kbp, vbp, tl, t0, t_end, qscale, s_acc, s_mw);
     __syncthreads();
+    TSV_STAMP(4);
     finish_split<D, G, NT, NW, true>(s_acc, s_mw, partials, out, b, h, Hq, S, split, S);
   } else if (S == 1) {  // no tokens at all
     for (int i = tid; i < G * D; i += NT) orow[i] = 0.f;
@@ -1984,14 +2019,21 @@ __global__ __launch_bounds__(NT, (step_min_blocks<DT, D, G, NT>())) void k_step(
     for (int i = tid; i < k_max; i += NT) srow[i] = i < cnt ? (int32_t)s_key[i] : -1;
     if (tid == 0) sel_count[unit] = cnt;
   }
-  if (S == 1) return;
+  if (S == 1) {
+    TSV_STAMP(5);
+    return;
+  }
   // the last split of the row to get here merges the S partial states
   stores_done();
   __syncthreads();
   if (tid == 0) s_flag = row_finish(rsync, S);
   __syncthreads();
-  if (!s_flag) return;
+  if (!s_flag) {
+    TSV_STAMP(5);
+    return;
+  }
   merge_row<D, G, NT>(partials, S, orow, hq0);
+  TSV_STAMP(5);
 }
 
 }  // namespace

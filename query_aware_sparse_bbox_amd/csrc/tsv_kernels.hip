@@ -2,6 +2,7 @@
 // file once per KV type (TSV_DT) and kernel family (TSV_PART: phased kernels
 // or the one-launch step), so the instantiations of the device templates
 // spread over several objects that compile in parallel.
+#include <algorithm>
 #include <type_traits>
 
 #include "tsv_device.h"
@@ -180,6 +181,14 @@ template hipError_t decode_t<TSV_DT>(const Dims&, const DecodePlan&, const float
                                      const int32_t*, const int32_t*, const int32_t*, int, float,
                                      const Workspace&, float*, hipStream_t);
 #elif TSV_PART == TSV_PART_STEP
+#ifdef TSV_PHASE_STAMPS
+// The last step launch's phase stamps of this KV type (testing build).
+template <>
+hipError_t read_phase_stamps_t<TSV_DT>(void* host, size_t bytes) {
+  return hipMemcpyFromSymbol(host, HIP_SYMBOL(g_phase_stamps),
+                             std::min(bytes, sizeof(g_phase_stamps)), 0, hipMemcpyDeviceToHost);
+}
+#endif
 template hipError_t step_t<TSV_DT>(const Dims&, const StepPlan&, const float*, const void*,
                                    const void*, void*, void*, void*, const int32_t*,
                                    const int32_t*, int, const int32_t*, const SelectPolicy&,

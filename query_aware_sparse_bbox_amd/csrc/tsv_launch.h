@@ -114,6 +114,10 @@ hipError_t decode_t(const Dims& d, const DecodePlan& plan, const float* q, const
                     const void* v_pool, const int32_t* bt, const int32_t* seq_lens,
                     const int32_t* sel, const int32_t* sel_phys, const int32_t* sel_count,
                     int k_max, float scale, const Workspace& ws, float* out, hipStream_t s);
+// Testing build only: copies the last step launch's phase stamps of KV type
+// DT (kStampWorkgroups x 8 words of 64 bits, tsv_device.h) to host memory.
+template <int DT>
+hipError_t read_phase_stamps_t(void* host, size_t bytes);
 template <int DT>
 hipError_t step_t(const Dims& d, const StepPlan& plan, const float* q, const void* k_new,
                   const void* v_new, void* k_pool, void* v_pool, void* meta, const int32_t* bt,
