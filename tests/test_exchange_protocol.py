@@ -233,4 +233,4 @@ def test_model_matches_the_source():
     after_ex = step[i_ex:]
     assert re.search(r"if \(s_flag\) \{\s*for \(int p = tid; p < n; p \+= NT\)\s*"
                      r"if \(\(p / PB\) % S != split\) s_key\[p\] = ld_dev\(krow \+ p\);", after_ex)
-    assert re.search(r"if \(!s_flag\) return;\s*merge_row<", step[i_fin:])
+    assert re.search(r"if \(!s_flag\) \{[^}]*return;\s*\}\s*merge_row<", step[i_fin:])
