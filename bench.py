@@ -70,14 +70,14 @@ KERNEL_SOURCES = [os.path.join(ROOT, "query_aware_sparse_bbox_amd", "csrc", f)
 # hex digits).  Keys: configuration, or configuration:KV type when the
 # configuration's KV type is overridden.
 TRAFFIC = {
-    "tinyllama": {"source": "928756b5314509d8", "bytes_per_step": 23229112, "read": 22233784, "written": 995328},
-    "tiny": {"source": "928756b5314509d8", "bytes_per_step": 598392, "read": 597112, "written": 1280},
-    "gpt2": {"source": "928756b5314509d8", "bytes_per_step": 42732534, "read": 42552310, "written": 180224},
-    "llama_long": {"source": "928756b5314509d8", "bytes_per_step": 202323770, "read": 202184506, "written": 139264},
-    "ragged": {"source": "928756b5314509d8", "bytes_per_step": 403169199, "read": 401673338, "written": 1495861},
-    "tinyllama:fp8e4m3": {"source": "928756b5314509d8", "bytes_per_step": 12806429, "read": 11811101, "written": 995328},
-    "llama_long:fp8e4m3": {"source": "928756b5314509d8", "bytes_per_step": 101613955, "read": 101474691, "written": 139264},
-    "ragged:fp8e4m3": {"source": "928756b5314509d8", "bytes_per_step": 204417300, "read": 203062955, "written": 1354344},
+    "tinyllama": {"source": "5edd5a04acb29ce9", "bytes_per_step": 23205472, "read": 22210144, "written": 995328},
+    "tiny": {"source": "5edd5a04acb29ce9", "bytes_per_step": 568563, "read": 567283, "written": 1280},
+    "gpt2": {"source": "5edd5a04acb29ce9", "bytes_per_step": 42690142, "read": 42509918, "written": 180224},
+    "llama_long": {"source": "5edd5a04acb29ce9", "bytes_per_step": 202258207, "read": 202118943, "written": 139264},
+    "ragged": {"source": "5edd5a04acb29ce9", "bytes_per_step": 403271685, "read": 401783268, "written": 1488417},
+    "tinyllama:fp8e4m3": {"source": "5edd5a04acb29ce9", "bytes_per_step": 12796314, "read": 11800986, "written": 995328},
+    "llama_long:fp8e4m3": {"source": "5edd5a04acb29ce9", "bytes_per_step": 101709497, "read": 101570233, "written": 139264},
+    "ragged:fp8e4m3": {"source": "5edd5a04acb29ce9", "bytes_per_step": 204536095, "read": 203188334, "written": 1347761},
 }
 
 
