@@ -214,6 +214,9 @@ def parse():
                     help="host threads of the threaded oracle run (0: the CPUs this "
                          "process may use, at most 16)")
     ap.add_argument("--eager", action="store_true", help="launch steps one by one (no graph)")
+    ap.add_argument("--settle-ms", type=float, default=50.0,
+                    help="untimed steps for about this long before the warm-up steps, so that "
+                         "the GPU's clocks have settled under this load (0: none)")
     ap.add_argument("--no-quality", action="store_true",
                     help="skip the selection-quality / dense-speedup report")
     ap.add_argument("--copy-calibrate", type=float, default=0.0, metavar="MB",
@@ -440,9 +443,19 @@ def main():
         assert torch.equal(first.out.view(torch.int32), ref_out.view(torch.int32)), \
             "graph replay changed the output"
 
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    settle = 0
+    if args.settle_ms > 0:
+        t0.record(stream)
+        run(R)
+        t1.record(stream)
+        torch.cuda.synchronize()
+        settle = min(200000, max(R, math.ceil(args.settle_ms / max(t0.elapsed_time(t1) / R,
+                                                                     1e-4))))
+        run(settle)
+        torch.cuda.synchronize()
     run(Wm)
     torch.cuda.synchronize()
-    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     wall0 = time.perf_counter()
     t0.record(stream)
     run(K)
@@ -579,6 +592,7 @@ def main():
                    W.DTYPE_NAMES[sh.kv_dtype], "batch": B, "q_heads": Hq, "kv_heads": Hkv,
                    "head_dim": D, "page_size": sh.page_size, "k_max": k_max,
                    "rotating_instances": R, "graph": not args.eager,
+                   "untimed_settle_steps": settle,
                    "selection": {"n_sink": n_sink, "n_recent": args.recent,
                                  "group_agg": args.group_agg}},
         "step_algorithmic_bytes": nb["total"],
