@@ -510,6 +510,49 @@ def test_split_rows_exchange_fallback_bit_identical():
     assert not a["sync"].any() and not b["sync"].any()
 
 
+@pytest.mark.parametrize("name,kw", [("tinyllama", dict(batch=4, context=4096)),
+                                     ("gpt2", dict(batch=12, context=900))])
+def test_phase_stamps_of_the_testing_library(name, kw):
+    """The testing library's step kernels stamp every workgroup's phases: for
+    each workgroup of the last step the stamps are non-decreasing from start
+    to end, the recorded (row, split) pairs cover every row's splits once,
+    and the results equal the library proper's bit for bit."""
+    import query_aware_sparse_bbox_amd as T
+
+    t = T.testing_library()
+    wl = W.make(name, **kw)
+    sh = wl.shape
+    say(f"[case] phase stamps {name} {kw}")
+    a = gpu_run(wl)
+    b = gpu_run(wl, lib=t)
+    st = t.tsv_debug_phase_stamps(sh.kv_dtype).astype(np.int64)
+    for k in ("sel", "cnt"):
+        assert np.array_equal(a[k], b[k]), k
+    for k in ("scores", "out"):
+        assert np.array_equal(a[k].view(np.uint32), b[k].view(np.uint32)), k
+    units = sh.batch * sh.num_kv_heads
+    S = T.tsv_decode_step_launches(sh, wl.k_max, bool(wl.steps))  # 1: one launch
+    assert S == 1
+    ids = st[:, 6]
+    rows, splits = ids >> 32, ids & 0xffffffff
+    # workgroups of this launch: stamped within 1 ms of its latest start (the
+    # array keeps earlier launches' stamps in rows this grid does not reach)
+    live = ((st[:, 5] >= st[:, 0]) & (st[:, 0] >= st[:, 0].max() - 100_000) &
+            (rows < units))
+    st, rows, splits = st[live], rows[live], splits[live]
+    pairs = set(zip(rows.tolist(), splits.tolist()))
+    assert len(pairs) == len(rows), "a (row, split) stamped twice"
+    assert set(rows.tolist()) == set(range(units))
+    nsplit = max(splits) + 1
+    assert len(rows) == units * nsplit
+    # start <= staged <= scored <= selected <= decoded <= end (decoded is only
+    # stamped by workgroups that had tokens)
+    for i0, i1 in ((0, 1), (1, 2), (2, 3), (3, 5)):
+        assert (st[:, i1] >= st[:, i0]).all(), (i0, i1)
+    span_us = (st[:, 5].max() - st[:, 0].min()) / 100.0
+    assert 0 < span_us < 10000, span_us
+
+
 def test_split_rows_workspace_shared_by_shapes():
     """One zero-filled workspace serves split-row steps of different shapes (and
     a phased call in between); each call leaves the counter prefix at zero."""
