@@ -309,7 +309,7 @@ def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(f"bench.py: --gpus {args.gpus} / WORLD_SIZE {world} requested, but this build "
+        print(f"bench.py: --gpus {args.gpus} / WORLD_SIZE {world} requested, but this library "
               "runs the decode step on one GPU only (no multi-GPU path); run with --gpus 1.",
               file=sys.stderr)
         sys.exit(2)
