@@ -253,6 +253,62 @@ int tsv_decode_step_ex(const tsv_shape* shape, const float* q, const void* k_new
                        int32_t* sel_count, float* scores_out, float* out,
                        void* workspace, size_t workspace_bytes, void* stream);
 
+/* Longest-first row schedule of the one-launch step (abstract: scoring,
+   sparse memory access and masked attention fused into one pass; method
+   details, key design: the sparse accesses are organised around what the
+   hardware does well).  The step's rows ((sequence, KV head) pairs) differ
+   in work by the number of pages they score and keep; a serving loop knows
+   every sequence's length on the host, and from those lengths this call
+   ranks the rows by the bytes their step reads (every page box, the keys and
+   values of a full budget of full pages, the block-table row) and writes the
+   order in which the workgroups of tsv_decode_step_scheduled take them.
+   The GPU starts workgroups in index order, which makes the order a
+   longest-processing-time-first queue: the first num_cus * per_cu
+   workgroups are resident together (workgroup j*num_cus + c on the same CU
+   as workgroup c), and the heaviest rows fill them, each going to the CU
+   with the least weight so far among those with fewer than per_cu rows (so
+   heavy rows share a CU with light ones, or keep it to themselves while
+   light ones share); entries of -1 are idle workgroups in the slots a CU
+   does not use.  Rows after those follow heaviest first and start as
+   earlier workgroups finish.
+   seq_lens [B] (len_b as for the step), k_per_seq [B] (nullable, as for the
+   step) and row_order are HOST arrays; the call makes no HIP call.  num_cus
+   and per_cu as tsv_step_residency reports them (>= 1).  *order_len
+   receives the order's length, at most max(B*Hkv, num_cus*per_cu); with
+   row_order NULL only the length is computed, otherwise `capacity` entries
+   must hold it (TSV_ERR_INVALID_ARG if they do not).  The order only decides which
+   workgroup runs which row and when: the step's results do not depend on
+   it. */
+int tsv_schedule_rows(const tsv_shape* shape, int32_t k_max, const int32_t* seq_lens,
+                      const int32_t* k_per_seq, int32_t num_cus, int32_t per_cu,
+                      int32_t* row_order, int32_t capacity, int32_t* order_len);
+
+/* The current device's CU count, and how many workgroups of this shape's
+   one-launch step one CU holds at once.  *per_cu = 0 when the step of this
+   shape takes no row order (it needs several launches, or it spreads each
+   row over several workgroups, which happens when B*Hkv <= 128).  Queries
+   the HIP runtime; enqueues nothing.  TSV_ERR_HIP when the queries fail. */
+int tsv_step_residency(const tsv_shape* shape, int32_t k_max, int32_t* num_cus,
+                       int32_t* per_cu);
+
+/* tsv_decode_step_ex whose workgroups take their rows from row_order: a
+   DEVICE array of order_len int32 (4-byte aligned), order_len in
+   [B*Hkv, 2^24]; workgroup w handles row row_order[w] = b*Hkv + h, and
+   entries outside [0, B*Hkv) are idle workgroups.  The order must list every
+   row exactly once, as tsv_schedule_rows writes it: a row left out is not
+   computed (its outputs keep their old contents), a row listed twice is
+   computed twice.  It is used where tsv_step_residency reports per_cu > 0
+   and ignored otherwise; row_order = NULL is tsv_decode_step_ex.  Results
+   are bitwise those of tsv_decode_step_ex. */
+int tsv_decode_step_scheduled(const tsv_shape* shape, const float* q, const void* k_new,
+                              const void* v_new, void* k_pool, void* v_pool, void* meta,
+                              const int32_t* block_table, const int32_t* seq_lens,
+                              int32_t k_max, const int32_t* k_per_seq, int32_t n_sink,
+                              const tsv_select_opts* opts, const int32_t* row_order,
+                              int32_t order_len, float scale, int32_t* sel,
+                              int32_t* sel_count, float* scores_out, float* out,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
 /* tsv_decode_step_ex for callers that cannot allocate device memory: code
    under HIP graph capture that may not call hipMalloc, tight serving loops,
    harnesses that forbid allocation.  There is no workspace argument: the

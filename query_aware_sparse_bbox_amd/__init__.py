@@ -35,7 +35,8 @@ TSV_AGG_MAX, TSV_AGG_SUM = 0, 1
 EXPORTS = ("tsv_version", "tsv_status_string", "tsv_meta_bytes", "tsv_workspace_bytes",
            "tsv_decode_step_launches", "tsv_meta_build", "tsv_meta_append",
            "tsv_select_pages", "tsv_sparse_decode", "tsv_decode_step",
-           "tsv_select_pages_ex", "tsv_decode_step_ex", "tsv_decode_step_noalloc")
+           "tsv_select_pages_ex", "tsv_decode_step_ex", "tsv_decode_step_noalloc",
+           "tsv_schedule_rows", "tsv_step_residency", "tsv_decode_step_scheduled")
 # declared in include/tsv_testing.h, exported by the testing library only
 TEST_EXPORTS = ("tsv_debug_exchange_polls", "tsv_debug_phase_stamps")
 
@@ -86,6 +87,10 @@ _SIGS = {
                             _P, _P, _P, _Z, _P], ctypes.c_int),
     "tsv_decode_step_noalloc": ([_SP, _P, _P, _P, _P, _P, _P, _P, _P, _I, _P, _I, _OP, _F, _P,
                                  _P, _P, _P, _P], ctypes.c_int),
+    "tsv_schedule_rows": ([_SP, _I, _P, _P, _I, _I, _P, _I, _P], ctypes.c_int),
+    "tsv_step_residency": ([_SP, _I, _P, _P], ctypes.c_int),
+    "tsv_decode_step_scheduled": ([_SP, _P, _P, _P, _P, _P, _P, _P, _P, _I, _P, _I, _OP, _P, _I,
+                                   _F, _P, _P, _P, _P, _P, _Z, _P], ctypes.c_int),
 }
 _TEST_SIGS = {"tsv_debug_exchange_polls": ([_I], ctypes.c_int),
               "tsv_debug_phase_stamps": ([_I, ctypes.c_void_p, ctypes.c_size_t], ctypes.c_int)}
@@ -243,6 +248,44 @@ class Library:
                    _opts(n_recent, group_agg), float(scale), _ptr(sel), _ptr(sel_count),
                    _ptr(scores_out), _ptr(out), _stream(stream))
 
+    def tsv_step_residency(self, shape, k_max: int):
+        """(num_cus, per_cu) of the current device for this shape's step."""
+        cus, per = ctypes.c_int32(0), ctypes.c_int32(0)
+        self._call("tsv_step_residency", ctypes.byref(Shape.of(shape)), int(k_max),
+                   ctypes.byref(cus), ctypes.byref(per))
+        return cus.value, per.value
+
+    def tsv_schedule_rows(self, shape, k_max, seq_lens, k_per_seq, num_cus, per_cu):
+        """The row order (int32 numpy array) for host arrays seq_lens and
+        k_per_seq (None allowed) of B entries each."""
+        import numpy as np
+
+        sl = np.ascontiguousarray(seq_lens, dtype=np.int32)
+        kp = None if k_per_seq is None else np.ascontiguousarray(k_per_seq, dtype=np.int32)
+        if sl.shape != (int(shape.batch),) or (kp is not None and kp.shape != sl.shape):
+            raise ValueError("seq_lens / k_per_seq must hold one entry per sequence")
+        n = ctypes.c_int32(0)
+        args = (ctypes.byref(Shape.of(shape)), int(k_max), ctypes.c_void_p(sl.ctypes.data),
+                None if kp is None else ctypes.c_void_p(kp.ctypes.data), int(num_cus),
+                int(per_cu))
+        self._call("tsv_schedule_rows", *args, None, 0, ctypes.byref(n))
+        order = np.empty(n.value, dtype=np.int32)
+        self._call("tsv_schedule_rows", *args, ctypes.c_void_p(order.ctypes.data), order.size,
+                   ctypes.byref(n))
+        return order
+
+    def tsv_decode_step_scheduled(self, shape, q, k_new, v_new, k_pool, v_pool, meta,
+                                  block_table, seq_lens, k_max, k_per_seq, n_sink, n_recent,
+                                  group_agg, row_order, scale, sel, sel_count, scores_out, out,
+                                  workspace, stream=None):
+        self._call("tsv_decode_step_scheduled", ctypes.byref(Shape.of(shape)), _ptr(q),
+                   _ptr(k_new), _ptr(v_new), _ptr(k_pool), _ptr(v_pool), _ptr(meta),
+                   _ptr(block_table), _ptr(seq_lens), int(k_max), _ptr(k_per_seq), int(n_sink),
+                   _opts(n_recent, group_agg), _ptr(row_order),
+                   0 if row_order is None else row_order.numel(), float(scale), _ptr(sel),
+                   _ptr(sel_count), _ptr(scores_out), _ptr(out), _ptr(workspace),
+                   _nbytes(workspace), _stream(stream))
+
 
 # the library proper; the module-level functions are its methods
 _default = Library(LIB_PATH)
@@ -275,3 +318,6 @@ tsv_decode_step = _default.tsv_decode_step
 tsv_select_pages_ex = _default.tsv_select_pages_ex
 tsv_decode_step_ex = _default.tsv_decode_step_ex
 tsv_decode_step_noalloc = _default.tsv_decode_step_noalloc
+tsv_schedule_rows = _default.tsv_schedule_rows
+tsv_step_residency = _default.tsv_step_residency
+tsv_decode_step_scheduled = _default.tsv_decode_step_scheduled

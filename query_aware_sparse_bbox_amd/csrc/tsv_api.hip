@@ -7,7 +7,9 @@
 // tsv_testing.h.
 #include <stdint.h>
 
+#include <algorithm>
 #include <atomic>
+#include <vector>
 
 #include "../../include/tsv.h"
 #include "tsv_launch.h"
@@ -107,6 +109,9 @@ int check_decode_args(const Dims& d, const float* q, const void* k_pool,
 }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? TSV_OK : TSV_ERR_HIP; }
+
+// Longest row order tsv_decode_step_scheduled accepts (workgroups per launch).
+constexpr int32_t kMaxOrderLen = 1 << 24;
 
 #ifdef TSV_TEST_HOOKS
 // Polls of a split row's score exchange, settable by tsv_debug_exchange_polls.
@@ -274,13 +279,15 @@ int run_step(const Dims& d, const tsv::SelectPolicy& pol, const float* q, const 
              const void* v_new, void* k_pool, void* v_pool, void* meta,
              const int32_t* block_table, const int32_t* seq_lens, int32_t k_max,
              const int32_t* k_per_seq, float scale, int32_t* sel, int32_t* sel_count,
-             float* scores_out, float* out, void* workspace, hipStream_t s) {
+             float* scores_out, float* out, void* workspace, hipStream_t s,
+             const int32_t* row_order = nullptr, int32_t order_len = 0) {
   tsv::Workspace ws;
   tsv::workspace_layout(d, k_max, workspace, &ws);
   if (tsv::step_fits(d))  // every row's whole step in its own workgroup(s)
     return hip_status(tsv::launch_step(d, exchange_polls(), q, k_new, v_new, k_pool, v_pool,
                                        meta, block_table, seq_lens, k_max, k_per_seq, pol,
-                                       scale, sel, sel_count, scores_out, ws, out, s));
+                                       scale, row_order, order_len, sel, sel_count,
+                                       scores_out, ws, out, s));
   int rc;
   if (k_new) {
     rc = hip_status(tsv::launch_meta_append(d, k_new, v_new, k_pool, v_pool, meta,
@@ -337,6 +344,80 @@ int tsv_decode_step_noalloc(const tsv_shape* shape, const float* q, const void* 
   if (rc) return rc;
   return run_step(d, pol, q, k_new, v_new, k_pool, v_pool, meta, block_table, seq_lens, k_max,
                   k_per_seq, scale, sel, sel_count, scores_out, out, scratch, s);
+}
+
+int tsv_step_residency(const tsv_shape* shape, int32_t k_max, int32_t* num_cus,
+                       int32_t* per_cu) {
+  Dims d;
+  int rc = check_shape(shape, &d);
+  if (rc) return rc;
+  if (k_max < 1 || !num_cus || !per_cu) return TSV_ERR_INVALID_ARG;
+  int dev = 0, cus = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return TSV_ERR_HIP;
+  if (tsv::step_fits(d) && tsv::step_splits_for(d, k_max) == 1 &&
+      tsv::step_per_cu(d, k_max, &n) != hipSuccess)
+    return TSV_ERR_HIP;
+  *num_cus = cus;
+  *per_cu = n;
+  return TSV_OK;
+}
+
+int tsv_schedule_rows(const tsv_shape* shape, int32_t k_max, const int32_t* seq_lens,
+                      const int32_t* k_per_seq, int32_t num_cus, int32_t per_cu,
+                      int32_t* row_order, int32_t capacity, int32_t* order_len) {
+  Dims d;
+  int rc = check_shape(shape, &d);
+  if (rc) return rc;
+  if (k_max < 1 || !seq_lens || !order_len || num_cus < 1 || per_cu < 1 || capacity < 0 ||
+      (capacity > 0 && !row_order))
+    return TSV_ERR_INVALID_ARG;
+  if ((int64_t)d.B * d.Hkv > INT32_MAX / 2) return TSV_ERR_UNSUPPORTED;
+  const int units = d.B * d.Hkv;
+  // weight of a row: the bytes its step reads -- every page box, the kept
+  // pages' keys and values (a full budget of full pages), the block-table row
+  const double e = tsv::kv_bytes(d.dt), box = 2.0 * d.D * e, page = 2.0 * d.D * e * d.P;
+  std::vector<double> w(units);
+  for (int b = 0; b < d.B; ++b) {
+    const long len_b = std::min<long>(std::max(seq_lens[b], 0), (long)d.MP * d.P);
+    const long n = (len_b + d.P - 1) / d.P;
+    const long kb = std::min<long>(
+        n, std::max(1, std::min(k_per_seq ? k_per_seq[b] : k_max, k_max)));
+    const double wb = box * n + page * kb + 4.0 * n;
+    for (int h = 0; h < d.Hkv; ++h) w[(size_t)b * d.Hkv + h] = wb;
+  }
+  long len = 0;
+  tsv::schedule_rows(w.data(), units, num_cus, per_cu, nullptr, 0, &len);
+  if (len > INT32_MAX) return TSV_ERR_UNSUPPORTED;
+  *order_len = (int32_t)len;
+  if (row_order == nullptr) return TSV_OK;  // length query
+  if (len > capacity) return TSV_ERR_INVALID_ARG;
+  tsv::schedule_rows(w.data(), units, num_cus, per_cu, row_order, capacity, &len);
+  return TSV_OK;
+}
+
+int tsv_decode_step_scheduled(const tsv_shape* shape, const float* q, const void* k_new,
+                              const void* v_new, void* k_pool, void* v_pool, void* meta,
+                              const int32_t* block_table, const int32_t* seq_lens,
+                              int32_t k_max, const int32_t* k_per_seq, int32_t n_sink,
+                              const tsv_select_opts* opts, const int32_t* row_order,
+                              int32_t order_len, float scale, int32_t* sel,
+                              int32_t* sel_count, float* scores_out, float* out,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  Dims d;
+  tsv::SelectPolicy pol;
+  int rc = check_step(shape, q, k_new, v_new, k_pool, v_pool, meta, block_table, seq_lens,
+                      k_max, n_sink, opts, sel, sel_count, out, &d, &pol);
+  if (rc) return rc;
+  rc = check_workspace(d, k_max, workspace, workspace_bytes);
+  if (rc) return rc;
+  if (row_order != nullptr &&
+      (!aligned(row_order, 4) || order_len < (int64_t)d.B * d.Hkv || order_len > kMaxOrderLen))
+    return TSV_ERR_INVALID_ARG;
+  return run_step(d, pol, q, k_new, v_new, k_pool, v_pool, meta, block_table, seq_lens, k_max,
+                  k_per_seq, scale, sel, sel_count, scores_out, out, workspace,
+                  (hipStream_t)stream, row_order, row_order ? order_len : 0);
 }
 
 int tsv_decode_step(const tsv_shape* shape, const float* q, const void* k_new,

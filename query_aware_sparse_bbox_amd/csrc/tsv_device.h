@@ -1909,9 +1909,10 @@ __global__ __launch_bounds__(NT, (step_min_blocks<DT, D, G, NT>())) void k_step(
     void* __restrict__ meta, const int32_t* __restrict__ bt,
     const int32_t* __restrict__ seq_lens, int units, int Hq, int Hkv, int log2P, int MP,
     int NP, int k_max, const int32_t* __restrict__ k_per_seq, SelectPolicy pol, float qscale,
-    int S, int polls, int32_t* __restrict__ sel, int32_t* __restrict__ sel_count,
-    float* __restrict__ scores_out, uint32_t* __restrict__ sync, uint32_t* __restrict__ keys,
-    float* __restrict__ partials, float* __restrict__ out) {
+    int S, int polls, const int32_t* __restrict__ order, int32_t* __restrict__ sel,
+    int32_t* __restrict__ sel_count, float* __restrict__ scores_out,
+    uint32_t* __restrict__ sync, uint32_t* __restrict__ keys, float* __restrict__ partials,
+    float* __restrict__ out) {
   constexpr int NW = NT / kWave;
   constexpr bool MF = step_uses_mfma<DT, D, G>();
   constexpr int PB = ScoreCfg<DT, D, G, NT>::PB;
@@ -1925,11 +1926,21 @@ __global__ __launch_bounds__(NT, (step_min_blocks<DT, D, G, NT>())) void k_step(
   __shared__ int s_flag;
 
   // workgroup -> (row, split): the S splits of a row share blockIdx mod 8,
-  // i.e. one XCD and its L2, which then serves the keys they exchange
+  // i.e. one XCD and its L2, which then serves the keys they exchange.  A
+  // scheduled launch (S = 1) takes its row from the caller's order instead;
+  // entries outside [0, units) leave their workgroup idle.
   TSV_STAMP(0);
-  const int grp = blockIdx.x / (8 * S), within = blockIdx.x - grp * 8 * S;
-  const int split = within >> 3, unit = grp * 8 + (within & 7);
-  if (unit >= units) return;
+  int unit, split;
+  if (order != nullptr) {
+    unit = order[blockIdx.x];
+    split = 0;
+    if ((unsigned)unit >= (unsigned)units) return;
+  } else {
+    const int grp = blockIdx.x / (8 * S), within = blockIdx.x - grp * 8 * S;
+    split = within >> 3;
+    unit = grp * 8 + (within & 7);
+    if (unit >= units) return;
+  }
   TSV_STAMP_VALUE(6, ((unsigned long long)unit << 32) | (unsigned)split);
   const int b = unit / Hkv, h = unit - b * Hkv;
   const int tid = threadIdx.x;

@@ -2,7 +2,10 @@
 // the one-launch step's workgroup shape, and dispatch to the launchers of the
 // call's KV type.  No device code.
 #include <algorithm>
+#include <numeric>
+#include <queue>
 #include <type_traits>
+#include <vector>
 
 #include "tsv_launch.h"
 
@@ -170,16 +173,72 @@ hipError_t launch_step(const Dims& d, int polls, const float* q, const void* k_n
                        const void* v_new, void* k_pool, void* v_pool, void* meta,
                        const int32_t* bt, const int32_t* seq_lens, int k_max,
                        const int32_t* k_per_seq, const SelectPolicy& pol, float scale,
-                       int32_t* sel, int32_t* sel_count, float* scores_out,
-                       const Workspace& ws, float* out, hipStream_t s) {
+                       const int32_t* order, int order_len, int32_t* sel,
+                       int32_t* sel_count, float* scores_out, const Workspace& ws,
+                       float* out, hipStream_t s) {
   const StepPlan plan = plan_step(d, k_max, polls);
   if (plan.lds > kStepMaxLds) return hipErrorInvalidValue;
   clear_stale_error();
   return by_dtype(d.dt, [&](auto DT) {
     return step_t<decltype(DT)::value>(d, plan, q, k_new, v_new, k_pool, v_pool, meta, bt,
-                                       seq_lens, k_max, k_per_seq, pol, scale, sel, sel_count,
-                                       scores_out, ws, out, s);
+                                       seq_lens, k_max, k_per_seq, pol, scale, order,
+                                       order_len, sel, sel_count, scores_out, ws, out, s);
   });
+}
+
+int step_splits_for(const Dims& d, int k_max) { return step_splits(d, k_max); }
+
+hipError_t step_per_cu(const Dims& d, int k_max, int* per_cu) {
+  const StepPlan plan = plan_step(d, k_max, kDefaultExchangePolls);
+  return by_dtype(d.dt, [&](auto DT) {
+    return step_per_cu_t<decltype(DT)::value>(d, plan, per_cu);
+  });
+}
+
+// Longest-processing-time-first list scheduling with the workgroup
+// dispatcher as the queue.  The dispatcher starts workgroups in index order:
+// the first num_cus*per_cu of them are resident at once, workgroup
+// j*num_cus + c of that first wave on the same CU as workgroup c (measured on
+// MI355X), and every later one starts when a resident one ends.  So the
+// heaviest rows make the first wave: each, heaviest first, goes to the CU
+// with the least weight so far among those holding fewer than per_cu rows
+// (the second row of a CU pairs heavy rows with light ones; with room for
+// three, a heavy row may keep its CU to itself while light rows share
+// one), and a CU's k-th row is its workgroup of round k.  Slots a CU does not
+// use are idle workgroups (-1), so that every workgroup of the wave still
+// lands on its CU.  Rows after the first wave follow in descending weight:
+// each takes the next slot to free up.
+bool schedule_rows(const double* w, int units, int num_cus, int per_cu, int32_t* order,
+                   long cap, long* len) {
+  const long C = std::max(1, num_cus), m = std::max(1, per_cu);
+  const long first = std::min<long>(units, C * m);
+  std::vector<int> rank(units);
+  std::iota(rank.begin(), rank.end(), 0);
+  std::stable_sort(rank.begin(), rank.end(), [&](int a, int b) { return w[a] > w[b]; });
+  // the first wave: the CU with the least weight among those with a free
+  // slot (equal weights: lower CU first) takes the next row
+  using Slot = std::pair<double, long>;  // (weight so far, CU)
+  std::priority_queue<Slot, std::vector<Slot>, std::greater<Slot>> free_cus;
+  for (long c = 0; c < std::min(C, first); ++c) free_cus.push({0.0, c});
+  std::vector<int> count(std::min(C, first), 0);
+  std::vector<long> where(first);  // first-wave slot of rank r: round * C + CU
+  long wave = 0;  // workgroups of the first wave (idle ones at its end left out
+                 // when no rows follow)
+  for (long r = 0; r < first; ++r) {
+    const Slot s = free_cus.top();
+    free_cus.pop();
+    where[r] = count[s.second] * C + s.second;
+    wave = std::max(wave, where[r] + 1);
+    if (++count[s.second] < m) free_cus.push({s.first + w[rank[r]], s.second});
+  }
+  if (units > first) wave = (wave + C - 1) / C * C;
+  *len = wave + (units - first);
+  if (order == nullptr) return true;
+  if (*len > cap) return false;
+  std::fill(order, order + wave, -1);
+  for (long r = 0; r < first; ++r) order[where[r]] = rank[r];
+  for (long r = first; r < units; ++r) order[wave + (r - first)] = rank[r];
+  return true;
 }
 
 }  // namespace tsv

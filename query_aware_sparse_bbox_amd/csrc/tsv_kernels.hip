@@ -147,21 +147,37 @@ template <int dt>
 hipError_t step_t(const Dims& d, const StepPlan& plan, const float* q, const void* k_new,
                   const void* v_new, void* k_pool, void* v_pool, void* meta, const int32_t* bt,
                   const int32_t* seq_lens, int k_max, const int32_t* k_per_seq,
-                  const SelectPolicy& pol, float scale, int32_t* sel, int32_t* sel_count,
-                  float* scores_out, const Workspace& ws, float* out, hipStream_t s) {
+                  const SelectPolicy& pol, float scale, const int32_t* order, int order_len,
+                  int32_t* sel, int32_t* sel_count, float* scores_out, const Workspace& ws,
+                  float* out, hipStream_t s) {
   const int log2P = ilog2(d.P);
   const float qscale = scale * kLog2e;  // exp2 in the softmax
   const int units = d.B * d.Hkv, S = plan.S;
-  const dim3 grid((units + 7) / 8 * 8 * S);
+  // a row order replaces the workgroup -> row mapping of one-workgroup rows
+  const int32_t* ord = S == 1 ? order : nullptr;
+  const dim3 grid(ord ? order_len : (units + 7) / 8 * 8 * S);
   return by_d_g(d, [&](auto HD, auto GG) -> hipError_t {
     constexpr int hd = decltype(HD)::value, g = decltype(GG)::value;
     auto go = [&](auto NTc) -> hipError_t {
       constexpr int nthr = decltype(NTc)::value;
       hipLaunchKernelGGL((k_step<dt, hd, g, nthr>), grid, dim3(nthr), plan.lds, s, q, k_new,
                          v_new, k_pool, v_pool, meta, bt, seq_lens, units, d.Hq, d.Hkv, log2P,
-                         d.MP, d.NP, k_max, k_per_seq, pol, qscale, S, plan.polls, sel,
+                         d.MP, d.NP, k_max, k_per_seq, pol, qscale, S, plan.polls, ord, sel,
                          sel_count, scores_out, ws.sync, ws.keys, ws.partials, out);
       return hipGetLastError();
+    };
+    return plan.nt == 256 ? go(IC<256>{}) : go(IC<512>{});
+  });
+}
+
+template <int dt>
+hipError_t step_per_cu_t(const Dims& d, const StepPlan& plan, int* per_cu) {
+  return by_d_g(d, [&](auto HD, auto GG) -> hipError_t {
+    constexpr int hd = decltype(HD)::value, g = decltype(GG)::value;
+    auto go = [&](auto NTc) -> hipError_t {
+      constexpr int nthr = decltype(NTc)::value;
+      return hipOccupancyMaxActiveBlocksPerMultiprocessor(
+          per_cu, reinterpret_cast<const void*>(&k_step<dt, hd, g, nthr>), nthr, plan.lds);
     };
     return plan.nt == 256 ? go(IC<256>{}) : go(IC<512>{});
   });
@@ -192,8 +208,9 @@ hipError_t read_phase_stamps_t<TSV_DT>(void* host, size_t bytes) {
 template hipError_t step_t<TSV_DT>(const Dims&, const StepPlan&, const float*, const void*,
                                    const void*, void*, void*, void*, const int32_t*,
                                    const int32_t*, int, const int32_t*, const SelectPolicy&,
-                                   float, int32_t*, int32_t*, float*, const Workspace&, float*,
-                                   hipStream_t);
+                                   float, const int32_t*, int, int32_t*, int32_t*, float*,
+                                   const Workspace&, float*, hipStream_t);
+template hipError_t step_per_cu_t<TSV_DT>(const Dims&, const StepPlan&, int*);
 #else
 #error "unknown TSV_PART"
 #endif

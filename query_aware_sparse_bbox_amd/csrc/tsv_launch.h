@@ -118,12 +118,18 @@ hipError_t decode_t(const Dims& d, const DecodePlan& plan, const float* q, const
 // DT (kStampWorkgroups x 8 words of 64 bits, tsv_device.h) to host memory.
 template <int DT>
 hipError_t read_phase_stamps_t(void* host, size_t bytes);
+// order (nullable, device): row of each workgroup of a launch with one
+// workgroup per row (plan.S == 1), order_len workgroups; unused otherwise.
 template <int DT>
 hipError_t step_t(const Dims& d, const StepPlan& plan, const float* q, const void* k_new,
                   const void* v_new, void* k_pool, void* v_pool, void* meta, const int32_t* bt,
                   const int32_t* seq_lens, int k_max, const int32_t* k_per_seq,
-                  const SelectPolicy& pol, float scale, int32_t* sel, int32_t* sel_count,
-                  float* scores_out, const Workspace& ws, float* out, hipStream_t s);
+                  const SelectPolicy& pol, float scale, const int32_t* order, int order_len,
+                  int32_t* sel, int32_t* sel_count, float* scores_out, const Workspace& ws,
+                  float* out, hipStream_t s);
+// Workgroups of the step kernel for d / plan that one CU holds at once.
+template <int DT>
+hipError_t step_per_cu_t(const Dims& d, const StepPlan& plan, int* per_cu);
 
 // Dispatch by KV type (tsv_host.hip).
 hipError_t launch_meta_build(const Dims& d, const void* k_pool, void* meta,
@@ -149,11 +155,25 @@ hipError_t launch_decode(const Dims& d, const float* q, const void* k_pool,
 // workgroups that share the row's scoring, each select the whole row and
 // decode a share of it; the last one to finish merges the shares): [append]
 // -> score -> top-K -> decode, one launch.  Usable when step_fits(d).
+// With `order` non-null and plan.S == 1, workgroup w of order_len handles
+// row order[w] (entries outside [0, B*Hkv) idle).
 hipError_t launch_step(const Dims& d, int polls, const float* q, const void* k_new,
                        const void* v_new, void* k_pool, void* v_pool, void* meta,
                        const int32_t* bt, const int32_t* seq_lens, int k_max,
                        const int32_t* k_per_seq, const SelectPolicy& pol, float scale,
-                       int32_t* sel, int32_t* sel_count, float* scores_out,
-                       const Workspace& ws, float* out, hipStream_t s);
+                       const int32_t* order, int order_len, int32_t* sel,
+                       int32_t* sel_count, float* scores_out, const Workspace& ws,
+                       float* out, hipStream_t s);
+// Workgroups per row of the one-launch step (1: a row order applies).
+int step_splits_for(const Dims& d, int k_max);
+// Workgroups of the one-launch step one CU holds at once.
+hipError_t step_per_cu(const Dims& d, int k_max, int* per_cu);
+
+// Longest-first row order for the one-launch step (host only, no HIP call).
+// w[u] is row u's weight; num_cus CUs hold per_cu workgroups each.  Writes
+// the order's length to *len and, when order != null and *len <= cap, the
+// order itself (-1 = an idle workgroup).  Returns false when cap is too small.
+bool schedule_rows(const double* w, int units, int num_cus, int per_cu, int32_t* order,
+                   long cap, long* len);
 
 }  // namespace tsv

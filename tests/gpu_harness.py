@@ -45,13 +45,33 @@ def oracle_run(wl, k_max=None, k_per_seq="wl", n_sink=None, step=0, n_recent=0, 
     return dict(meta=meta, sel=sel, cnt=cnt, scores=sc, out=out, k_pool=kp, v_pool=vp)
 
 
+def host_lengths(wl, k_max=None, k_per_seq="wl", step=0):
+    """Host copies of the step's sequence lengths and budgets."""
+    lens = wl.steps[step].seq_lens if wl.steps else wl.seq_lens
+    if isinstance(k_per_seq, str):
+        k_per_seq = wl.steps[step].k_per_seq if wl.steps else wl.k_per_seq
+    return lens, k_per_seq
+
+
+def lpt_order(wl, k_max=None, k_per_seq="wl", step=0, lib=None):
+    """The library's longest-first row order for this step on this GPU."""
+    import query_aware_sparse_bbox_amd as T_mod
+    T = lib if lib is not None else T_mod
+    k_max = wl.k_max if k_max is None else k_max
+    cus, per = T.tsv_step_residency(wl.shape, k_max)
+    lens, kps = host_lengths(wl, k_max, k_per_seq, step)
+    return T.tsv_schedule_rows(wl.shape, k_max, lens, kps, cus, max(per, 1))
+
+
 def gpu_run(wl, k_max=None, k_per_seq="wl", n_sink=None, step=0, separate=False, n_recent=0,
-            group_agg=0, ws=None, lib=None):
+            group_agg=0, ws=None, lib=None, row_order=None):
     """HIP results of the same step; `separate` uses the three-call path.  With
     selection options the _ex entry points are called, else the plain ones.
     `ws`: a workspace to use (default: a new zero-filled one); the result's
     "sync" holds its counter prefix after the call.  `lib`: the library to call
-    (default: the package's libtsv.so; the testing library for hooks)."""
+    (default: the package's libtsv.so; the testing library for hooks).
+    `row_order`: call tsv_decode_step_scheduled with this order (an int32
+    array, or "lpt" for the library's own schedule)."""
     import torch
 
     import query_aware_sparse_bbox_amd as T_mod
@@ -96,6 +116,13 @@ def gpu_run(wl, k_max=None, k_per_seq="wl", n_sink=None, step=0, separate=False,
                                sel, cnt, sc, ws)
         T.tsv_sparse_decode(sh, q, d.k_pool, d.v_pool, d.block_table, seq_lens, sel, cnt,
                             k_max, wl.scale, out, ws)
+    elif row_order is not None:
+        if isinstance(row_order, str):
+            row_order = lpt_order(wl, k_max, k_per_seq, step, lib)
+        ro = torch.from_numpy(np.ascontiguousarray(row_order, dtype=np.int32)).cuda()
+        T.tsv_decode_step_scheduled(sh, q, k_new, v_new, d.k_pool, d.v_pool, d.meta,
+                                    d.block_table, seq_lens, k_max, kps, n_sink, n_recent,
+                                    group_agg, ro, wl.scale, sel, cnt, sc, out, ws)
     elif n_recent or group_agg:
         T.tsv_decode_step_ex(sh, q, k_new, v_new, d.k_pool, d.v_pool, d.meta, d.block_table,
                              seq_lens, k_max, kps, n_sink, n_recent, group_agg, wl.scale, sel,

@@ -43,7 +43,8 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ("tsv_meta_append", "tsv_select_pages", "tsv_sparse_decode", "tsv_decode_step",
               "tsv_meta_build", "tsv_workspace_bytes", "tsv_meta_bytes", "tsv_status_string",
-              "tsv_version", "tsv_select_pages_ex", "tsv_decode_step_ex"):
+              "tsv_version", "tsv_select_pages_ex", "tsv_decode_step_ex",
+              "tsv_schedule_rows", "tsv_decode_step_scheduled"):
         assert n in names
 
 
@@ -235,6 +236,33 @@ def test_noalloc_rejects_shapes_beyond_its_scratch_before_any_hip_call(tsv):
                                      0, None, ctypes.c_float(0.1), f, f, None, f, None) == -1
     assert L.tsv_decode_step_noalloc(ctypes.byref(s), f, None, None, f, f, f, f, f, 0, None,
                                      0, None, ctypes.c_float(0.1), f, f, None, f, None) == -1
+
+
+def test_scheduled_step_rejects_bad_orders_before_any_hip_call(tsv):
+    """The scheduled step checks its row order (4-byte aligned, at least one
+    entry per row, at most 2^24) after the step's own checks, before any HIP
+    call; the residency query checks its outputs before querying."""
+    f = ctypes.c_void_p(1 << 20)
+    L = tsv._lib
+    s = shape()  # 2 sequences x 2 KV heads
+    need = L.tsv_workspace_bytes(ctypes.byref(s), 4)
+    sc = ctypes.c_float(0.1)
+
+    def step(order, n, q=f, ws_bytes=need):
+        return L.tsv_decode_step_scheduled(ctypes.byref(s), q, None, None, f, f, f, f, f, 4,
+                                           None, 0, None, order, n, sc, f, f, None, f, f,
+                                           ws_bytes, None)
+
+    assert step(ctypes.c_void_p((1 << 20) + 2), 4) == -1   # misaligned
+    assert step(f, 3) == -1                                  # fewer entries than rows
+    assert step(f, (1 << 24) + 1) == -1                      # beyond the limit
+    assert step(f, 4, q=None) == -1                          # the step's own checks
+    assert step(f, 4, ws_bytes=need - 1) == -1
+    assert step(None, 0, q=None) == -1
+    one = ctypes.c_int32(0)
+    assert L.tsv_step_residency(ctypes.byref(s), 4, None, ctypes.byref(one)) == -1
+    assert L.tsv_step_residency(ctypes.byref(s), 0, ctypes.byref(one), ctypes.byref(one)) == -1
+    assert L.tsv_step_residency(None, 4, ctypes.byref(one), ctypes.byref(one)) == -1
 
 
 def test_one_hip_runtime_whatever_the_import_order():

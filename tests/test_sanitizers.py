@@ -117,6 +117,9 @@ HOST_DRIVER = textwrap.dedent(r"""
                                 P_, P_, P_, Z_, P_], ctypes.c_int),
         "tsv_decode_step_noalloc": ([SP, P_, P_, P_, P_, P_, P_, P_, P_, I_, P_, I_, OP, F_, P_,
                                      P_, P_, P_, P_], ctypes.c_int),
+        "tsv_schedule_rows": ([SP, I_, P_, P_, I_, I_, P_, I_, P_], ctypes.c_int),
+        "tsv_decode_step_scheduled": ([SP, P_, P_, P_, P_, P_, P_, P_, P_, I_, P_, I_, OP, P_, I_,
+                                       F_, P_, P_, P_, P_, P_, Z_, P_], ctypes.c_int),
     }
     for name, (a, r) in sig.items():
         f = getattr(L, name); f.argtypes = a; f.restype = r
@@ -178,6 +181,31 @@ HOST_DRIVER = textwrap.dedent(r"""
     for b in bad_shapes:
         assert L.tsv_decode_step_ex(ctypes.byref(b), f, None, None, f, f, f, f, f, 4, None, 0,
                                     None, sc, f, f, None, f, f, need, None) in (-1, -2)
+    # the row schedule (host code only) over random lengths, budgets and CU
+    # geometries: every row exactly once in a buffer of exactly its length
+    import random
+    rnd = random.Random(5)
+    for it in range(300):
+        B, Hkv = rnd.randint(1, 70), rnd.choice((1, 2, 8))
+        s2 = Shape(B, Hkv * 4, Hkv, 128, 16, 64, 64 * B, rnd.randint(0, 4))
+        lens = (ctypes.c_int32 * B)(*[rnd.randint(-5, 64 * 16 + 9) for _ in range(B)])
+        kps = (ctypes.c_int32 * B)(*[rnd.randint(-2, 70) for _ in range(B)])
+        k, cus, per = rnd.randint(1, 64), rnd.choice((1, 7, 64, 256)), rnd.randint(1, 4)
+        kp = kps if it % 2 else None
+        n2 = ctypes.c_int32(0)
+        assert L.tsv_schedule_rows(ctypes.byref(s2), k, lens, kp, cus, per, None, 0,
+                                   ctypes.byref(n2)) == 0
+        buf = (ctypes.c_int32 * n2.value)()
+        assert L.tsv_schedule_rows(ctypes.byref(s2), k, lens, kp, cus, per, buf, n2.value,
+                                   ctypes.byref(n2)) == 0
+        got = sorted(x for x in buf if x >= 0)
+        assert got == list(range(B * Hkv)), it
+    # the scheduled step's own checks, before any HIP call
+    assert L.tsv_decode_step_scheduled(ctypes.byref(s), f, None, None, f, f, f, f, f, 4, None,
+                                       0, None, ctypes.c_void_p((1 << 20) + 2), 4, sc, f, f,
+                                       None, f, f, need, None) == -1
+    assert L.tsv_decode_step_scheduled(ctypes.byref(s), f, None, None, f, f, f, f, f, 4, None,
+                                       0, None, f, 3, sc, f, f, None, f, f, need, None) == -1
     print(f"host layer ok: {n} shapes queried")
 """)
 
