@@ -1,9 +1,13 @@
 """Benchmark one decode step of query-aware page selection + sparse paged decode.
 
-A step is one tsv_decode_step over one batch: [append one token per sequence]
--> score every page's box against the query -> keep the top-K pages -> masked
-softmax attention over the kept pages only (TinyServe, "Query-Aware Cache
-Selection for Efficient LLM Serving": abstract, method details).  Inputs are
+A step is one tsv_decode_step_scheduled over one batch: [append one token per
+sequence] -> score every page's box against the query -> keep the top-K pages
+-> masked softmax attention over the kept pages only (TinyServe, "Query-Aware
+Cache Selection for Efficient LLM Serving": abstract, method details), its
+rows taken longest first in the order tsv_schedule_rows plans on the host from
+the sequence lengths (planned once before the timed region, as a serving loop
+plans a step from the lengths it keeps; the planning time is reported;
+--schedule none: tsv_decode_step, rows in index order).  Inputs are
 seeded synthetic tensors with the decode shapes of the pages' models,
 resident in HBM before the timed region.  R copies of the pool and metadata
 are rotated so that every step reads HBM rather than the 256 MB Infinity
@@ -221,6 +225,9 @@ def parse():
                     help="skip the selection-quality / dense-speedup report")
     ap.add_argument("--copy-calibrate", type=float, default=0.0, metavar="MB",
                     help="only run a plain device copy of MB megabytes, 5 times, and exit")
+    ap.add_argument("--schedule", default="lpt", choices=["lpt", "none"],
+                    help="row order of the step: the library's longest-first schedule "
+                         "(default) or index order")
     ap.add_argument("--phases", action="store_true",
                     help="only print the one-launch step's per-workgroup phase times, from the "
                          "testing library's phase stamps over --steps eager steps, and exit")
@@ -251,8 +258,25 @@ PHASES = [("stage", 0, 1, "start -> block-table row staged (and the token append
           ("finish", 4, 5, "combine of the waves' states, output (merge of split rows)")]
 
 
+def plan_rows(T, sh, k_max, lens_np, kps_np, dev):
+    """The library's longest-first row order for one step, on the device,
+    and a record of it (with the host time the planning takes, median of 20)."""
+    import torch
+
+    cus, per = T.tsv_step_residency(sh, k_max)
+    times = []
+    for _ in range(20):
+        t = time.perf_counter()
+        order = T.tsv_schedule_rows(sh, k_max, lens_np, kps_np, cus, max(per, 1))
+        times.append(time.perf_counter() - t)
+    rec = {"kind": "lpt", "num_cus": cus, "per_cu": per, "used": per > 0,
+           "workgroups": int(order.size), "idle_workgroups": int((order < 0).sum()),
+           "host_plan_us": float(np.median(times) * 1e6)}
+    return torch.from_numpy(order).to(dev), rec
+
+
 def phases(args, T, sh, wl, instance, q, k_new, v_new, bt, lens, k_max, kps, n_sink, scale,
-           launches):
+           launches, order):
     """Phase times of the one-launch step from the testing library's stamps
     (100 MHz real-time counter, 10 ns ticks), per workgroup, over the last
     --steps eager steps (each read back right after its step)."""
@@ -268,8 +292,9 @@ def phases(args, T, sh, wl, instance, q, k_new, v_new, bt, lens, k_max, kps, n_s
     torch.cuda.synchronize()
 
     def step(d):
-        t.tsv_decode_step(sh, q, k_new, v_new, d.k_pool, d.v_pool, d.meta, bt, lens, k_max, kps,
-                          n_sink, scale, d.sel, d.cnt, None, d.out, d.ws)
+        t.tsv_decode_step_scheduled(sh, q, k_new, v_new, d.k_pool, d.v_pool, d.meta, bt, lens,
+                                    k_max, kps, n_sink, 0, 0, order, scale, d.sel, d.cnt, None,
+                                    d.out, d.ws)
 
     for i in range(args.warmup):
         step(insts[i % R])
@@ -290,7 +315,8 @@ def phases(args, T, sh, wl, instance, q, k_new, v_new, bt, lens, k_max, kps, n_s
             per[name].append((st[:, b] - st[:, a]) / 100.0)
     cmd = "python3 bench.py " + " ".join(sys.argv[1:])
     lines = [f"# {args.config}" + (f" (KV {args.kv_dtype})" if args.kv_dtype else "") +
-             ": one-launch step, phase times per workgroup", "",
+             ": one-launch step, phase times per workgroup" +
+             (", rows in the longest-first order" if order is not None else ""), "",
              f"  {cmd}", "",
              f"  shape {sh}", f"  workgroups per step: {int(live.sum())}; "
              f"{args.steps} eager steps after {args.warmup} warm-up, each read back right after it",
@@ -359,9 +385,17 @@ def main():
 
     agg = {"max": T.TSV_AGG_MAX, "sum": T.TSV_AGG_SUM}[args.group_agg]
     variant = args.recent != 0 or agg != T.TSV_AGG_MAX
+    order, sched = None, {"kind": "none"}
+    if args.schedule == "lpt":
+        order, sched = plan_rows(T, sh, k_max, lens_np, kps_np, dev)
+        print(f"[bench] longest-first row order: {sched}", flush=True)
 
     def step(d):
-        if variant:
+        if order is not None:
+            T.tsv_decode_step_scheduled(sh, q, k_new, v_new, d.k_pool, d.v_pool, d.meta, bt,
+                                        lens, k_max, kps, n_sink, args.recent, agg, order,
+                                        scale, d.sel, d.cnt, None, d.out, d.ws)
+        elif variant:
             T.tsv_decode_step_ex(sh, q, k_new, v_new, d.k_pool, d.v_pool, d.meta, bt, lens,
                                  k_max, kps, n_sink, args.recent, agg, scale, d.sel, d.cnt,
                                  None, d.out, d.ws)
@@ -371,7 +405,7 @@ def main():
 
     if args.phases:
         phases(args, T, sh, wl, instance, q, k_new, v_new, bt, lens, k_max, kps, n_sink, scale,
-               launches)
+               launches, order)
         return
 
     first = instance()
@@ -493,10 +527,13 @@ def main():
             e.src = d
             dense.append(e)
 
+        dorder = plan_rows(T, sh, MP, lens_np, None, dev)[0] if order is not None else None
+
         def dstep(e):
             d = e.src
-            T.tsv_decode_step(sh, q, k_new, v_new, d.k_pool, d.v_pool, d.meta, bt, lens, MP,
-                              None, n_sink, scale, e.sel, e.cnt, None, e.out, e.ws)
+            T.tsv_decode_step_scheduled(sh, q, k_new, v_new, d.k_pool, d.v_pool, d.meta, bt,
+                                        lens, MP, None, n_sink, 0, 0, dorder, scale, e.sel,
+                                        e.cnt, None, e.out, e.ws)
 
         s2 = torch.cuda.Stream()
         s2.wait_stream(stream)
@@ -547,7 +584,8 @@ def main():
                    "rows_sampled": len(rows), "query_heads_sampled": int(recalls.size),
                    "dense_step_us": ms_dense * 1e3,
                    "sparse_speedup_vs_dense": ms_dense / ms_step,
-                   "dense": "the same tsv_decode_step with every page kept (k_max = max pages)"}
+                   "dense": "the same step with every page kept (k_max = max pages, its own "
+                            "row order)"}
         print(f"[bench] dense step {ms_dense * 1e3:.2f} us, speedup {ms_dense / ms_step:.2f}x, "
               f"attention-mass recall mean {recalls.mean():.4f} min {recalls.min():.4f}",
               flush=True)
@@ -569,6 +607,8 @@ def main():
     step_gbs = nb["total"] / (ms_step * 1e-3) / 1e9
     src = source_hash()
     tkey = args.config if kv_dtype == own_dtype else f"{args.config}:{W.DTYPE_NAMES[kv_dtype]}"
+    if order is None:
+        tkey += ":unscheduled"
     tr = None if variant else TRAFFIC.get(tkey)
     traffic = tr["bytes_per_step"] if tr and tr["source"] == src else None
     kernel = {1: "k_step (append, score, select, decode of every row)"}.get(
@@ -592,7 +632,7 @@ def main():
                    W.DTYPE_NAMES[sh.kv_dtype], "batch": B, "q_heads": Hq, "kv_heads": Hkv,
                    "head_dim": D, "page_size": sh.page_size, "k_max": k_max,
                    "rotating_instances": R, "graph": not args.eager,
-                   "untimed_settle_steps": settle,
+                   "untimed_settle_steps": settle, "row_schedule": sched,
                    "selection": {"n_sink": n_sink, "n_recent": args.recent,
                                  "group_agg": args.group_agg}},
         "step_algorithmic_bytes": nb["total"],
