@@ -270,9 +270,16 @@ def plan_rows(T, sh, k_max, lens_np, kps_np, dev):
         t = time.perf_counter()
         order = T.tsv_schedule_rows(sh, k_max, lens_np, kps_np, cus, max(per, 1))
         times.append(time.perf_counter() - t)
-    rec = {"kind": "lpt", "num_cus": cus, "per_cu": per, "used": per > 0,
+    identity = order.size == sh.batch * sh.num_kv_heads and np.array_equal(
+        order, np.arange(order.size))
+    rec = {"kind": "lpt", "num_cus": cus, "per_cu": per, "used": per > 0 and not identity,
            "workgroups": int(order.size), "idle_workgroups": int((order < 0).sum()),
            "host_plan_us": float(np.median(times) * 1e6)}
+    if identity:
+        # rows of equal weight keep index order: the plain step does the same
+        # without the order's load
+        rec["identity"] = True
+        return None, rec
     return torch.from_numpy(order).to(dev), rec
 
 

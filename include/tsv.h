@@ -278,7 +278,9 @@ int tsv_decode_step_ex(const tsv_shape* shape, const float* q, const void* k_new
    row_order NULL only the length is computed, otherwise `capacity` entries
    must hold it (TSV_ERR_INVALID_ARG if they do not).  The order only decides which
    workgroup runs which row and when: the step's results do not depend on
-   it. */
+   it.  Rows of equal weight keep index order, so equal lengths and budgets
+   give 0 .. B*Hkv-1, the plain step's own order, which the plain step runs
+   without the order's load. */
 int tsv_schedule_rows(const tsv_shape* shape, int32_t k_max, const int32_t* seq_lens,
                       const int32_t* k_per_seq, int32_t num_cus, int32_t per_cu,
                       int32_t* row_order, int32_t capacity, int32_t* order_len);
