@@ -120,6 +120,25 @@ def step_bytes(wl, lens, sel, cnt):
                 total=meta + kv + qo + table + append)
 
 
+def attention_mass_recall(keys, q, scale, page_size, kept_pages):
+    """Share of each query head's exact softmax mass that falls on the kept
+    pages, in float64.  keys [L][D]: the valid keys of one (sequence, KV head)
+    in token order (token t on page t // page_size); q [G][D]: the group's
+    queries; kept_pages: the kept logical pages.  Returns G floats."""
+    keys = np.asarray(keys, dtype=np.float64)
+    q = np.asarray(q, dtype=np.float64)
+    L = keys.shape[0]
+    page_of = np.arange(L) // page_size
+    keep = np.zeros((L + page_size - 1) // page_size, dtype=bool)
+    keep[np.asarray(list(kept_pages), dtype=np.int64)] = True
+    out = []
+    for g in range(q.shape[0]):
+        z = (keys @ q[g]) * float(scale)
+        w = np.exp(z - z.max())
+        out.append(float(w[keep[page_of]].sum() / w.sum()))
+    return out
+
+
 def cpu_model() -> str:
     try:
         with open("/proc/cpuinfo") as f:
@@ -578,14 +597,9 @@ def main():
             n_pages = (L + P - 1) // P
             phys = torch.from_numpy(wl.block_table[b, :n_pages].astype(np.int64)).to(dev)
             kt = W.storage_to_f32(WD.kv_numpy(first.k_pool[phys, h].reshape(-1, D)[:L],
-                                              sh.kv_dtype), sh.kv_dtype).astype(np.float64)
-            page_of = np.arange(L) // P
-            keep = np.zeros(n_pages, dtype=bool)
-            keep[sel_np[b, h, :cnt_np[b, h]]] = True
-            for g in range(sh.group):
-                z = (kt @ q_np[b, h * sh.group + g].astype(np.float64)) * float(scale)
-                w = np.exp(z - z.max())
-                recalls.append(float(w[keep[page_of]].sum() / w.sum()))
+                                              sh.kv_dtype), sh.kv_dtype)
+            recalls += attention_mass_recall(kt, q_np[b, h * sh.group:(h + 1) * sh.group],
+                                             scale, P, sel_np[b, h, :cnt_np[b, h]])
         recalls = np.array(recalls)
         quality = {"attention_mass_recall_mean": float(recalls.mean()),
                    "attention_mass_recall_min": float(recalls.min()),
