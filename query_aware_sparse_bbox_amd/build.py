@@ -13,7 +13,13 @@ Flags:
   -ffp-contract=off   no implicit multiply-add fusion: page scores must match
                       the fixed rounding sequence bit for bit (attention code
                       writes its fused multiply-adds explicitly);
-  -packed-fp32-ops    disabled: no packed fp32 VALU instructions are emitted.
+  -packed-fp32-ops    disabled: no packed fp32 VALU instructions are emitted;
+  -amdgpu-kernarg-preload-count=16
+                      the first kernel arguments arrive in scalar registers
+                      with the wave instead of through a load (the compiler
+                      takes as many as the free user registers hold, 14 dwords
+                      for the step kernel, and keeps a fallback that loads
+                      them for firmware without preloading).
 """
 import os
 import subprocess
@@ -42,6 +48,7 @@ def flags(extra=()):
     return [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
             "-ffp-contract=off", "-fno-gpu-flush-denormals-to-zero",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            "-mllvm", "-amdgpu-kernarg-preload-count=16",
             "-Wall", "-Wno-unused-function", "-I", os.path.join(ROOT, "include"), *extra]
 
 

@@ -1903,16 +1903,19 @@ __device__ __forceinline__ void merge_row(const float* __restrict__ partials, in
 }
 
 template <int DT, int D, int G, int NT>
+// The arguments a workgroup needs first (its row, the block-table row, the
+// length and budget) lead the list: the first 14 dwords of the arguments
+// arrive in scalar registers with the wave (kernarg preloading), the rest
+// through the usual loads, which complete while the row is staged.
 __global__ __launch_bounds__(NT, (step_min_blocks<DT, D, G, NT>())) void k_step(
-    const float* __restrict__ q, const void* __restrict__ k_new,
-    const void* __restrict__ v_new, void* __restrict__ k_pool, void* __restrict__ v_pool,
-    void* __restrict__ meta, const int32_t* __restrict__ bt,
-    const int32_t* __restrict__ seq_lens, int units, int Hq, int Hkv, int log2P, int MP,
-    int NP, int k_max, const int32_t* __restrict__ k_per_seq, SelectPolicy pol, float qscale,
-    int S, int polls, const int32_t* __restrict__ order, int32_t* __restrict__ sel,
-    int32_t* __restrict__ sel_count, float* __restrict__ scores_out,
-    uint32_t* __restrict__ sync, uint32_t* __restrict__ keys, float* __restrict__ partials,
-    float* __restrict__ out) {
+    const int32_t* __restrict__ order, const int32_t* __restrict__ bt,
+    const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ k_per_seq, int S,
+    int units, int Hkv, int MP, int log2P, int NP, const float* __restrict__ q,
+    const void* __restrict__ k_new, const void* __restrict__ v_new, void* __restrict__ k_pool,
+    void* __restrict__ v_pool, void* __restrict__ meta, int Hq, int k_max, SelectPolicy pol,
+    float qscale, int polls, int32_t* __restrict__ sel, int32_t* __restrict__ sel_count,
+    float* __restrict__ scores_out, uint32_t* __restrict__ sync, uint32_t* __restrict__ keys,
+    float* __restrict__ partials, float* __restrict__ out) {
   constexpr int NW = NT / kWave;
   constexpr bool MF = step_uses_mfma<DT, D, G>();
   constexpr int PB = ScoreCfg<DT, D, G, NT>::PB;

@@ -160,9 +160,9 @@ hipError_t step_t(const Dims& d, const StepPlan& plan, const float* q, const voi
     constexpr int hd = decltype(HD)::value, g = decltype(GG)::value;
     auto go = [&](auto NTc) -> hipError_t {
       constexpr int nthr = decltype(NTc)::value;
-      hipLaunchKernelGGL((k_step<dt, hd, g, nthr>), grid, dim3(nthr), plan.lds, s, q, k_new,
-                         v_new, k_pool, v_pool, meta, bt, seq_lens, units, d.Hq, d.Hkv, log2P,
-                         d.MP, d.NP, k_max, k_per_seq, pol, qscale, S, plan.polls, ord, sel,
+      hipLaunchKernelGGL((k_step<dt, hd, g, nthr>), grid, dim3(nthr), plan.lds, s, ord, bt,
+                         seq_lens, k_per_seq, S, units, d.Hkv, d.MP, log2P, d.NP, q, k_new,
+                         v_new, k_pool, v_pool, meta, d.Hq, k_max, pol, qscale, plan.polls, sel,
                          sel_count, scores_out, ws.sync, ws.keys, ws.partials, out);
       return hipGetLastError();
     };
