@@ -137,3 +137,26 @@ def test_graph_replay_of_the_scheduled_step():
         say(f"  replay {i}")
         assert torch.equal(sel, ref[0]) and torch.equal(cnt, ref[1])
         assert torch.equal(out.view(torch.int32), ref[2].view(torch.int32))
+
+
+@pytest.mark.parametrize("name,kw", [
+    ("gpt2", dict(batch=40, context=700)),                                     # MHA, VALU decode
+    ("gpt2", dict(batch=20, context=500, head_dim=128, kv_dtype=W.F32)),       # fp32 KV
+    ("ragged", dict(batch=20, lens_range=(50, 1500), num_q_heads=128,          # G = 16
+                    head_dim=64)),
+    ("llama_long", dict(batch=6, context=3000, page_size=64, kv_dtype=W.F16)),  # 64-token pages
+    ("ragged", dict(batch=24, lens_range=(20, 2500), kv_dtype=W.F8E5)),        # fp8, ragged
+])
+def test_scheduled_step_across_shapes(name, kw):
+    """More than 128 rows, one workgroup each: the library's order and its
+    reverse give the plain step's results bit for bit."""
+    import query_aware_sparse_bbox_amd as T
+
+    wl = W.make(name, **kw)
+    U = wl.shape.batch * wl.shape.num_kv_heads
+    assert U > 128 and T.tsv_step_residency(wl.shape, wl.k_max)[1] >= 1
+    say(f"[case] {name} {kw}: {U} rows")
+    plain = gpu_run(wl)
+    order = lpt_order(wl)
+    assert_bitwise_equal(gpu_run(wl, row_order=order), plain)
+    assert_bitwise_equal(gpu_run(wl, row_order=order[::-1].copy()), plain)
