@@ -160,3 +160,29 @@ def test_scheduled_step_across_shapes(name, kw):
     order = lpt_order(wl)
     assert_bitwise_equal(gpu_run(wl, row_order=order), plain)
     assert_bitwise_equal(gpu_run(wl, row_order=order[::-1].copy()), plain)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_scheduled_step_random_shapes(seed):
+    """Seeded random one-launch shapes with more than 128 rows (group size,
+    head dim, page size, KV type, ragged lengths, budget, sinks, appends):
+    the library's order gives the plain step's results bit for bit."""
+    import query_aware_sparse_bbox_amd as T
+
+    rng = np.random.default_rng(500 + seed)
+    G = int(rng.choice([1, 2, 4, 8]))
+    Hkv = int(rng.choice([2, 4, 8]))
+    D = int(rng.choice([64, 128]))
+    P = int(rng.choice([8, 16, 32]))
+    dt = [W.F16, W.BF16, W.F8, W.F8E5, W.F32][int(rng.integers(0, 5))]
+    B = int(rng.integers(130 // Hkv + 1, 300 // Hkv + 1))
+    hi = int(rng.integers(200, 3000))
+    kw = dict(batch=B, num_q_heads=G * Hkv, num_kv_heads=Hkv, head_dim=D, page_size=P,
+              kv_dtype=dt, lens_range=(1, hi), budget=("ragged", 32, 4),
+              n_sink=int(rng.integers(0, 2)), append_steps=int(rng.integers(0, 2)))
+    wl = W.make("ragged", **kw)
+    say(f"[case] seed {seed}: {kw}")
+    if T.tsv_step_residency(wl.shape, wl.k_max)[1] == 0:
+        pytest.skip("shape takes the phased step")
+    plain = gpu_run(wl)
+    assert_bitwise_equal(gpu_run(wl, row_order="lpt"), plain)
