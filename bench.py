@@ -283,17 +283,36 @@ def plan_rows(T, sh, k_max, lens_np, kps_np, dev):
     and a record of it (with the host time the planning takes, median of 20)."""
     import torch
 
+    import ctypes
+
     cus, per = T.tsv_step_residency(sh, k_max)
     times = []
     for _ in range(20):
         t = time.perf_counter()
         order = T.tsv_schedule_rows(sh, k_max, lens_np, kps_np, cus, max(per, 1))
         times.append(time.perf_counter() - t)
+    # the C planner alone, on buffers set up once (what a serving loop in C
+    # pays per step)
+    shp = T.Shape.of(sh)
+    lens32 = np.ascontiguousarray(lens_np, dtype=np.int32)
+    kps32 = None if kps_np is None else np.ascontiguousarray(kps_np, dtype=np.int32)
+    buf = np.empty(order.size, dtype=np.int32)
+    n = ctypes.c_int32(0)
+    args = (ctypes.byref(shp), int(k_max), ctypes.c_void_p(lens32.ctypes.data),
+            None if kps32 is None else ctypes.c_void_p(kps32.ctypes.data), int(cus),
+            int(max(per, 1)), ctypes.c_void_p(buf.ctypes.data), int(buf.size), ctypes.byref(n))
+    c_times = []
+    for _ in range(200):
+        t = time.perf_counter()
+        T._lib.tsv_schedule_rows(*args)
+        c_times.append(time.perf_counter() - t)
+    assert np.array_equal(buf, order)
     identity = order.size == sh.batch * sh.num_kv_heads and np.array_equal(
         order, np.arange(order.size))
     rec = {"kind": "lpt", "num_cus": cus, "per_cu": per, "used": per > 0 and not identity,
            "workgroups": int(order.size), "idle_workgroups": int((order < 0).sum()),
-           "host_plan_us": float(np.median(times) * 1e6)}
+           "host_plan_us": float(np.median(c_times) * 1e6),
+           "host_plan_us_via_python": float(np.median(times) * 1e6)}
     if identity:
         # rows of equal weight keep index order: the plain step does the same
         # without the order's load

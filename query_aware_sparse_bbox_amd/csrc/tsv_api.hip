@@ -374,27 +374,26 @@ int tsv_schedule_rows(const tsv_shape* shape, int32_t k_max, const int32_t* seq_
       (capacity > 0 && !row_order))
     return TSV_ERR_INVALID_ARG;
   if ((int64_t)d.B * d.Hkv > INT32_MAX / 2) return TSV_ERR_UNSUPPORTED;
-  const int units = d.B * d.Hkv;
   // weight of a row: the bytes its step reads -- every page box, the kept
   // pages' keys and values (a full budget of full pages), the block-table row
   const double e = tsv::kv_bytes(d.dt), box = 2.0 * d.D * e, page = 2.0 * d.D * e * d.P;
-  std::vector<double> w(units);
+  std::vector<double> w(d.B);  // per sequence: each of its Hkv rows weighs the same
   for (int b = 0; b < d.B; ++b) {
     const long len_b = std::min<long>(std::max(seq_lens[b], 0), (long)d.MP * d.P);
     const long n = (len_b + d.P - 1) / d.P;
     const long kb = std::min<long>(
         n, std::max(1, std::min(k_per_seq ? k_per_seq[b] : k_max, k_max)));
-    const double wb = box * n + page * kb + 4.0 * n;
-    for (int h = 0; h < d.Hkv; ++h) w[(size_t)b * d.Hkv + h] = wb;
+    w[b] = box * n + page * kb + 4.0 * n;
   }
+  // one planning pass: it reports the length, and fills row_order when
+  // given and large enough
   long len = 0;
-  tsv::schedule_rows(w.data(), units, num_cus, per_cu, nullptr, 0, &len);
+  const bool filled = tsv::schedule_rows(w.data(), d.B, d.Hkv, num_cus, per_cu, row_order,
+                                         capacity, &len);
   if (len > INT32_MAX) return TSV_ERR_UNSUPPORTED;
   *order_len = (int32_t)len;
   if (row_order == nullptr) return TSV_OK;  // length query
-  if (len > capacity) return TSV_ERR_INVALID_ARG;
-  tsv::schedule_rows(w.data(), units, num_cus, per_cu, row_order, capacity, &len);
-  return TSV_OK;
+  return filled ? TSV_OK : TSV_ERR_INVALID_ARG;
 }
 
 int tsv_decode_step_scheduled(const tsv_shape* shape, const float* q, const void* k_new,

@@ -208,13 +208,21 @@ hipError_t step_per_cu(const Dims& d, int k_max, int* per_cu) {
 // use are idle workgroups (-1), so that every workgroup of the wave still
 // lands on its CU.  Rows after the first wave follow in descending weight:
 // each takes the next slot to free up.
-bool schedule_rows(const double* w, int units, int num_cus, int per_cu, int32_t* order,
+bool schedule_rows(const double* w, int B, int Hkv, int num_cus, int per_cu, int32_t* order,
                    long cap, long* len) {
+  const int units = B * Hkv;
   const long C = std::max(1, num_cus), m = std::max(1, per_cu);
   const long first = std::min<long>(units, C * m);
+  // rows heaviest first, equal weights in row order: the sequences sorted,
+  // each followed by its KV heads (all of a sequence's rows weigh the same)
+  std::vector<int> seq(B);
+  std::iota(seq.begin(), seq.end(), 0);
+  std::sort(seq.begin(), seq.end(),
+            [&](int a, int b) { return w[a] > w[b] || (w[a] == w[b] && a < b); });
   std::vector<int> rank(units);
-  std::iota(rank.begin(), rank.end(), 0);
-  std::stable_sort(rank.begin(), rank.end(), [&](int a, int b) { return w[a] > w[b]; });
+  for (int i = 0; i < B; ++i)
+    for (int h = 0; h < Hkv; ++h) rank[(size_t)i * Hkv + h] = seq[i] * Hkv + h;
+  auto wrow = [&](int u) { return w[u / Hkv]; };
   // the first wave: the CU with the least weight among those with a free
   // slot (equal weights: lower CU first) takes the next row
   using Slot = std::pair<double, long>;  // (weight so far, CU)
@@ -229,7 +237,7 @@ bool schedule_rows(const double* w, int units, int num_cus, int per_cu, int32_t*
     free_cus.pop();
     where[r] = count[s.second] * C + s.second;
     wave = std::max(wave, where[r] + 1);
-    if (++count[s.second] < m) free_cus.push({s.first + w[rank[r]], s.second});
+    if (++count[s.second] < m) free_cus.push({s.first + wrow(rank[r]), s.second});
   }
   if (units > first) wave = (wave + C - 1) / C * C;
   *len = wave + (units - first);

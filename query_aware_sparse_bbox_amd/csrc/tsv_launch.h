@@ -170,10 +170,11 @@ int step_splits_for(const Dims& d, int k_max);
 hipError_t step_per_cu(const Dims& d, int k_max, int* per_cu);
 
 // Longest-first row order for the one-launch step (host only, no HIP call).
-// w[u] is row u's weight; num_cus CUs hold per_cu workgroups each.  Writes
-// the order's length to *len and, when order != null and *len <= cap, the
-// order itself (-1 = an idle workgroup).  Returns false when cap is too small.
-bool schedule_rows(const double* w, int units, int num_cus, int per_cu, int32_t* order,
+// w[b] is the weight of each of sequence b's Hkv rows; num_cus CUs hold
+// per_cu workgroups each.  Writes the order's length to *len and, when
+// order != null and *len <= cap, the order itself (-1 = an idle workgroup).
+// Returns false when cap is too small.
+bool schedule_rows(const double* w, int B, int Hkv, int num_cus, int per_cu, int32_t* order,
                    long cap, long* len);
 
 }  // namespace tsv
