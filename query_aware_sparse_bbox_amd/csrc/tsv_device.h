@@ -2015,6 +2015,10 @@ __global__ __launch_bounds__(NT, (step_min_blocks<DT, D, G, NT>())) void k_step(
   }
   __syncthreads();
   TSV_STAMP(2);
+  // The rest of the row (select, decode, finish) is its critical path, while
+  // a workgroup beside it on the CU may still be scoring, bound by vector ALU
+  // throughput: this row's waves take instruction-issue priority from here.
+  __builtin_amdgcn_s_setprio(2);
   if (scores_out && split == 0) {  // uniform over the workgroup
     float* srow_out = scores_out + (size_t)unit * MP;
     for (int p = tid; p < n; p += NT) srow_out[p] = key_to_score(s_key[p]);
