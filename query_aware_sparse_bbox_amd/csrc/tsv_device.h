@@ -1821,30 +1821,25 @@ template <int DT, int D, int G, int NT>
 constexpr int step_min_blocks() { return NT == 256 && (G <= 4 || DT != DT_F32) ? 2 : 1; }
 
 // Split rows: the S workgroups of a row meet twice through the row's line of
-// counters in the workspace (word 0: arrivals at the score exchange, word 1:
-// set when all have arrived, word 2: finished decodes; all zero between
-// calls).  Everything they exchange (page keys, partial states, counters) is
+// counters in the workspace (word 0: arrivals at the score exchange, word 2:
+// finished decodes; both zero between calls).  Everything they exchange (page keys, partial states, counters) is
 // written and read with device-scope atomic stores and loads, which are
 // coherent across the chip on their own; a writer waits for its stores to
 // complete before it counts itself in.  No cache-wide writeback or
 // invalidation is needed.
-constexpr int kSyncArrive = 0, kSyncAll = 1, kSyncDone = 2;
+constexpr int kSyncArrive = 0, kSyncDone = 2;
 
 // Score exchange of one split row, called by one thread after every thread
 // of the workgroup stored its keys and waited for them.  Returns 1 when all S
 // splits have arrived (their keys can then be read), 0 when `polls` reads of
-// the row's flag found it still clear.  The last split to arrive re-arms the
-// arrival count and sets the flag.
+// the row's arrival count found fewer than S.  Nothing is re-armed here: the
+// count stays at S until the last split to finish clears it (row_finish).
 __device__ __forceinline__ int row_exchange(uint32_t* c, int S, int polls) {
   const uint32_t o =
       __hip_atomic_fetch_add(c + kSyncArrive, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  if (o == (uint32_t)S - 1) {
-    st_dev(c + kSyncArrive, 0u);
-    st_dev(c + kSyncAll, 1u);
-    return 1;
-  }
+  if (o == (uint32_t)S - 1) return 1;
   for (int it = 0; it < polls; ++it) {
-    if (ld_dev(c + kSyncAll) != 0u) return 1;
+    if (ld_dev(c + kSyncArrive) == (uint32_t)S) return 1;
     __builtin_amdgcn_s_sleep(2);
   }
   return 0;
@@ -1853,15 +1848,15 @@ __device__ __forceinline__ int row_exchange(uint32_t* c, int S, int polls) {
 // Called by one thread after every thread of the workgroup stored its share
 // of the partial state and waited for it: 1 for the last of the row's S
 // splits to finish (which then merges), else 0.  Never waits.  Every split
-// gets here after it has left the score exchange (and the split that set the
-// flag has waited for that store), so the last one also clears the flag: the
-// row's counters are all zero again when the kernel ends.
+// gets here after it has left the score exchange, so the last one also
+// clears the arrival count: the row's counters are all zero again when the
+// kernel ends.
 __device__ __forceinline__ int row_finish(uint32_t* c, int S) {
   const uint32_t o =
       __hip_atomic_fetch_add(c + kSyncDone, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   if (o != (uint32_t)S - 1) return 0;
   st_dev(c + kSyncDone, 0u);
-  st_dev(c + kSyncAll, 0u);
+  st_dev(c + kSyncArrive, 0u);
   return 1;
 }
 

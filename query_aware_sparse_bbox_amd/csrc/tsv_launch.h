@@ -81,8 +81,8 @@ struct DecodePlan {
 DecodePlan plan_decode(const Dims& d, int k_max);
 
 // One-launch step: nt threads per workgroup, S workgroups per row, lds bytes
-// of dynamic local memory, `polls` reads of a row's flag before a split stops
-// waiting for the row's other splits' page keys.
+// of dynamic local memory, `polls` reads of a row's arrival count before a
+// split stops waiting for the row's other splits' page keys.
 struct StepPlan {
   int nt, S, polls;
   size_t lds;

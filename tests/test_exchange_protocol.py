@@ -1,11 +1,12 @@
 """The split-row counter protocol of the one-launch step, checked on the CPU.
 
-A row of the step split over S workgroups meets twice through three counter
-words: the score exchange (`row_exchange`: arrivals, then an all-arrived flag
-that waiting splits poll a bounded number of times) and the finish
-(`row_finish`: the last split to finish merges and clears the words).  Those
-two functions and their call sites in `k_step` are the whole protocol, and
-the model below is a transcription of them:
+A row of the step split over S workgroups meets twice through two counter
+words: the score exchange (`row_exchange`: each split counts itself in, and
+a split that is not the last polls the count, a bounded number of times,
+until it reaches S) and the finish (`row_finish`: the last split to finish
+merges and clears both words).  Those two functions and their call sites in
+`k_step` are the whole protocol, and the model below is a transcription of
+them:
 
 * every store is relaxed: it is issued into a per-split set of stores in
   flight, each of which may land in memory at any later point, in any order;
@@ -18,13 +19,13 @@ the model below is a transcription of them:
 Every interleaving of S <= 4 splits, with every poll budget from 0 (every
 waiting split times out at once) to 3, is explored over two consecutive calls
 (the second call starts from the memory the first one left).  In every
-reachable state: a split that leaves the exchange with the flag set reads
-every other split's keys of the current call, the merging split reads every
-split's partial state of the current call, and the three words are zero once
-a call has ended, which is what the next call starts from.  The structure of
-the model is tied to the source: the test reads the two functions and the
-step kernel from the device header and checks that they perform the same
-operations in the same order.
+reachable state: a split that leaves the exchange having seen all S arrivals
+reads every other split's keys of the current call, the merging split reads
+every split's partial state of the current call, and both words are zero
+once a call has ended, which is what the next call starts from.  The
+structure of the model is tied to the source: the test reads the two
+functions and the step kernel from the device header and checks that they
+perform the same operations in the same order.
 """
 import os
 import re
@@ -35,11 +36,12 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 DEVICE_H = os.path.join(ROOT, "query_aware_sparse_bbox_amd", "csrc", "tsv_device.h")
 
 # program counters of one split
-(KEY_STORE, KEY_WAIT, ARRIVE, REARM, SET_FLAG, POLL, READ_KEYS, PART_STORE, PART_WAIT, FINISH,
- CLEAR_DONE, CLEAR_FLAG, MERGE, END) = range(14)
+(KEY_STORE, KEY_WAIT, ARRIVE, POLL, READ_KEYS, PART_STORE, PART_WAIT, FINISH, CLEAR_DONE,
+ CLEAR_ARRIVE, MERGE, END) = range(12)
 
-# memory: arrive, flag, done, key[0..S-1], part[0..S-1]
-ARRIVE_W, FLAG_W, DONE_W = 0, 1, 2
+# memory: arrive, done, key[0..S-1], part[0..S-1]
+ARRIVE_W, DONE_W = 0, 1
+NWORDS = 2
 
 
 def explore(S, polls, calls=2, mistake=None):
@@ -48,11 +50,13 @@ def explore(S, polls, calls=2, mistake=None):
     `mistake` plants one error in the protocol, to show that the checks
     catch it: "no_key_wait" (a split counts itself in before its keys
     land), "no_part_wait" (likewise before its partial state lands),
-    "flag_left_set" (the last split to finish does not clear the flag) or
-    "no_rearm" (the last split to arrive does not reset the arrivals)."""
-    key = lambda s: 3 + s
-    part = lambda s: 3 + S + s
-    mem0 = (0,) * (3 + 2 * S)
+    "no_rearm" (the last split to finish leaves the arrival count set),
+    "done_left_set" (it leaves the finish count set) or "rearm_on_arrival"
+    (the last split to arrive clears the arrival count, as a flag-based
+    protocol would, so that a split still polling never sees S)."""
+    key = lambda s: NWORDS + s
+    part = lambda s: NWORDS + S + s
+    mem0 = (0,) * (NWORDS + 2 * S)
     # split state: (pc, polls left, stores in flight)
     split0 = tuple((KEY_STORE, 0, frozenset()) for _ in range(S))
     start = (1, mem0, split0)
@@ -92,17 +96,16 @@ def explore(S, polls, calls=2, mistake=None):
                 got = mem[ARRIVE_W]
                 m = with_word(ARRIVE_W, got + 1)
                 if got == S - 1:
-                    go(SET_FLAG if mistake == "no_rearm" else REARM, mem2=m)
+                    if mistake == "rearm_on_arrival":
+                        go(READ_KEYS, mem2=m, pend2=pend | {(ARRIVE_W, 0)})
+                    else:
+                        go(READ_KEYS, mem2=m)
                 else:
                     go(POLL, left2=polls, mem2=m)
-            elif pc == REARM:
-                go(SET_FLAG, pend2=pend | {(ARRIVE_W, 0)})
-            elif pc == SET_FLAG:
-                go(READ_KEYS, pend2=pend | {(FLAG_W, 1)})
             elif pc == POLL:
                 if left == 0:
                     go(PART_STORE)  # timed out: this split scores every page itself
-                elif mem[FLAG_W] != 0:
+                elif mem[ARRIVE_W] == S:
                     go(READ_KEYS)
                 else:
                     go(POLL, left2=left - 1)
@@ -126,10 +129,11 @@ def explore(S, polls, calls=2, mistake=None):
                 m = with_word(DONE_W, got + 1)
                 go(CLEAR_DONE if got == S - 1 else END, mem2=m)
             elif pc == CLEAR_DONE:
-                go(MERGE if mistake == "flag_left_set" else CLEAR_FLAG,
-                   pend2=pend | {(DONE_W, 0)})
-            elif pc == CLEAR_FLAG:
-                go(MERGE, pend2=pend | {(FLAG_W, 0)})
+                go(CLEAR_ARRIVE,
+                   pend2=pend if mistake == "done_left_set" else pend | {(DONE_W, 0)})
+            elif pc == CLEAR_ARRIVE:
+                go(MERGE,
+                   pend2=pend if mistake == "no_rearm" else pend | {(ARRIVE_W, 0)})
             elif pc == MERGE:
                 for k in range(S):
                     assert mem[part(k)] == call, (
@@ -145,8 +149,8 @@ def explore(S, polls, calls=2, mistake=None):
         if not nxt:
             # every split ended and every store landed: the launch is over
             assert all(x[0] == END and not x[2] for x in sp), f"stuck state {state}"
-            assert mem[ARRIVE_W] == 0 and mem[FLAG_W] == 0 and mem[DONE_W] == 0, (
-                f"S={S} polls={polls}: counters {mem[:3]} left after call {call}")
+            assert mem[ARRIVE_W] == 0 and mem[DONE_W] == 0, (
+                f"S={S} polls={polls}: counters {mem[:NWORDS]} left after call {call}")
             ended += 1
             if call < calls:
                 nxt = [(call + 1, mem, split0)]
@@ -167,12 +171,22 @@ def test_every_interleaving(S, polls):
 @pytest.mark.parametrize("mistake,pattern", [
     ("no_key_wait", "keys of call"),
     ("no_part_wait", "partial state of call"),
-    ("flag_left_set", "left after call|keys of call"),
-    ("no_rearm", "left after call"),
+    ("no_rearm", "left after call|keys of call"),
+    ("done_left_set", "left after call"),
 ])
 def test_model_catches_planted_mistakes(mistake, pattern):
     with pytest.raises(AssertionError, match=pattern):
         explore(2, 2, mistake=mistake)
+
+
+def test_rearm_on_arrival_only_delays():
+    """Clearing the arrival count when the last split arrives (a flag
+    protocol's re-arm) breaks nothing the checks see, but a split that polls
+    after the clear never finds S arrivals and scores its whole row itself:
+    the model reaches states where a poll times out with every split
+    arrived.  The kernel therefore leaves the count at S until the finish."""
+    states, ended = explore(2, 2, mistake="rearm_on_arrival")
+    assert ended >= 1
 
 
 # --- the model's operations, read from the source -------------------------
@@ -209,17 +223,15 @@ def ops(body):
 def test_model_matches_the_source():
     text = open(DEVICE_H).read()
     ex = function_body(text, "int row_exchange(uint32_t* c, int S, int polls)")
-    assert ops(ex) == [("fetch_add", "kSyncArrive"), ("store", "kSyncArrive", "0u"),
-                       ("store", "kSyncAll", "1u"), ("load", "kSyncAll")]
-    # the re-arm and flag stores sit in the last arrival's branch, the poll in
-    # a loop bounded by `polls`
-    assert re.search(r"if \(o == \(uint32_t\)S - 1\) \{[^}]*st_dev\(c \+ kSyncArrive, 0u\);\s*"
-                     r"st_dev\(c \+ kSyncAll, 1u\);\s*return 1;", ex)
-    assert re.search(r"for \(int it = 0; it < polls; \+\+it\) \{\s*if \(ld_dev\(c \+ kSyncAll\) "
-                     r"!= 0u\) return 1;", ex)
+    assert ops(ex) == [("fetch_add", "kSyncArrive"), ("load", "kSyncArrive")]
+    # the last arrival returns at once; the others poll the count, in a loop
+    # bounded by `polls`, until it reaches S
+    assert re.search(r"if \(o == \(uint32_t\)S - 1\) return 1;", ex)
+    assert re.search(r"for \(int it = 0; it < polls; \+\+it\) \{\s*if \(ld_dev\(c \+ kSyncArrive\) "
+                     r"== \(uint32_t\)S\) return 1;", ex)
     fin = function_body(text, "int row_finish(uint32_t* c, int S)")
     assert ops(fin) == [("fetch_add", "kSyncDone"), ("store", "kSyncDone", "0u"),
-                        ("store", "kSyncAll", "0u")]
+                        ("store", "kSyncArrive", "0u")]
     assert re.search(r"if \(o != \(uint32_t\)S - 1\) return 0;", fin)
     # call sites: each split's stores are waited for before it counts itself in
     step = function_body(text, "void k_step(")
