@@ -118,13 +118,13 @@ size_t tsv_meta_bytes(const tsv_shape* shape);
    pages; 0 when the shape is invalid or unsupported.  The workspace holds the
    page-score keys, the selected pages' physical indices and the split
    decode's partial softmax states.  It must be 256-byte aligned.  Its first
-   TSV_WORKSPACE_ZERO_BYTES bytes hold counters through which the workgroups
-   of one row synchronise: they must be zero before the workspace is first
-   used (for example hipMemsetAsync once after allocation), and every call
-   leaves them zero, whatever the shape; the rest needs no initialisation.
-   Calls that may run at the same time (different streams) need separate
-   workspaces. */
-#define TSV_WORKSPACE_ZERO_BYTES 16384
+   TSV_WORKSPACE_ZERO_BYTES bytes hold the counters and page-key slots
+   through which the workgroups of one row synchronise: they must be zero
+   before the workspace is first used (for example hipMemsetAsync once after
+   allocation), and every call leaves them zero, whatever the shape; the rest
+   needs no initialisation.  Calls that may run at the same time (different
+   streams) need separate workspaces. */
+#define TSV_WORKSPACE_ZERO_BYTES 2113536
 size_t tsv_workspace_bytes(const tsv_shape* shape, int32_t k_max);
 
 /* Kernel launches one tsv_decode_step makes for `shape` (with_append != 0:
@@ -314,16 +314,16 @@ int tsv_decode_step_scheduled(const tsv_shape* shape, const float* q, const void
 /* tsv_decode_step_ex for callers that cannot allocate device memory: code
    under HIP graph capture that may not call hipMalloc, tight serving loops,
    harnesses that forbid allocation.  There is no workspace argument: the
-   step's scratch (split-row counters, page-score keys, partial softmax
-   states) lives in a device array owned by the library,
+   step's scratch (split-row counters and key slots, page-score keys,
+   partial softmax states) lives in a device array owned by the library,
    TSV_NOALLOC_SCRATCH_BYTES on each GPU, which exists from the loading of the
    library's device code on that GPU until the process ends.  The call
    allocates nothing (no hipMalloc, no allocating library routine).  The
    first call on a GPU also enqueues one small kernel on `stream` that clears
-   the array's counter prefix; every call leaves that prefix zero.  All calls
-   on one GPU share its array: calls that may run at the same time on one GPU
-   (different streams, or a graph replay overlapping another call) race on it
-   and must not be made.  TSV_ERR_UNSUPPORTED when tsv_workspace_bytes(shape,
+   the array's first TSV_WORKSPACE_ZERO_BYTES; every call leaves them zero.
+   All calls on one GPU share its array: calls that may run at the same time
+   on one GPU (different streams, or a graph replay overlapping another call)
+   race on it and must not be made.  TSV_ERR_UNSUPPORTED when tsv_workspace_bytes(shape,
    k_max) exceeds TSV_NOALLOC_SCRATCH_BYTES; TSV_ERR_HIP when the array's
    device address cannot be obtained; otherwise arguments, results and errors
    as for tsv_decode_step_ex. */

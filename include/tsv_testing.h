@@ -17,7 +17,7 @@ extern "C" {
 
 /* When a row's step is spread over several workgroups they exchange page
    scores; a workgroup that finds the others' scores missing after `polls`
-   reads of the row's counter scores the rest of the row itself, which gives
+   reads of the row's key slots scores the rest of the row itself, which gives
    bit-identical results (only the time differs).  polls >= 0 sets the limit
    for later calls of this library instance, process-wide, and returns the
    previous one; polls < 0 only returns the current one (default 16384).

@@ -17,7 +17,7 @@
 #include "../../include/tsv_testing.h"
 #endif
 
-static_assert(tsv::kSyncBytes == TSV_WORKSPACE_ZERO_BYTES, "zeroed workspace prefix");
+static_assert(tsv::kZeroBytes == TSV_WORKSPACE_ZERO_BYTES, "zeroed workspace prefix");
 static_assert(tsv::kNoAllocScratchBytes == TSV_NOALLOC_SCRATCH_BYTES, "no-allocation scratch");
 
 namespace {

@@ -310,9 +310,13 @@ __device__ __forceinline__ int block_excl_scan(int v, int* tmp, int* total) {
 }
 
 // Order-preserving map of fp32 (no NaN) to uint32: a > b <=> key(a) > key(b).
+// The key is never 0 (the least, -inf, maps to 0x007fffff; the one NaN that
+// would map to 0 maps to 1), so a split row's key slots can use 0 for "not
+// yet written".
 __device__ __forceinline__ uint32_t order_key(float s) {
   const uint32_t u = __float_as_uint(s);
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  const uint32_t k = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return k | (uint32_t)(k == 0u);
 }
 
 __device__ __forceinline__ float key_to_score(uint32_t k) {
@@ -1820,43 +1824,62 @@ constexpr size_t step_decode_lds() {
 template <int DT, int D, int G, int NT>
 constexpr int step_min_blocks() { return NT == 256 && (G <= 4 || DT != DT_F32) ? 2 : 1; }
 
-// Split rows: the S workgroups of a row meet twice through the row's line of
-// counters in the workspace (word 0: arrivals at the score exchange, word 2:
-// finished decodes; both zero between calls).  Everything they exchange (page keys, partial states, counters) is
-// written and read with device-scope atomic stores and loads, which are
-// coherent across the chip on their own; a writer waits for its stores to
-// complete before it counts itself in.  No cache-wide writeback or
+// Split rows: the S workgroups of a row exchange page keys through the row's
+// slots in the workspace, then meet once more through a counter of finished
+// decodes (word 0 of the row's line of counters).  Slots and counter are zero
+// between calls.  Everything they exchange (page keys, partial states, the
+// counter) is written and read with device-scope atomic stores and loads,
+// which are coherent across the chip on their own: no cache-wide writeback or
 // invalidation is needed.
-constexpr int kSyncArrive = 0, kSyncDone = 2;
+constexpr int kSyncDone = 0;
 
-// Score exchange of one split row, called by one thread after every thread
-// of the workgroup stored its keys and waited for them.  Returns 1 when all S
-// splits have arrived (their keys can then be read), 0 when `polls` reads of
-// the row's arrival count found fewer than S.  Nothing is re-armed here: the
-// count stays at S until the last split to finish clears it (row_finish).
-__device__ __forceinline__ int row_exchange(uint32_t* c, int S, int polls) {
-  const uint32_t o =
-      __hip_atomic_fetch_add(c + kSyncArrive, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  if (o == (uint32_t)S - 1) return 1;
+// Reads the keys of the pages that the row's other splits score (batch b of
+// PB pages belongs to split b mod S) from the row's slots into s_key, up to
+// `polls` times, until none of them reads 0 (not yet written).  A slot is
+// written once per call, with a key that is never 0, so a non-zero read is
+// that split's key of this call.  Returns 1 when every key has arrived, 0
+// when the reads ran out first (then s_key holds no usable foreign keys).
+// Uniform over the workgroup.  A thread reads its slots four at a time, so
+// that their round trips overlap.
+template <int NT, int PB>
+__device__ __forceinline__ int poll_row_keys(const uint32_t* xrow, uint32_t* s_key, int n, int S,
+                                             int split, int polls) {
+  constexpr int R = 4;
   for (int it = 0; it < polls; ++it) {
-    if (ld_dev(c + kSyncArrive) == (uint32_t)S) return 1;
+    int missing = 0;
+    for (int p0 = threadIdx.x; p0 < n; p0 += R * NT) {
+      uint32_t v[R];
+#pragma unroll
+      for (int j = 0; j < R; ++j) {
+        const int p = p0 + j * NT;
+        v[j] = p < n && (p / PB) % S != split ? ld_dev(xrow + p) : 1u;
+      }
+#pragma unroll
+      for (int j = 0; j < R; ++j) {
+        const int p = p0 + j * NT;
+        if (p < n && (p / PB) % S != split) {
+          s_key[p] = v[j];
+          missing |= v[j] == 0u;
+        }
+      }
+    }
+    if (!__syncthreads_or(missing)) return 1;
     __builtin_amdgcn_s_sleep(2);
   }
   return 0;
 }
 
 // Called by one thread after every thread of the workgroup stored its share
-// of the partial state and waited for it: 1 for the last of the row's S
-// splits to finish (which then merges), else 0.  Never waits.  Every split
-// gets here after it has left the score exchange, so the last one also
-// clears the arrival count: the row's counters are all zero again when the
-// kernel ends.
+// of the partial state and waited for it (and for its key stores): 1 for the
+// last of the row's S splits to finish, else 0.  Never waits.  The last
+// split resets the counter; every split has left the key exchange by then,
+// so it also clears the row's key slots, and the row's prefix of the
+// workspace is all zero again when the kernel ends.
 __device__ __forceinline__ int row_finish(uint32_t* c, int S) {
   const uint32_t o =
       __hip_atomic_fetch_add(c + kSyncDone, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   if (o != (uint32_t)S - 1) return 0;
   st_dev(c + kSyncDone, 0u);
-  st_dev(c + kSyncArrive, 0u);
   return 1;
 }
 
@@ -1909,7 +1932,7 @@ __global__ __launch_bounds__(NT, (step_min_blocks<DT, D, G, NT>())) void k_step(
     const void* __restrict__ k_new, const void* __restrict__ v_new, void* __restrict__ k_pool,
     void* __restrict__ v_pool, void* __restrict__ meta, int Hq, int k_max, SelectPolicy pol,
     float qscale, int polls, int32_t* __restrict__ sel, int32_t* __restrict__ sel_count,
-    float* __restrict__ scores_out, uint32_t* __restrict__ sync, uint32_t* __restrict__ keys,
+    float* __restrict__ scores_out, uint32_t* __restrict__ sync, uint32_t* __restrict__ xkeys,
     float* __restrict__ partials, float* __restrict__ out) {
   constexpr int NW = NT / kWave;
   constexpr bool MF = step_uses_mfma<DT, D, G>();
@@ -1978,11 +2001,12 @@ __global__ __launch_bounds__(NT, (step_min_blocks<DT, D, G, NT>())) void k_step(
   __syncthreads();  // block-table row staged; the appended token visible to the workgroup
   TSV_STAMP(1);
   // Scoring.  A split row's S workgroups score every S-th batch of pages
-  // each and exchange the keys through the workspace; a split whose wait
+  // each and exchange the keys through the row's slots; a split whose wait
   // times out scores the remaining batches itself (bit-identical keys).
   const int nbatch = (n + PB - 1) / PB;
-  bool share = S > 1 && nbatch > 1;
-  uint32_t* krow = keys + (size_t)unit * MP;
+  const bool xchg = S > 1 && nbatch > 1;  // the same for every split of the row
+  bool share = xchg;
+  uint32_t* xrow = xkeys + (size_t)unit * MP;
   for (int bstart = share ? split : 0, bstride = share ? S : 1;;) {
     if (pol.group_sum)  // uniform branch: one copy of the scoring loop per aggregation
       score_pages<DT, D, G, NT, true>(q, meta, s_phys, b, h, Hq, Hkv, n, bstart, bstride, s_key);
@@ -1990,21 +2014,16 @@ __global__ __launch_bounds__(NT, (step_min_blocks<DT, D, G, NT>())) void k_step(
       score_pages<DT, D, G, NT, false>(q, meta, s_phys, b, h, Hq, Hkv, n, bstart, bstride, s_key);
     if (!share) break;
     __syncthreads();
+    // publish this split's keys; each slot tells its readers by itself
+    // whether it has been written, so nothing waits for these stores here
     for (int bi = split; bi < nbatch; bi += S)
       for (int i = tid; i < PB; i += NT) {
         const int p = bi * PB + i;
-        if (p < n) st_dev(krow + p, s_key[p]);
+        if (p < n) st_dev(xrow + p, s_key[p]);
       }
-    stores_done();
-    __syncthreads();
-    if (tid == 0) s_flag = row_exchange(rsync, S, polls);
-    __syncthreads();
-    if (s_flag) {
-      for (int p = tid; p < n; p += NT)
-        if ((p / PB) % S != split) s_key[p] = ld_dev(krow + p);
-      break;
-    }
-    share = false;  // timed out: score every batch here
+    if (poll_row_keys<NT, PB>(xrow, s_key, n, S, split, polls)) break;
+    __syncthreads();  // no thread still reads s_key for the stores above
+    share = false;    // timed out: score every batch here
     bstart = 0;
     bstride = 1;
   }
@@ -2068,7 +2087,9 @@ __global__ __launch_bounds__(NT, (step_min_blocks<DT, D, G, NT>())) void k_step(
     TSV_STAMP(5);
     return;
   }
-  // the last split of the row to get here merges the S partial states
+  // the last split of the row to get here clears the row's key slots (every
+  // split has read them and its own key stores have landed) and merges the S
+  // partial states
   stores_done();
   __syncthreads();
   if (tid == 0) s_flag = row_finish(rsync, S);
@@ -2077,6 +2098,8 @@ __global__ __launch_bounds__(NT, (step_min_blocks<DT, D, G, NT>())) void k_step(
     TSV_STAMP(5);
     return;
   }
+  if (xchg)
+    for (int p = tid; p < n; p += NT) st_dev(xrow + p, 0u);
   merge_row<D, G, NT>(partials, S, orow, hq0);
   TSV_STAMP(5);
 }

@@ -73,12 +73,12 @@ size_t step_lds_bytes(const Dims& d) {
 // over up to 8 workgroups each (they share the scoring, every one selects the
 // whole row, then decodes its share of the kept tokens), as far as k_max
 // pages give each split its minimum span; the last split to finish merges.
-// Only the first kSyncRows rows have synchronisation counters.
+// Only the first kSyncRows rows have synchronisation counters and key slots.
 int step_splits(const Dims& d, int k_max) {
   const long units = (long)d.B * d.Hkv;
   const long minspan = kStepMinSpanSteps * 16 * (step_threads(d) / kWave);
   const long by_tokens = (long)k_max * d.P / minspan;
-  if (units > kSyncRows) return 1;
+  if (units > kSyncRows || (size_t)units * d.MP > kXchgWords) return 1;
   return (int)std::max(1L, std::min({(long)kStepMaxSplits, 256 / units, by_tokens}));
 }
 
@@ -104,7 +104,8 @@ DecodePlan plan_decode(const Dims& d, int k_max) {
 size_t workspace_layout(const Dims& d, int k_max, void* base, Workspace* ws) {
   const size_t units = (size_t)d.B * d.Hkv;
   const size_t o_sync = 0;
-  const size_t o_keys = o_sync + kSyncBytes;
+  const size_t o_xkeys = o_sync + kSyncBytes;
+  const size_t o_keys = o_sync + kZeroBytes;
   const size_t o_phys = o_keys + round_up(units * d.MP * sizeof(uint32_t));
   const size_t o_part = o_phys + round_up(units * k_max * sizeof(int32_t));
   const size_t splits = std::max(decode_splits(d, k_max), step_splits(d, k_max));
@@ -113,6 +114,7 @@ size_t workspace_layout(const Dims& d, int k_max, void* base, Workspace* ws) {
   if (base && ws) {
     char* c = static_cast<char*>(base);
     ws->sync = reinterpret_cast<uint32_t*>(c + o_sync);
+    ws->xkeys = reinterpret_cast<uint32_t*>(c + o_xkeys);
     ws->keys = reinterpret_cast<uint32_t*>(c + o_keys);
     ws->sel_phys = reinterpret_cast<int32_t*>(c + o_phys);
     ws->partials = reinterpret_cast<float*>(c + o_part);

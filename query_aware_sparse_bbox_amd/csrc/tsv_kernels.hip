@@ -163,7 +163,7 @@ hipError_t step_t(const Dims& d, const StepPlan& plan, const float* q, const voi
       hipLaunchKernelGGL((k_step<dt, hd, g, nthr>), grid, dim3(nthr), plan.lds, s, ord, bt,
                          seq_lens, k_per_seq, S, units, d.Hkv, d.MP, log2P, d.NP, q, k_new,
                          v_new, k_pool, v_pool, meta, d.Hq, k_max, pol, qscale, plan.polls, sel,
-                         sel_count, scores_out, ws.sync, ws.keys, ws.partials, out);
+                         sel_count, scores_out, ws.sync, ws.xkeys, ws.partials, out);
       return hipGetLastError();
     };
     return plan.nt == 256 ? go(IC<256>{}) : go(IC<512>{});

@@ -48,19 +48,27 @@ int decode_splits(const Dims& d, int k_max);
 // Partial-state floats per (sequence, query head, split).
 inline int partial_stride(const Dims& d) { return d.D + 2; }
 
-// Rows whose step is spread over several workgroups synchronise through
-// counters at the start of the workspace: one 128-byte line per row (rows are
-// split only when B*Hkv <= 128), zero before the first call and left zero by
-// every call.  The region does not depend on the shape, so a workspace reused
-// for other shapes keeps it intact.
+// Rows whose step is spread over several workgroups synchronise through the
+// start of the workspace, zero before the first call and left zero by every
+// call: one 128-byte line of counters per row (rows are split only when
+// B*Hkv <= 128), then the slots through which the row's workgroups exchange
+// page keys, [B*Hkv][MP] of the current shape, at most kSyncRows rows of
+// kMaxPagesPerSeq pages.  A slot reads 0 until its key is written (an order
+// key is never 0) and the row's last workgroup to finish clears the slots it
+// used.  The prefix does not depend on the shape, so a workspace reused for
+// other shapes keeps it intact.
 constexpr int kSyncRows = 128;
 constexpr int kSyncWordsPerRow = 32;
 constexpr size_t kSyncBytes = (size_t)kSyncRows * kSyncWordsPerRow * sizeof(uint32_t);
+constexpr size_t kXchgWords = (size_t)kSyncRows * kMaxPagesPerSeq;
+constexpr size_t kZeroBytes = kSyncBytes + kXchgWords * sizeof(uint32_t);
 
-// Regions of the caller's workspace (only `sync` needs initialisation).
+// Regions of the caller's workspace (only `sync` and `xkeys` need
+// initialisation).
 struct Workspace {
   uint32_t* sync;      // [kSyncRows][kSyncWordsPerRow] split-row counters
-  uint32_t* keys;      // [B*Hkv][MP] order keys of the page scores
+  uint32_t* xkeys;     // [B*Hkv][MP] split-row key slots (kXchgWords at most)
+  uint32_t* keys;      // [B*Hkv][MP] order keys of the page scores (phased path)
   int32_t* sel_phys;   // [B*Hkv][k_max] physical page of each selection
   float* partials;     // [B*Hq][splits][D+2] tile softmax states
 };
@@ -70,7 +78,7 @@ size_t workspace_layout(const Dims& d, int k_max, void* base, Workspace* ws);
 // Scratch of tsv_decode_step_noalloc: a library-owned device array of this
 // many bytes per GPU (tsv_scratch.hip).  noalloc_scratch returns its device
 // address on the current device; the first call on a device also enqueues,
-// on stream s, the clearing of its split-row counter prefix.
+// on stream s, the clearing of its split-row prefix (kZeroBytes).
 constexpr size_t kNoAllocScratchBytes = (size_t)32 << 20;
 hipError_t noalloc_scratch(hipStream_t s, void** out);
 
@@ -81,8 +89,8 @@ struct DecodePlan {
 DecodePlan plan_decode(const Dims& d, int k_max);
 
 // One-launch step: nt threads per workgroup, S workgroups per row, lds bytes
-// of dynamic local memory, `polls` reads of a row's arrival count before a
-// split stops waiting for the row's other splits' page keys.
+// of dynamic local memory, `polls` reads of a row's key slots before a split
+// stops waiting for the row's other splits' page keys.
 struct StepPlan {
   int nt, S, polls;
   size_t lds;

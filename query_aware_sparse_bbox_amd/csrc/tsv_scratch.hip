@@ -13,7 +13,8 @@ namespace {
 
 static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
 
-// Clears n 32-bit words (the split-row counters of the workspace layout).
+// Clears n 32-bit words (the split-row counters and key slots at the start of
+// the workspace layout).
 __global__ void k_clear_words(uint32_t* p, int n) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) p[i] = 0u;
@@ -22,7 +23,7 @@ __global__ void k_clear_words(uint32_t* p, int n) {
 constexpr int kMaxDevices = 64;
 std::mutex g_mutex;
 void* g_ptr[kMaxDevices];      // device address of `scratch` on each device
-bool g_cleared[kMaxDevices];   // counter prefix cleared on that device
+bool g_cleared[kMaxDevices];   // split-row prefix cleared on that device
 
 }  // namespace
 
@@ -40,10 +41,10 @@ hipError_t noalloc_scratch(hipStream_t s, void** out) {
     g_ptr[dev] = p;
   }
   if (!g_cleared[dev]) {
-    // the counter prefix must start at zero; every step leaves it zero.  A
+    // the split-row prefix must start at zero; every step leaves it zero.  A
     // kernel rather than a memset, so that a first call under graph capture
     // records a node that replays correctly.
-    const int words = (int)(kSyncBytes / sizeof(uint32_t));
+    const int words = (int)(kZeroBytes / sizeof(uint32_t));
     (void)hipGetLastError();  // the check below sees this launch only
     hipLaunchKernelGGL(k_clear_words, dim3((words + 255) / 256), dim3(256), 0, s,
                        static_cast<uint32_t*>(g_ptr[dev]), words);

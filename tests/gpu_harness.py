@@ -14,7 +14,7 @@ import oracle as O
 import workloads as W
 
 TOL = {W.F32: 1e-5, W.F16: 2e-3, W.BF16: 2e-3, W.F8: 2e-3, W.F8E5: 2e-3}
-SYNC_BYTES = 16384  # TSV_WORKSPACE_ZERO_BYTES: zero before and after every call
+SYNC_BYTES = 2113536  # TSV_WORKSPACE_ZERO_BYTES: zero before and after every call
 
 
 def say(*a):

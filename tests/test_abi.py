@@ -104,11 +104,13 @@ def test_sizes(tsv):
 
 
 def test_workspace_zeroed_prefix(tsv):
-    """The counters of split rows sit in a fixed zero-initialised prefix of
-    the workspace; every workspace is at least that large, whatever the shape."""
+    """The counters and key slots of split rows sit in a fixed
+    zero-initialised prefix of the workspace (128 rows: a 128-byte line of
+    counters each, then 4096 four-byte page slots each); every workspace is
+    at least that large, whatever the shape."""
     text = open(HEADER).read()
     zero = int(re.search(r"#define TSV_WORKSPACE_ZERO_BYTES (\d+)", text).group(1))
-    assert zero == 16384
+    assert zero == 128 * 128 + 128 * 4096 * 4
     for s in (shape(), shape(batch=1, max_pages_per_seq=1), shape(batch=128, head_dim=128)):
         assert tsv.tsv_workspace_bytes(s, 1) > zero
 
