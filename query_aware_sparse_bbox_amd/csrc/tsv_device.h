@@ -310,13 +310,11 @@ __device__ __forceinline__ int block_excl_scan(int v, int* tmp, int* total) {
 }
 
 // Order-preserving map of fp32 (no NaN) to uint32: a > b <=> key(a) > key(b).
-// The key is never 0 (the least, -inf, maps to 0x007fffff; the one NaN that
-// would map to 0 maps to 1), so a split row's key slots can use 0 for "not
-// yet written".
+// The least key of a non-NaN score is 0x007fffff (-inf); only one NaN
+// pattern maps to 0.
 __device__ __forceinline__ uint32_t order_key(float s) {
   const uint32_t u = __float_as_uint(s);
-  const uint32_t k = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-  return k | (uint32_t)(k == 0u);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
 __device__ __forceinline__ float key_to_score(uint32_t k) {
@@ -2015,11 +2013,18 @@ __global__ __launch_bounds__(NT, (step_min_blocks<DT, D, G, NT>())) void k_step(
     if (!share) break;
     __syncthreads();
     // publish this split's keys; each slot tells its readers by itself
-    // whether it has been written, so nothing waits for these stores here
+    // whether it has been written (a published key is never 0: the one NaN
+    // key that is becomes 1, here and in this split's own copy, so that every
+    // split of the row ranks the same keys), so nothing waits for these
+    // stores here
     for (int bi = split; bi < nbatch; bi += S)
       for (int i = tid; i < PB; i += NT) {
         const int p = bi * PB + i;
-        if (p < n) st_dev(xrow + p, s_key[p]);
+        if (p < n) {
+          const uint32_t k = max(s_key[p], 1u);
+          s_key[p] = k;
+          st_dev(xrow + p, k);
+        }
       }
     if (poll_row_keys<NT, PB>(xrow, s_key, n, S, split, polls)) break;
     __syncthreads();  // no thread still reads s_key for the stores above

@@ -196,9 +196,11 @@ def ops(body):
 
 def test_model_matches_the_source():
     text = open(DEVICE_H).read()
-    # an order key is never 0, the value of a slot not yet written
-    ok = function_body(text, "uint32_t order_key(float s)")
-    assert re.search(r"return k \| \(uint32_t\)\(k == 0u\);", ok)
+    step = function_body(text, "void k_step(")
+    # a published key is never 0, the value of a slot not yet written, and the
+    # split's own copy holds the same value
+    assert re.search(r"const uint32_t k = max\(s_key\[p\], 1u\);\s*s_key\[p\] = k;\s*"
+                     r"st_dev\(xrow \+ p, k\);", step)
     poll = function_body(text, "int poll_row_keys(")
     # up to `polls` rounds, each reading every other split's slots, until
     # none reads 0
@@ -211,11 +213,10 @@ def test_model_matches_the_source():
     fin = function_body(text, "int row_finish(uint32_t* c, int S)")
     assert ops(fin) == [("fetch_add", "kSyncDone"), ("store", "kSyncDone", "0u")]
     assert re.search(r"if \(o != \(uint32_t\)S - 1\) return 0;", fin)
-    step = function_body(text, "void k_step(")
     # the slots are written twice: this split's keys before the poll, zeros
     # by the last split to finish
-    assert re.findall(r"st_dev\(xrow \+ p, ([^)]*)\)", step) == ["s_key[p]", "0u"]
-    i_pub = step.index("st_dev(xrow + p, s_key[p]);")
+    assert re.findall(r"st_dev\(xrow \+ p, ([^)]*)\)", step) == ["k", "0u"]
+    i_pub = step.index("st_dev(xrow + p, k);")
     i_poll = step.index("poll_row_keys<NT, PB>(xrow, s_key, n, S, split, polls)")
     i_fin = step.index("row_finish(rsync, S)")
     assert i_pub < i_poll < i_fin
