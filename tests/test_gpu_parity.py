@@ -485,9 +485,8 @@ def test_ragged_appends_seventeen_steps(kw):
 def test_split_rows_exchange_fallback_bit_identical():
     """Rows spread over several workgroups share their page scoring through the
     workspace.  With the wait cut to zero polls (testing library), every split
-    but the last to arrive scores the rest of its row itself: scores,
-    selections and outputs are the same bits, and the counters are left at
-    zero either way."""
+    scores the rest of its row itself: scores, selections and outputs are the
+    same bits, and the counters and key slots are left at zero either way."""
     import query_aware_sparse_bbox_amd as T
 
     t = T.testing_library()
