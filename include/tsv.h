@@ -61,7 +61,10 @@
 extern "C" {
 #endif
 
-#define TSV_VERSION 1
+/* 2: TSV_WORKSPACE_ZERO_BYTES grew from 16384 to 2113536 (the split rows'
+   page-key slots joined their counters); a workspace zeroed for version 1
+   must be zeroed again over the new prefix. */
+#define TSV_VERSION 2
 
 /* KV storage types.  TSV_FP8_E4M3 is the OCP 8-bit float E4M3 ("FN"): sign,
    4 exponent bits (bias 7), 3 mantissa bits, no infinities, NaN only at

@@ -74,7 +74,7 @@ def test_library_is_built_for_gfx950(tsv, which):
 
 
 def test_version_and_status_strings(tsv):
-    assert tsv.tsv_version() == 1
+    assert tsv.tsv_version() == 2
     assert tsv.status_string(0) == "ok"
     assert "invalid" in tsv.status_string(-1)
     assert "unsupported" in tsv.status_string(-2)
