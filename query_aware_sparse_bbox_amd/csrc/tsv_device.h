@@ -977,10 +977,10 @@ __global__ __launch_bounds__(kSelectThreads) void k_select(
 // never loaded: their V stays zero and their logit -inf, so a NaN in an
 // unused slot cannot reach the output.
 //
-// Each tile leaves (max, sum, acc[D]) per query head in `partials`; the last
-// tile of a unit to finish (arrival counter) merges them into `out`.  A unit
-// with one tile writes `out` directly; a unit with nothing selected gets zero
-// rows from its first tile slot.
+// Each tile leaves (max, sum, acc[D]) per query head in `partials`, and
+// k_merge, launched after the tiles, combines a unit's tiles into `out`.  A
+// unit with one tile writes `out` directly; a unit with nothing selected gets
+// zero rows from its first tile slot.
 
 // Token span of one split when a row's t_all selected tokens are spread over
 // at most S workgroups of at least `minspan` tokens each (a multiple of 16,
