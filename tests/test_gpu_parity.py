@@ -198,10 +198,11 @@ def test_shape_sweep(name, kw, opts):
 
 
 def test_scores_with_wide_single_wave_selection():
-    """Rows of at most 512 pages select in one wave, which overwrites the page
-    keys in local memory with page indices; with more than 64 pages kept the
-    exported scores must still be the page scores (300-page rows, budget
-    128), on the one-launch step and the three-call path."""
+    """The select overwrites the page keys in local memory with the kept
+    page indices, so the exported scores are copied out before it: with more
+    than 64 pages kept (300-page rows, budget 128, the workgroup select) they
+    must still be the page scores, on the one-launch step and the three-call
+    path."""
     wl = W.make("tinyllama", batch=2, context=300 * 16 - 5)
     assert wl.shape.max_pages_per_seq >= 300
     g, o = _case(wl, k_max=128, k_per_seq=None)
